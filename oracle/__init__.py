@@ -1,0 +1,225 @@
+"""CPU oracle for one EAGLE-2 draft-tree verification step (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package; the product path never does.  It wraps ``oracle.c`` (plain C loops,
+fp64 attention) through ctypes and takes numpy arrays on the host.  bf16
+inputs are passed as their raw uint16 bit patterns.
+
+Every function follows the passages named in ``oracle.c``'s header; the
+arithmetic of the softmax weights is defined there ("Spec S").
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+OK, ERR_ARG, ERR_DATA, ERR_CLOSURE, ERR_PATH = 0, -1, -2, -3, -4
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (always when force=True)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = C.CDLL(_LIB)
+        vp, i32, i64, f32, f64 = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_double
+        L.orc_exp_spec.restype = f32
+        L.orc_exp_spec.argtypes = [f32]
+        L.orc_weight.restype = f64
+        L.orc_weight.argtypes = [f32, f32, f32]
+        L.orc_row_stats.argtypes = [vp, i32, i64, i32, i32, i32, f32, vp, vp, vp, vp]
+        L.orc_build_tree.argtypes = [vp, i32, vp, i32, i64, i32, vp, i32, vp, vp, vp, vp, vp, vp,
+                                     i32, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+        L.orc_tree_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_tree_attn_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+        L.orc_accept.argtypes = [i32, f32, i32, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp]
+        for f in ("orc_row_stats", "orc_build_tree", "orc_tree_mask", "orc_tree_attn",
+                  "orc_tree_attn_rows", "orc_accept", "orc_num_threads"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"oracle {what} failed with code {code}")
+        self.code = code
+
+
+def _check(code, what):
+    if code != OK:
+        raise OracleError(code, what)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _logits(a):
+    """(array, dtype code): fp32 stays fp32, uint16 is bf16 bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, 0
+    if a.dtype == np.uint16:
+        return a, 1
+    raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def exp_spec(x) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    f = lib().orc_exp_spec
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.float32).reshape(x.shape)
+
+
+def weight(l, M, T=1.0) -> float:
+    return lib().orc_weight(float(l), float(M), float(T))
+
+
+def row_stats(logits, C: int, T: float = 1.0):
+    """logits [rows][V] -> (M [rows] f32, W [rows] f64, top_id [rows][C], top_w [rows][C] f64)."""
+    a, dt = _logits(logits)
+    rows, V = a.shape
+    M = np.zeros(rows, np.float32)
+    W = np.zeros(rows, np.float64)
+    tid = np.zeros((rows, C), np.int32)
+    tw = np.zeros((rows, C), np.float64)
+    _check(lib().orc_row_stats(_p(a), dt, V, rows, V, C, T, _p(M), _p(W), _p(tid), _p(tw)), "row_stats")
+    return M, W, tid, tw
+
+
+class _TreeParams(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("depth", "topk", "children", "m", "chain_k", "vocab")]
+
+
+def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_max=None,
+               debug=False):
+    """draft_logits [B][R_max][V] -> dict of tree arrays (rank order), plus candidates if debug."""
+    a, dt = _logits(draft_logits)
+    B, R, V = a.shape
+    if m_max is None:
+        m_max = m
+    kinds = np.zeros(B, np.int32) if kinds is None else np.ascontiguousarray(kinds, dtype=np.int32)
+    p = _TreeParams(depth, topk, children, m, chain_k, V)
+    out = {k: np.zeros((B, m_max), np.int32) for k in ("tokens", "parent", "depth", "src_row")}
+    out["score"] = np.zeros((B, m_max), np.float64)
+    out["num_nodes"] = np.zeros(B, np.int32)
+    nmax = max(children + (depth - 1) * topk * children, chain_k)
+    dbg = {}
+    if debug:
+        dbg = {k: np.zeros((B, nmax), np.int32) for k in ("token", "parent", "depth", "row", "rank")}
+        dbg["V"] = np.zeros((B, nmax), np.float64)
+        dbg["n"] = np.zeros(B, np.int32)
+    code = lib().orc_build_tree(
+        C.byref(p), B, _p(a), dt, V, R, _p(kinds), m_max,
+        _p(out["tokens"]), _p(out["parent"]), _p(out["depth"]), _p(out["score"]), _p(out["src_row"]),
+        _p(out["num_nodes"]), nmax, _p(dbg.get("n")), _p(dbg.get("token")), _p(dbg.get("parent")),
+        _p(dbg.get("depth")), _p(dbg.get("V")), _p(dbg.get("row")), _p(dbg.get("rank")))
+    _check(code, "build_tree")
+    if debug:
+        out["cand"] = dbg
+    return out
+
+
+def tree_mask(parent, num_nodes, prefix_len):
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    num_nodes = np.ascontiguousarray(num_nodes, dtype=np.int32)
+    prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
+    B, M = parent.shape
+    anc = np.zeros((B, M), np.uint64)
+    pos = np.zeros((B, M), np.int32)
+    _check(lib().orc_tree_mask(B, M, _p(parent), _p(num_nodes), _p(prefix_len), _p(anc), _p(pos)),
+           "tree_mask")
+    return anc, pos
+
+
+class _AttnParams(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int), ("num_kv_heads", C.c_int), ("head_dim", C.c_int),
+                ("m_max", C.c_int), ("block_size", C.c_int), ("max_blocks", C.c_int),
+                ("max_prefix", C.c_int), ("dtype", C.c_int), ("scale", C.c_double)]
+
+
+def _attn_common(q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, anc, scale):
+    arrs = [np.ascontiguousarray(x) for x in (q, k_draft, v_draft, k_cache, v_cache)]
+    dt = 0 if arrs[0].dtype == np.float32 else 1
+    for x in arrs:
+        if (x.dtype == np.float32) != (dt == 0) or x.dtype not in (np.float32, np.uint16):
+            raise TypeError("attention inputs must all be float32 or all uint16 (bf16 bits)")
+    q_, kd, vd, kc, vc = arrs
+    B, M, Hq, d = q_.shape
+    Hkv = kd.shape[2]
+    if block_table is None:
+        bs, maxb, maxp = 0, 0, kc.shape[2]
+        bt = None
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bs, maxb, maxp = kc.shape[2], bt.shape[1], 0
+    p = _AttnParams(Hq, Hkv, d, M, bs, maxb, maxp, dt, scale if scale is not None else 1.0 / np.sqrt(d))
+    pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
+    an = np.ascontiguousarray(anc, dtype=np.uint64)
+    return p, (q_, kd, vd, kc, vc, bt, pl, an)
+
+
+def tree_attn(q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, anc, num_nodes,
+              scale=None):
+    """All output rows in fp64: [B][m_max][Hq][d]; rows past num_nodes are zero."""
+    p, (q_, kd, vd, kc, vc, bt, pl, an) = _attn_common(q, k_draft, v_draft, k_cache, v_cache,
+                                                      block_table, prefix_len, anc, scale)
+    nn = np.ascontiguousarray(num_nodes, dtype=np.int32)
+    out = np.zeros(q_.shape, np.float64)
+    _check(lib().orc_tree_attn(C.byref(p), q_.shape[0], _p(q_), _p(kd), _p(vd), _p(kc), _p(vc),
+                               _p(bt), _p(pl), _p(an), _p(nn), _p(out)), "tree_attn")
+    return out
+
+
+def tree_attn_rows(q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, anc, sel,
+                   scale=None):
+    """Selected rows: sel = list of (b, i, h); returns [n_sel][d] fp64."""
+    p, (q_, kd, vd, kc, vc, bt, pl, an) = _attn_common(q, k_draft, v_draft, k_cache, v_cache,
+                                                      block_table, prefix_len, anc, scale)
+    sel = np.asarray(sel, dtype=np.int32).reshape(-1, 3)
+    sb, si, sh = (np.ascontiguousarray(sel[:, j]) for j in range(3))
+    out = np.zeros((len(sel), q_.shape[3]), np.float64)
+    _check(lib().orc_tree_attn_rows(C.byref(p), _p(q_), _p(kd), _p(vd), _p(kc), _p(vc), _p(bt),
+                                    _p(pl), _p(an), len(sel), _p(sb), _p(si), _p(sh), _p(out)),
+           "tree_attn_rows")
+    return out
+
+
+def accept(mode, target_logits, tokens, parent, num_nodes, max_accept, rand_words=None, T=1.0):
+    """mode 0 greedy / 1 sample -> (accepted [B][max_accept], accept_len [B], bonus [B])."""
+    a, dt = _logits(target_logits)
+    B, M1, V = a.shape
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    nn = np.ascontiguousarray(num_nodes, dtype=np.int32)
+    rw = None if rand_words is None else np.ascontiguousarray(rand_words).view(np.uint32)
+    acc = np.zeros((B, max_accept), np.int32)
+    alen = np.zeros(B, np.int32)
+    bon = np.zeros(B, np.int32)
+    _check(lib().orc_accept(mode, T, B, M1 - 1, max_accept, V, _p(a), dt, V, _p(tokens), _p(parent),
+                            _p(nn), _p(rw), _p(acc), _p(alen), _p(bon)), "accept")
+    return acc, alen, bon

@@ -1,0 +1,269 @@
+"""Pins for the oracle's dynamic draft tree (EAGLE-2 explainer, "Dynamic draft
+tree construction" and its Python concept sketch) and ancestor mask ("Attention
+mask adjustment").
+
+Pins: a hand-derived golden example; the concept sketch's own special case
+(every parent at a depth shares one children list); invariants recomputed with
+library sorts and exact integer weights; degenerate shapes that reduce to a
+sort of one row or to a greedy chain; brute-force reflexive-transitive closure
+for the mask.
+"""
+import heapq
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import spec_emul
+import synth
+from conftest import to_np
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hand():
+    with open(os.path.join(GOLD, "hand_tree.json")) as f:
+        return json.load(f)
+
+
+def test_hand_example_tree_mask_greedy(orc):
+    g = _hand()
+    p = g["params"]
+    logits = np.array(g["draft_logits"], np.float32)[None]
+    t = orc.build_tree(logits, p["depth"], p["topk"], p["children"], p["m"])
+    e = g["tree"]
+    assert list(t["tokens"][0]) == e["tokens"]
+    assert list(t["parent"][0]) == e["parent"]
+    assert list(t["depth"][0]) == e["depth"]
+    assert list(t["src_row"][0]) == e["src_row"]
+    assert [float.fromhex(h) for h in e["score_hex"]] == list(t["score"][0])
+    assert t["num_nodes"][0] == e["num_nodes"]
+    anc, pos = orc.tree_mask(t["parent"], t["num_nodes"], [g["mask"]["prefix_len"]])
+    assert [int(v) for v in anc[0]] == g["mask"]["anc"]
+    assert list(pos[0]) == g["mask"]["pos"]
+    for case in g["greedy_cases"]:
+        tl = np.array(case["target_logits"], np.float32)[None]
+        acc, alen, bon = orc.accept(0, tl, t["tokens"], t["parent"], t["num_nodes"], p["depth"])
+        assert list(acc[0]) == case["accepted"], case["why"]
+        assert alen[0] == case["accept_len"] and bon[0] == case["bonus"], case["why"]
+
+
+# ---------------------------------------------------------------------------
+# the concept sketch's special case: shared children per depth
+# ---------------------------------------------------------------------------
+
+def _sketch_semantics(per_depth, m, k, max_depth):
+    """Independent restatement of the sketch's behaviour: stable sort of the
+    current layer by V (descending) and keep k; every kept parent gets the
+    depth's (token, conf) list; V = parent V * conf; then the m largest V over
+    all generated nodes (heapq.nlargest keeps first-seen order among equals);
+    then ancestors of the selection are appended if missing."""
+    nodes = []                       # (token, V, depth, parent_index or -1)
+    layer = [(-1, 1.0)]              # (node index or -1 for the root, V)
+    for depth in range(1, max_depth + 1):
+        if depth - 1 >= len(per_depth):
+            break
+        keep = sorted(layer, key=lambda t: t[1], reverse=True)[:k]
+        nxt = []
+        for par_idx, par_v in keep:
+            for tok, conf in per_depth[depth - 1]:
+                nodes.append((tok, par_v * conf, depth, par_idx))
+                nxt.append((len(nodes) - 1, par_v * conf))
+        layer = nxt
+    chosen = heapq.nlargest(m, range(len(nodes)), key=lambda i: nodes[i][1])
+    have = set(chosen)
+    for i in list(chosen):
+        a = nodes[i][3]
+        while a >= 0:
+            if a not in have:
+                chosen.append(a)
+                have.add(a)
+            a = nodes[a][3]
+    return nodes, chosen
+
+
+@pytest.mark.parametrize("seed,V,dt", [(0, 50, "f32"), (1, 300, "bf16"), (2, 1000, "f32")])
+def test_sketch_special_case_shared_children(orc, seed, V, dt):
+    D, k, C, m = 4, 3, 4, 12
+    rng = np.random.default_rng(seed)
+    base = (rng.standard_normal((D, V)) * 2).astype(np.float32)
+    R = 1 + (D - 1) * k
+    rows = np.zeros((R, V), np.float32)
+    rows[0] = base[0]
+    for d in range(1, D):
+        rows[1 + (d - 1) * k: 1 + d * k] = base[d]          # every parent at depth d shares a row
+    if dt == "bf16":
+        rows = torch.from_numpy(rows).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    t = orc.build_tree(rows[None], D, k, C, m)
+    # the sketch consumes per-depth (token, conf) lists with conf = w / W of that row
+    per_depth = []
+    for d in range(D):
+        r = 0 if d == 0 else 1 + (d - 1) * k
+        M, W, ids, ws = spec_emul.row_stats(rows[r], C)
+        per_depth.append([(int(i), w / W) for i, w in zip(ids, ws)])
+    nodes, chosen = _sketch_semantics(per_depth, m, k, D)
+    assert len(chosen) == m                                     # closure added nothing
+    assert list(t["tokens"][0]) == [nodes[i][0] for i in chosen]
+    assert list(t["score"][0]) == [nodes[i][1] for i in chosen]
+    assert list(t["depth"][0]) == [nodes[i][2] for i in chosen]
+    pos_of = {n: r for r, n in enumerate(chosen)}
+    assert list(t["parent"][0]) == [-1 if nodes[i][3] < 0 else pos_of[nodes[i][3]] for i in chosen]
+
+
+# ---------------------------------------------------------------------------
+# invariants on random trees, recomputed independently
+# ---------------------------------------------------------------------------
+
+def _rows_np(w, seed):
+    return to_np(synth.draft_logits(w, seed))
+
+
+@pytest.mark.parametrize("base,seed,B", [(1, 11, 1), (2, 12, 2), (3, 13, 1)])
+def test_tree_invariants(orc, base, seed, B):
+    w = synth.small_workload(base, batch=B)
+    logits = _rows_np(w, seed)
+    t = orc.build_tree(logits, w.depth, w.topk, w.children, w.m, debug=True)
+    D, k, C, m = w.depth, w.topk, w.children, w.m
+    for b in range(B):
+        cd = {kk: v[b] for kk, v in t["cand"].items()}
+        N = int(cd["n"])
+        assert N == C + (D - 1) * k * C
+        stats = {}
+
+        def row(r):
+            if r not in stats:
+                stats[r] = spec_emul.row_stats(logits[b, r], C)
+            return stats[r]
+
+        # (1) children = top-C of the parent's row; V = fl64(V_parent * fl64(w / W))
+        sib_rank = {}
+        for i in range(N):
+            par = int(cd["parent"][i])
+            r = 0 if par < 0 else int(cd["row"][par])
+            assert r >= 0
+            j = sib_rank.get(par, 0)
+            sib_rank[par] = j + 1
+            M, W, ids, ws = row(r)
+            assert cd["token"][i] == ids[j]
+            pv = 1.0 if par < 0 else float(cd["V"][par])
+            assert cd["V"][i] == pv * (ws[j] / W)
+            assert cd["depth"][i] == (1 if par < 0 else cd["depth"][par] + 1)
+        # (2) expansion: the top-k of each depth by (V desc, creation asc) own rows 1+(d-1)k+p
+        for d in range(1, D):
+            at_d = [i for i in range(N) if cd["depth"][i] == d]
+            top = sorted(at_d, key=lambda i: (-cd["V"][i], i))[:k]
+            assert [int(cd["row"][i]) for i in top] == [1 + (d - 1) * k + p for p in range(len(top))]
+            assert all(cd["row"][i] < 0 for i in at_d if i not in top)
+        assert all(cd["row"][i] < 0 for i in range(N) if cd["depth"][i] == D)
+        # (3) rerank: the selection is the first m of the total order, in that order
+        order = sorted(range(N), key=lambda i: (-cd["V"][i], i))[:m]
+        assert [int(cd["rank"][i]) for i in order] == list(range(m))
+        assert sum(1 for i in range(N) if cd["rank"][i] >= 0) == m
+        # (4) closed under ancestors, exactly m nodes
+        for i in order:
+            a = int(cd["parent"][i])
+            while a >= 0:
+                assert cd["rank"][a] >= 0
+                a = int(cd["parent"][a])
+        # (5) outputs are the selection in rank order
+        assert t["num_nodes"][b] == m
+        for r_, i in enumerate(order):
+            assert t["tokens"][b, r_] == cd["token"][i]
+            assert t["score"][b, r_] == cd["V"][i]
+            assert t["depth"][b, r_] == cd["depth"][i]
+            assert t["src_row"][b, r_] == cd["row"][i]
+            par = int(cd["parent"][i])
+            assert t["parent"][b, r_] == (-1 if par < 0 else cd["rank"][par])
+            assert t["parent"][b, r_] < r_                      # rank order is topological
+        # (6) V equals the product of confidences along the root path (any order)
+        for r_ in range(m):
+            cs, a = [], r_
+            while a >= 0:
+                par = int(t["parent"][b, a])
+                pv = 1.0 if par < 0 else float(t["score"][b, par])
+                cs.append(float(t["score"][b, a]) / pv if pv > 0 else 0.0)
+                a = par
+            assert math.isclose(math.prod(reversed(cs)), t["score"][b, r_], rel_tol=1e-13, abs_tol=1e-300)
+
+
+def test_depth_one_is_top_m_of_root_row(orc):
+    rng = np.random.default_rng(5)
+    row = (rng.standard_normal((1, 1, 500)) * 2).astype(np.float32)
+    t = orc.build_tree(row, 1, 4, 16, 9)
+    M, W, ids, ws = spec_emul.row_stats(row[0, 0], 16)
+    assert list(t["tokens"][0]) == list(ids[:9])
+    assert list(t["score"][0]) == [x / W for x in ws[:9]]
+    assert list(t["parent"][0]) == [-1] * 9
+
+
+def test_k1_c1_tree_equals_chain(orc):
+    w = synth.small_workload(2, batch=1)
+    logits = _rows_np(w, 21)
+    D = 6
+    t = orc.build_tree(logits[:, :D], D, 1, 1, D)
+    c = orc.build_tree(logits[:, :D], D, 1, 1, D, chain_k=D, kinds=[1])
+    for kk in ("tokens", "parent", "depth", "score"):
+        assert np.array_equal(t[kk], c[kk])
+    assert list(t["parent"][0]) == [-1, 0, 1, 2, 3, 4]
+    # chain tokens are row argmaxes (ties to the smallest id)
+    for i in range(D):
+        lf = spec_emul.to_f32(logits[0, i])
+        assert c["tokens"][0, i] == int(np.flatnonzero(lf == lf.max())[0])
+
+
+def test_m_equals_n_selects_everything(orc):
+    rng = np.random.default_rng(6)
+    D, k, C = 3, 2, 3
+    R = 1 + (D - 1) * k
+    N = C + (D - 1) * k * C
+    rows = (rng.standard_normal((1, R, 40))).astype(np.float32)
+    t = orc.build_tree(rows, D, k, C, N, debug=True)
+    assert t["num_nodes"][0] == N and (t["cand"]["rank"][0][:N] >= 0).all()
+    with pytest.raises(orc.OracleError):
+        orc.build_tree(rows, D, k, C, N + 1)
+
+
+def test_chain_mode_src_rows_and_padding(orc):
+    w = synth.small_workload(5, batch=2, vocab=2000)
+    logits = _rows_np(w, 31)
+    t = orc.build_tree(logits, w.depth, w.topk, w.children, w.m, chain_k=7, kinds=[0, 1], m_max=60)
+    assert t["num_nodes"].tolist() == [60, 7]
+    assert list(t["src_row"][1, :7]) == [1, 2, 3, 4, 5, 6, -1]
+    assert (t["tokens"][1, 7:] == -1).all() and (t["parent"][1, 7:] == -1).all()
+
+
+# ---------------------------------------------------------------------------
+# mask: reflexive-transitive closure of parent
+# ---------------------------------------------------------------------------
+
+def test_mask_is_ancestor_closure(orc):
+    w = synth.small_workload(5, batch=4, vocab=3000)
+    logits = _rows_np(w, 41)
+    kinds = [0, 1, 0, 1]
+    t = orc.build_tree(logits, w.depth, w.topk, w.children, w.m, chain_k=7, kinds=kinds, m_max=60)
+    plen = np.array([100, 7, 1, 33], np.int32)
+    anc, pos = orc.tree_mask(t["parent"], t["num_nodes"], plen)
+    for b in range(4):
+        n = int(t["num_nodes"][b])
+        par = t["parent"][b]
+        reach = np.eye(60, dtype=bool)
+        for _ in range(64):                                  # closure by repeated composition
+            step = reach.copy()
+            for i in range(n):
+                if par[i] >= 0:
+                    step[i] |= reach[par[i]]
+            reach = step
+        for i in range(60):
+            bits = int(anc[b, i])
+            want = sum(1 << j for j in range(60) if i < n and reach[i, j])
+            assert bits == want
+            if i < n:
+                assert bin(bits).count("1") == t["depth"][b, i]
+                assert pos[b, i] == plen[b] + t["depth"][b, i] - 1
+            else:
+                assert pos[b, i] == -1
+        if kinds[b] == 1:                                    # chain -> lower triangular
+            assert [int(anc[b, i]) for i in range(7)] == [(1 << (i + 1)) - 1 for i in range(7)]
