@@ -1,0 +1,277 @@
+"""Python binding of libeagle.so: one EAGLE-2 draft-tree verification step on
+an MI355X (gfx950).
+
+The functions here carry the names of the C entry points declared in
+``include/eagle.h`` and only marshal arguments: torch tensors become device
+pointers, the current torch stream becomes the HIP stream, and a non-OK
+status becomes an ``EagleError``.  Every step of the computation runs in the
+HIP kernels of libeagle.so; there is no fallback.  ``VerifyStep`` allocates
+the outputs and workspaces of one step for fixed shapes and runs the four
+calls in order on one stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libeagle.so")
+
+EAGLE_OK, EAGLE_ERR_INVALID, EAGLE_ERR_UNSUPPORTED, EAGLE_ERR_WORKSPACE, EAGLE_ERR_HIP = 0, -1, -2, -3, -4
+EAGLE_F32, EAGLE_BF16 = 0, 1
+EAGLE_TREE_DYNAMIC, EAGLE_TREE_CHAIN = 0, 1
+EAGLE_ACCEPT_GREEDY, EAGLE_ACCEPT_SAMPLE = 0, 1
+DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 0x1, 0x2, 0x4, 0x8, 0x10
+
+# every function exported by libeagle.so (the declarations of include/eagle.h)
+EXPORTS = (
+    "eagle_workspace_init", "eagle_read_errors",
+    "eagle_build_tree_workspace_size", "eagle_build_tree",
+    "eagle_tree_mask",
+    "eagle_tree_attn_workspace_size", "eagle_tree_attn",
+    "eagle_accept_workspace_size", "eagle_accept",
+    "eagle_status_string", "eagle_last_error",
+)
+
+
+class EagleError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what}: status {status} ({detail})")
+        self.status = status
+
+
+class TreeParams(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("depth", "topk", "children", "m", "chain_k", "vocab", "m_max", "r_max")]
+
+
+class AttnParams(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("m_max", C.c_int32), ("block_size", C.c_int32), ("max_blocks", C.c_int32),
+                ("max_prefix", C.c_int32), ("scale", C.c_float), ("dtype", C.c_int)]
+
+
+class AcceptParams(C.Structure):
+    _fields_ = [("mode", C.c_int), ("temperature", C.c_float), ("m_max", C.c_int32),
+                ("vocab", C.c_int32), ("max_accept", C.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Loads libeagle.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m eagle_tree_verification_draft_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.eagle_workspace_init.argtypes = [vp, sz, vp]
+        L.eagle_read_errors.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
+        L.eagle_build_tree_workspace_size.argtypes = [C.POINTER(TreeParams), i32]
+        L.eagle_build_tree_workspace_size.restype = sz
+        L.eagle_build_tree.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, sz, vp]
+        L.eagle_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.eagle_tree_attn_workspace_size.argtypes = [C.POINTER(AttnParams), i32]
+        L.eagle_tree_attn_workspace_size.restype = sz
+        L.eagle_tree_attn.argtypes = [C.POINTER(AttnParams), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.eagle_accept_workspace_size.argtypes = [C.POINTER(AcceptParams), i32]
+        L.eagle_accept_workspace_size.restype = sz
+        L.eagle_accept.argtypes = [C.POINTER(AcceptParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   sz, vp]
+        L.eagle_status_string.argtypes = [C.c_int]
+        L.eagle_status_string.restype = C.c_char_p
+        L.eagle_last_error.argtypes = []
+        L.eagle_last_error.restype = C.c_char_p
+        for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_tree_mask",
+                  "eagle_tree_attn", "eagle_accept"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != EAGLE_OK:
+        raise EagleError(status, what, lib().eagle_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libeagle must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return EAGLE_F32
+    if dt == torch.bfloat16:
+        return EAGLE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+# ---------------------------------------------------------------------------
+# the C entry points
+# ---------------------------------------------------------------------------
+def workspace_init(ws: torch.Tensor, stream=None):
+    _check(lib().eagle_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "eagle_workspace_init")
+
+
+def read_errors(ws: torch.Tensor, stream=None) -> int:
+    bits = C.c_uint32(0)
+    _check(lib().eagle_read_errors(_ptr(ws), _stream(stream), C.byref(bits)), "eagle_read_errors")
+    return bits.value
+
+
+def build_tree_workspace_size(p: TreeParams, batch: int) -> int:
+    return lib().eagle_build_tree_workspace_size(C.byref(p), batch)
+
+
+def build_tree(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind: Optional[torch.Tensor],
+               tokens, parent, depth, score, src_row, num_nodes, workspace: torch.Tensor, stream=None):
+    _check(lib().eagle_build_tree(C.byref(p), batch, _ptr(draft_logits), dtype_code(draft_logits.dtype),
+                                  draft_logits.shape[-1], _ptr(kind), _ptr(tokens), _ptr(parent), _ptr(depth),
+                                  _ptr(score), _ptr(src_row), _ptr(num_nodes), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_build_tree")
+
+
+def tree_mask(batch: int, m_max: int, parent, num_nodes, prefix_len, anc_mask, pos,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().eagle_tree_mask(batch, m_max, _ptr(parent), _ptr(num_nodes), _ptr(prefix_len), _ptr(anc_mask),
+                                 _ptr(pos), _ptr(workspace), nbytes, _stream(stream)),
+           "eagle_tree_mask")
+
+
+def tree_attn_workspace_size(a: AttnParams, batch: int) -> int:
+    return lib().eagle_tree_attn_workspace_size(C.byref(a), batch)
+
+
+def tree_attn(a: AttnParams, batch: int, q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len,
+              anc_mask, num_nodes, out, workspace: torch.Tensor, stream=None):
+    _check(lib().eagle_tree_attn(C.byref(a), batch, _ptr(q), _ptr(k_draft), _ptr(v_draft), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(block_table), _ptr(prefix_len), _ptr(anc_mask),
+                                 _ptr(num_nodes), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_tree_attn")
+
+
+def accept_workspace_size(a: AcceptParams, batch: int) -> int:
+    return lib().eagle_accept_workspace_size(C.byref(a), batch)
+
+
+def accept(a: AcceptParams, batch: int, target_logits: torch.Tensor, tokens, parent, num_nodes,
+           rand_words: Optional[torch.Tensor], accepted, accept_len, bonus_token, workspace: torch.Tensor,
+           stream=None):
+    _check(lib().eagle_accept(C.byref(a), batch, _ptr(target_logits), dtype_code(target_logits.dtype),
+                              target_logits.shape[-1], _ptr(tokens), _ptr(parent), _ptr(num_nodes),
+                              _ptr(rand_words), _ptr(accepted), _ptr(accept_len), _ptr(bonus_token),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_accept")
+
+
+# ---------------------------------------------------------------------------
+# one verification step with preallocated buffers
+# ---------------------------------------------------------------------------
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte-aligned blocks
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
+@dataclasses.dataclass
+class StepShape:
+    batch: int
+    vocab: int
+    depth: int
+    topk: int
+    children: int
+    m: int
+    chain_k: int
+    m_max: int
+    r_max: int
+    max_accept: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    max_blocks: int
+    max_prefix: int
+    dtype: torch.dtype
+    accept_mode: int
+    temperature: float
+
+
+class VerifyStep:
+    """Outputs and workspaces of one step; run() enqueues the four calls."""
+
+    def __init__(self, s: StepShape, device="cuda"):
+        self.s = s
+        dev = torch.device(device)
+        B, M = s.batch, s.m_max
+        self.tree = TreeParams(s.depth, s.topk, s.children, s.m, s.chain_k, s.vocab, s.m_max, s.r_max)
+        self.attn = AttnParams(s.num_q_heads, s.num_kv_heads, s.head_dim, s.m_max, s.block_size, s.max_blocks,
+                               s.max_prefix, 0.0, dtype_code(s.dtype))
+        self.acc = AcceptParams(s.accept_mode, s.temperature, s.m_max, s.vocab, s.max_accept)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.tokens = torch.empty((B, M), **i32)
+        self.parent = torch.empty((B, M), **i32)
+        self.depth = torch.empty((B, M), **i32)
+        self.score = torch.empty((B, M), dtype=torch.float64, device=dev)
+        self.src_row = torch.empty((B, M), **i32)
+        self.num_nodes = torch.empty((B,), **i32)
+        self.anc = torch.empty((B, M), dtype=torch.int64, device=dev)
+        self.pos = torch.empty((B, M), **i32)
+        self.out = torch.empty((B, M, s.num_q_heads, s.head_dim), dtype=s.dtype, device=dev)
+        self.accepted = torch.empty((B, s.max_accept), **i32)
+        self.accept_len = torch.empty((B,), **i32)
+        self.bonus = torch.empty((B,), **i32)
+        self.ws_tree = _workspace(build_tree_workspace_size(self.tree, B), dev)
+        self.ws_mask = _workspace(256, dev)
+        self.ws_attn = _workspace(tree_attn_workspace_size(self.attn, B), dev)
+        self.ws_acc = _workspace(accept_workspace_size(self.acc, B), dev)
+
+    def build(self, draft_logits, kind=None, stream=None):
+        build_tree(self.tree, self.s.batch, draft_logits, kind, self.tokens, self.parent, self.depth, self.score,
+                   self.src_row, self.num_nodes, self.ws_tree, stream)
+
+    def mask(self, prefix_len, stream=None):
+        tree_mask(self.s.batch, self.s.m_max, self.parent, self.num_nodes, prefix_len, self.anc, self.pos,
+                  self.ws_mask, stream)
+
+    def attention(self, q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, stream=None):
+        tree_attn(self.attn, self.s.batch, q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len,
+                  self.anc, self.num_nodes, self.out, self.ws_attn, stream)
+
+    def accept(self, target_logits, rand_words=None, stream=None):
+        accept(self.acc, self.s.batch, target_logits, self.tokens, self.parent, self.num_nodes, rand_words,
+               self.accepted, self.accept_len, self.bonus, self.ws_acc, stream)
+
+    def run(self, draft_logits, kind, prefix_len, q, k_draft, v_draft, k_cache, v_cache, block_table,
+            target_logits, rand_words=None, stream=None):
+        self.build(draft_logits, kind, stream)
+        self.mask(prefix_len, stream)
+        self.attention(q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, stream)
+        self.accept(target_logits, rand_words, stream)
+
+    def errors(self) -> int:
+        bits = 0
+        for ws in (self.ws_tree, self.ws_mask, self.ws_attn, self.ws_acc):
+            bits |= read_errors(ws)
+        return bits

@@ -1,0 +1,462 @@
+// build_tree.hip -- dynamic draft tree construction (EAGLE-2 explainer,
+// "Dynamic draft tree construction"): per-row softmax statistics and top-C
+// children (kernel 1), then per-sequence expansion, rerank and compaction
+// (kernel 2).
+#include "common.h"
+#include "internal.h"
+
+namespace eagle {
+
+// ---------------------------------------------------------------------------
+// Kernel 1: one workgroup per draft row.  The row is read once from HBM with
+// 16-byte loads (coalesced across the workgroup) and kept in registers:
+//   M = row max; W = sum of exact integer weights (fp64, exact in any order);
+//   top-C by (logit desc, id asc): every top-C element is >= T, where T is the
+//   largest over waves of the C-th largest lane maximum in that wave (C lanes
+//   of that wave hold an element >= T, so the C-th largest of the row is >= T).
+//   Elements >= T are appended to an LDS list during the weight pass and
+//   ranked there.  If more than kCandCap qualify (heavy ties), C rounds of
+//   block argmax over the row select exactly.
+// ---------------------------------------------------------------------------
+constexpr int kCandCap = 2048;
+constexpr int kRowThreadsMax = 512;
+
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int n = 4; };
+template <> struct Vec<uint16_t> { static constexpr int n = 8; };
+
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4 &u, float *out);
+template <>
+__device__ __forceinline__ void unpack<float>(const uint4 &u, float *o)
+{
+    o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+    o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+}
+template <>
+__device__ __forceinline__ void unpack<uint16_t>(const uint4 &u, float *o)
+{
+    o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+    o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_scalar(const T *p);
+template <> __device__ __forceinline__ float load_scalar<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+// Loads this thread's part of a row: vector j holds elements [(j*NT + tid)*VEC, +VEC).
+// Missing elements read as -inf (never a candidate, weight 0).
+template <typename T, int kNV>
+__device__ __forceinline__ void load_row(const T *row, int V, bool vec_ok, uint4 (&x)[kNV])
+{
+    constexpr int VEC = Vec<T>::n;
+    const int NT = blockDim.x, tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) {
+        const int base = (j * NT + tid) * VEC;
+        if (vec_ok && base + VEC <= V) {
+            x[j] = ld16_stream(row + base);
+        } else {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                f[e] = (base + e < V) ? load_scalar<T>(row + base + e) : -__builtin_inff();
+            if constexpr (VEC == 4) {
+                x[j] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                                  __float_as_uint(f[3]));
+            } else {
+                // re-pack to bf16 pairs (values came from bf16, so truncation is exact)
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (__float_as_uint(f[2 * e]) >> 16) | (__float_as_uint(f[2 * e + 1]) & 0xffff0000u);
+                x[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
+struct RowStatsSmem {
+    BlockScratch red;
+    float cand_v[kCandCap];
+    int cand_i[kCandCap];
+    int sel[kMaxChildren];
+    float thr[16];
+    int count;
+};
+
+template <typename T, int kNV>
+__global__ __launch_bounds__(kRowThreadsMax) void k_row_stats(RowStatsArgs a)
+{
+    constexpr int VEC = Vec<T>::n;
+    __shared__ RowStatsSmem sm;
+    const int b = blockIdx.x / a.r_max, r = blockIdx.x % a.r_max;
+    const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
+    const int rows_needed = kind == EAGLE_TREE_CHAIN ? a.chain_k : a.rows_dyn;
+    if (r >= rows_needed) return;
+    const int C = kind == EAGLE_TREE_CHAIN ? 1 : a.children;
+    const int V = a.vocab, NT = blockDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const T *row = static_cast<const T *>(a.logits) + ((size_t)b * a.r_max + r) * (size_t)a.row_stride;
+
+    uint4 x[kNV];
+    load_row<T, kNV>(row, V, a.vec_ok, x);
+
+    // row max and per-lane max
+    // (the max pass unpacks opaque copies so that the unpacked values are not
+    // kept live until the weight pass)
+    float lmax = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) {
+        float f[VEC];
+        unpack<T>(opaque(x[j]), f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
+        if constexpr (kNV > 16) __builtin_amdgcn_sched_barrier(0);
+    }
+    const float M = block_max(lmax, sm.red);
+
+    // threshold: C-th largest lane max of this wave (bitonic sort, descending)
+    float s = lmax;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const float o = __shfl_xor(s, j);
+            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+            s = keep_max ? fmaxf(s, o) : fminf(s, o);
+        }
+    }
+    const float tw = __shfl(s, C - 1);
+    if (lane == 0) sm.thr[wv] = tw;
+    __syncthreads();
+    float thr = sm.thr[0];
+    for (int j = 1; j < (NT >> 6); ++j) thr = fmaxf(thr, sm.thr[j]);
+
+    // exact weight sum; elements >= thr are appended to the LDS candidate list
+    // (their order there is irrelevant: ranking is by (value, id)).  With
+    // thr == -inf (fewer than C lanes per wave hold data) the exact fallback runs.
+    if (tid == 0) sm.count = 0;
+    __syncthreads();
+    const bool use_list = thr != -__builtin_inff();
+    double wsum = 0.0;
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) {
+        float f[VEC];
+        unpack<T>(x[j], f);
+        const int base = (j * NT + tid) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            wsum += (double)weight_of(f[e], M);
+            if (f[e] >= thr) {
+                const int o = atomicAdd(&sm.count, 1);
+                if (o < kCandCap) { sm.cand_v[o] = f[e]; sm.cand_i[o] = base + e; }
+            }
+        }
+        if constexpr (kNV > 16) __builtin_amdgcn_sched_barrier(0);
+    }
+    const double W = block_sum_d(wsum, sm.red);   // contains barriers: the list is complete
+    const int total = sm.count;
+
+    if (tid < kMaxChildren) sm.sel[tid] = 0;
+    __syncthreads();
+    if (use_list && total <= kCandCap) {
+        for (int i = tid; i < total; i += NT) {
+            const float vi = sm.cand_v[i];
+            const int ii = sm.cand_i[i];
+            int rank = 0;
+            for (int j = 0; j < total && rank < C; ++j) rank += before(sm.cand_v[j], sm.cand_i[j], vi, ii) ? 1 : 0;
+            if (rank < C) sm.sel[rank] = i;
+        }
+        __syncthreads();
+        if (tid < C) {
+            const int i = sm.sel[tid];
+            const size_t o2 = ((size_t)b * a.r_max + r) * a.children + tid;
+            a.top_id[o2] = sm.cand_i[i];
+            a.top_w[o2] = (double)weight_of(sm.cand_v[i], M);
+        }
+    } else {
+        // heavy ties or thr == -inf: C rounds of "best element after the
+        // previous pick", re-reading the row (rare; exact for any input)
+        float pv = __builtin_inff();
+        int pi = -1;
+        for (int c = 0; c < C; ++c) {
+            float bv = -__builtin_inff();
+            int bi = 0x7fffffff;
+            for (int id = tid; id < V; id += NT) {
+                const float f = load_scalar<T>(row + id);
+                if (before(pv, pi, f, id) && before(f, id, bv, bi)) { bv = f; bi = id; }
+            }
+            block_best(bv, bi, sm.red);
+            if (tid == 0) {
+                const size_t o2 = ((size_t)b * a.r_max + r) * a.children + c;
+                a.top_id[o2] = bi;
+                a.top_w[o2] = (double)weight_of(bv, M);
+            }
+            pv = bv;
+            pi = bi;
+        }
+    }
+    if (tid == 0) {
+        const size_t ro = (size_t)b * a.r_max + r;
+        a.M[ro] = M;
+        a.W[ro] = W;
+        if (!__builtin_isfinite(M) || !__builtin_isfinite(W)) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: one workgroup per sequence.  Candidates live in LDS in creation
+// order; sorting by (V desc, creation asc) is a bottom-up merge sort whose
+// merge step places each element by a binary search in its partner run.
+// ---------------------------------------------------------------------------
+struct Key {
+    double v;
+    int i;
+    int pad;
+};
+
+__device__ __forceinline__ bool key_before(const Key &a, const Key &b)
+{
+    return a.v > b.v || (a.v == b.v && a.i < b.i);
+}
+
+// Sorts keys[0..n) in place (scratch holds n more).  Returns the buffer that
+// holds the result (keys or scratch).
+__device__ Key *merge_sort_keys(Key *keys, Key *scratch, int n)
+{
+    Key *src = keys, *dst = scratch;
+    for (int width = 1; width < n; width <<= 1) {
+        for (int e = threadIdx.x; e < n; e += blockDim.x) {
+            const int start = (e / (2 * width)) * (2 * width);
+            const int mid = min(start + width, n), end = min(start + 2 * width, n);
+            const Key me = src[e];
+            int lo, hi, own;
+            if (e < mid) { lo = mid; hi = end; own = e - start; }
+            else { lo = start; hi = mid; own = e - mid; }
+            // count elements of [lo, hi) that come before `me` (a prefix of the run)
+            int a = lo, c = hi;
+            while (a < c) {
+                const int md = (a + c) >> 1;
+                if (key_before(src[md], me)) a = md + 1; else c = md;
+            }
+            dst[start + own + (a - lo)] = me;
+        }
+        __syncthreads();
+        Key *t = src; src = dst; dst = t;
+    }
+    return src;
+}
+
+struct TreeSmem {
+    Key keys[kMaxCand];
+    Key scratch[kMaxCand];
+    double V[kMaxCand];
+    int tok[kMaxCand];
+    int par[kMaxCand];
+    int dep[kMaxCand];
+    int row[kMaxCand];
+    int rank_of[kMaxCand];
+    int exp_par[kMaxTopk];
+};
+
+__global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
+{
+    __shared__ TreeSmem sm;
+    const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x;
+    const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
+    const int m_max = a.m_max, Cw = a.children;
+    const size_t rb = (size_t)b * a.r_max;
+    int32_t *tokens = a.tokens + (size_t)b * m_max, *parent = a.parent + (size_t)b * m_max;
+    int32_t *depth = a.depth + (size_t)b * m_max, *src_row = a.src_row + (size_t)b * m_max;
+    double *score = a.score + (size_t)b * m_max;
+
+    if (kind == EAGLE_TREE_CHAIN) {
+        const int K = a.chain_k;
+        if (tid == 0) {
+            double Vp = 1.0;
+            for (int i = 0; i < K; ++i) {
+                const double c = a.top_w[(rb + i) * Cw] / a.W[rb + i];
+                Vp = Vp * c;
+                tokens[i] = a.top_id[(rb + i) * Cw];
+                parent[i] = i - 1;
+                depth[i] = i + 1;
+                score[i] = Vp;
+                src_row[i] = (i + 1 < K) ? i + 1 : -1;
+            }
+            a.num_nodes[b] = K;
+        }
+        for (int i = K + tid; i < m_max; i += NT) {
+            tokens[i] = -1; parent[i] = -1; depth[i] = -1; score[i] = 0.0; src_row[i] = -1;
+        }
+        return;
+    }
+
+    const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
+    // depth 1: children of the root's row 0
+    for (int j = tid; j < C; j += NT) {
+        sm.V[j] = a.top_w[rb * Cw + j] / a.W[rb];
+        sm.tok[j] = a.top_id[rb * Cw + j];
+        sm.par[j] = -1;
+        sm.dep[j] = 1;
+        sm.row[j] = -1;
+    }
+    __syncthreads();
+    int begin = 0, end = C;
+    for (int d = 1; d <= D - 1; ++d) {
+        const int cnt = end - begin;
+        for (int i = tid; i < cnt; i += NT) sm.keys[i] = Key{sm.V[begin + i], begin + i, 0};
+        __syncthreads();
+        const Key *sorted = merge_sort_keys(sm.keys, sm.scratch, cnt);
+        const int ne = cnt < k ? cnt : k;
+        for (int p = tid; p < ne; p += NT) {
+            const int pidx = sorted[p].i;
+            sm.exp_par[p] = pidx;
+            sm.row[pidx] = 1 + (d - 1) * k + p;
+        }
+        __syncthreads();
+        for (int t = tid; t < ne * C; t += NT) {
+            const int p = t / C, j = t % C;
+            const int pidx = sm.exp_par[p];
+            const size_t r = rb + 1 + (size_t)(d - 1) * k + p;
+            const double c = a.top_w[r * Cw + j] / a.W[r];
+            sm.V[end + t] = sm.V[pidx] * c;
+            sm.tok[end + t] = a.top_id[r * Cw + j];
+            sm.par[end + t] = pidx;
+            sm.dep[end + t] = d + 1;
+            sm.row[end + t] = -1;
+        }
+        __syncthreads();
+        begin = end;
+        end += ne * C;
+    }
+    const int N = end;
+    // rerank: the first m of all candidates in (V desc, creation asc)
+    for (int i = tid; i < N; i += NT) {
+        sm.keys[i] = Key{sm.V[i], i, 0};
+        sm.rank_of[i] = -1;
+    }
+    __syncthreads();
+    const Key *sorted = merge_sort_keys(sm.keys, sm.scratch, N);
+    for (int r = tid; r < m; r += NT) sm.rank_of[sorted[r].i] = r;
+    __syncthreads();
+    // connected tree check (holds by construction: V never grows along a path)
+    for (int r = tid; r < m; r += NT) {
+        int q = sm.par[sorted[r].i];
+        while (q >= 0) {
+            if (sm.rank_of[q] < 0) { raise_error(a.err, EAGLE_DEVERR_CLOSURE); break; }
+            q = sm.par[q];
+        }
+        const int i = sorted[r].i;
+        tokens[r] = sm.tok[i];
+        parent[r] = sm.par[i] < 0 ? -1 : sm.rank_of[sm.par[i]];
+        depth[r] = sm.dep[i];
+        score[r] = sm.V[i];
+        src_row[r] = sm.row[i];
+    }
+    for (int r = m + tid; r < m_max; r += NT) {
+        tokens[r] = -1; parent[r] = -1; depth[r] = -1; score[r] = 0.0; src_row[r] = -1;
+    }
+    if (tid == 0) a.num_nodes[b] = m;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
+{
+    BuildLayout L;
+    const size_t rows = (size_t)batch * p->r_max;
+    size_t o = kWsHeader;
+    L.off_M = o;      o = align_up(o + rows * sizeof(float), 256);
+    L.off_W = o;      o = align_up(o + rows * sizeof(double), 256);
+    L.off_id = o;     o = align_up(o + rows * p->children * sizeof(int32_t), 256);
+    L.off_w = o;      o = align_up(o + rows * p->children * sizeof(double), 256);
+    L.total = o;
+    return L;
+}
+
+// vectors per thread (16 or 32) and threads per row so one row fits the
+// registers of at most kRowThreadsMax threads; 0 if it does not fit
+int row_vectors(int vocab, int vec)
+{
+    if (vocab <= kRowThreadsMax * 16 * vec) return 16;
+    if (vocab <= kRowThreadsMax * 32 * vec) return 32;
+    return 0;
+}
+
+int row_threads(int vocab, int vec)
+{
+    const int nv = row_vectors(vocab, vec);
+    const int per = (nv ? nv : 32) * vec;
+    int nt = (vocab + per - 1) / per;
+    nt = (nt + 63) / 64 * 64;
+    if (nt < 64) nt = 64;
+    return nt;
+}
+
+hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const void *logits,
+                             eagle_dtype dt, int64_t row_stride, const int32_t *kind,
+                             int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                             int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    char *base = static_cast<char *>(ws);
+    RowStatsArgs ra;
+    ra.logits = logits;
+    ra.row_stride = row_stride;
+    ra.r_max = p->r_max;
+    ra.vocab = p->vocab;
+    ra.children = p->children;
+    ra.chain_k = p->chain_k;
+    ra.rows_dyn = 1 + (p->depth - 1) * p->topk;
+    ra.kind = kind;
+    ra.M = reinterpret_cast<float *>(base + L.off_M);
+    ra.W = reinterpret_cast<double *>(base + L.off_W);
+    ra.top_id = reinterpret_cast<int32_t *>(base + L.off_id);
+    ra.top_w = reinterpret_cast<double *>(base + L.off_w);
+    ra.err = reinterpret_cast<uint32_t *>(base);
+    const size_t esz = dt == EAGLE_F32 ? 4 : 2;
+    ra.vec_ok = ((uintptr_t)logits % 16 == 0) && ((size_t)row_stride * esz % 16 == 0);
+    const dim3 g1((unsigned)(batch * p->r_max));
+    if (batch > 0 && p->r_max > 0) {
+        const int vec = dt == EAGLE_F32 ? 4 : 8;
+        const dim3 blk(row_threads(p->vocab, vec));
+        const bool nv16 = row_vectors(p->vocab, vec) == 16;
+        if (dt == EAGLE_F32) {
+            if (nv16) hipLaunchKernelGGL((k_row_stats<float, 16>), g1, blk, 0, st, ra);
+            else hipLaunchKernelGGL((k_row_stats<float, 32>), g1, blk, 0, st, ra);
+        } else {
+            if (nv16) hipLaunchKernelGGL((k_row_stats<uint16_t, 16>), g1, blk, 0, st, ra);
+            else hipLaunchKernelGGL((k_row_stats<uint16_t, 32>), g1, blk, 0, st, ra);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    TreeSelectArgs ta;
+    ta.kind = kind;
+    ta.depth_max = p->depth;
+    ta.topk = p->topk;
+    ta.children = p->children;
+    ta.m = p->m;
+    ta.chain_k = p->chain_k;
+    ta.m_max = p->m_max;
+    ta.r_max = p->r_max;
+    ta.W = ra.W;
+    ta.top_id = ra.top_id;
+    ta.top_w = ra.top_w;
+    ta.tokens = tokens;
+    ta.parent = parent;
+    ta.depth = depth;
+    ta.score = score;
+    ta.src_row = src_row;
+    ta.num_nodes = num_nodes;
+    ta.err = ra.err;
+    if (batch > 0) {
+        hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(256), 0, st, ta);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace eagle

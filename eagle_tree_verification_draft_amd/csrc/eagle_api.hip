@@ -1,0 +1,253 @@
+// eagle_api.hip -- the C ABI declared in include/eagle.h: argument checks on
+// the host (before any launch), workspace sizing and kernel dispatch.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.h"
+#include "internal.h"
+
+using namespace eagle;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+eagle_status fail(eagle_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+eagle_status ok()
+{
+    g_err[0] = 0;
+    return EAGLE_OK;
+}
+
+eagle_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(EAGLE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+eagle_status check_workspace(void *ws, size_t have, size_t need)
+{
+    if (!ws) return fail(EAGLE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (((uintptr_t)ws & 255u) != 0) return fail(EAGLE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (have < need) return fail(EAGLE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return EAGLE_OK;
+}
+
+eagle_status check_tree_params(const eagle_tree_params *p, int32_t batch)
+{
+    if (!p) return fail(EAGLE_ERR_INVALID, "tree params are NULL");
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (p->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", p->vocab);
+    if (p->vocab > kMaxVocab) return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d > %d", p->vocab, kMaxVocab);
+    if (p->children < 1 || p->children > p->vocab)
+        return fail(EAGLE_ERR_INVALID, "children %d not in [1, vocab]", p->children);
+    if (p->children > kMaxChildren) return fail(EAGLE_ERR_UNSUPPORTED, "children %d > %d", p->children, kMaxChildren);
+    if (p->depth < 1 || p->topk < 1) return fail(EAGLE_ERR_INVALID, "depth and topk must be >= 1");
+    if (p->depth > kMaxDepth || p->topk > kMaxTopk)
+        return fail(EAGLE_ERR_UNSUPPORTED, "depth %d / topk %d above %d / %d", p->depth, p->topk, kMaxDepth, kMaxTopk);
+    if (p->m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", p->m_max);
+    if (p->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", p->m_max, kMaxMMax);
+    const long long N = (long long)p->children + (long long)(p->depth - 1) * p->topk * p->children;
+    if (N > kMaxCand) return fail(EAGLE_ERR_UNSUPPORTED, "%lld candidates > %d", N, kMaxCand);
+    if (p->m < 1 || p->m > p->m_max || p->m > N)
+        return fail(EAGLE_ERR_INVALID, "m %d not in [1, min(m_max %d, candidates %lld)]", p->m, p->m_max, N);
+    const long long rows_dyn = 1 + (long long)(p->depth - 1) * p->topk;
+    if (rows_dyn > p->r_max) return fail(EAGLE_ERR_INVALID, "dynamic trees use %lld rows > r_max %d", rows_dyn, p->r_max);
+    if (p->chain_k < 0 || p->chain_k > p->m_max || p->chain_k > p->r_max)
+        return fail(EAGLE_ERR_INVALID, "chain_k %d not in [0, min(m_max, r_max)]", p->chain_k);
+    return EAGLE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *eagle_status_string(eagle_status s)
+{
+    switch (s) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_ERR_INVALID: return "invalid argument";
+    case EAGLE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case EAGLE_ERR_WORKSPACE: return "workspace missing or too small";
+    case EAGLE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *eagle_last_error(void) { return g_err; }
+
+eagle_status eagle_workspace_init(void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!workspace || workspace_bytes < kWsHeader) return fail(EAGLE_ERR_WORKSPACE, "workspace NULL or below %zu bytes", kWsHeader);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(EAGLE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    return hip_status(launch_zero(workspace, workspace_bytes / 16 * 16, (hipStream_t)stream), "workspace init");
+}
+
+eagle_status eagle_read_errors(void *workspace, void *stream, uint32_t *host_bits)
+{
+    if (!workspace || !host_bits) return fail(EAGLE_ERR_INVALID, "workspace and host_bits must be non-NULL");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(host_bits, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = launch_zero(workspace, 16, st);
+    return hip_status(e, "read errors");
+}
+
+size_t eagle_build_tree_workspace_size(const eagle_tree_params *p, int32_t batch)
+{
+    if (check_tree_params(p, batch) != EAGLE_OK) return 0;
+    return build_layout(p, batch).total;
+}
+
+eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                              eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
+                              int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                              int32_t *src_row, int32_t *num_nodes, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    eagle_status s = check_tree_params(p, batch);
+    if (s != EAGLE_OK) return s;
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
+    if (row_vectors(p->vocab, dtype == EAGLE_F32 ? 4 : 8) == 0)
+        return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d too large for dtype %d rows", p->vocab, (int)dtype);
+    s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_build_tree(p, batch, draft_logits, dtype, row_stride, kind, tokens, parent, depth,
+                                        score, src_row, num_nodes, workspace, (hipStream_t)stream),
+                      "build_tree launch");
+}
+
+eagle_status eagle_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent,
+                             const int32_t *num_nodes, const int32_t *prefix_len,
+                             uint64_t *anc_mask, int32_t *pos, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", m_max);
+    if (m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", m_max, kMaxMMax);
+    if (!parent || !num_nodes || !prefix_len || !anc_mask || !pos) return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    uint32_t *err = nullptr;
+    if (workspace) {
+        eagle_status s = check_workspace(workspace, workspace_bytes, kWsHeader);
+        if (s != EAGLE_OK) return s;
+        err = static_cast<uint32_t *>(workspace);
+    }
+    if (batch == 0) return ok();
+    return hip_status(launch_tree_mask(batch, m_max, parent, num_nodes, prefix_len, anc_mask, pos, err,
+                                       (hipStream_t)stream),
+                      "tree_mask launch");
+}
+
+static eagle_status check_attn_params(const eagle_attn_params *a, int32_t batch)
+{
+    if (!a) return fail(EAGLE_ERR_INVALID, "attention params are NULL");
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (a->dtype != EAGLE_F32 && a->dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)a->dtype);
+    if (a->num_kv_heads < 1 || a->num_q_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
+        return fail(EAGLE_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    a->num_q_heads, a->num_kv_heads);
+    if (a->dtype == EAGLE_BF16 && a->head_dim != 128)
+        return fail(EAGLE_ERR_UNSUPPORTED, "bf16 head_dim %d (only 128)", a->head_dim);
+    if (a->dtype == EAGLE_F32 && a->head_dim != 64 && a->head_dim != 128)
+        return fail(EAGLE_ERR_UNSUPPORTED, "fp32 head_dim %d (only 64, 128)", a->head_dim);
+    if (a->m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", a->m_max);
+    if (a->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", a->m_max, kMaxMMax);
+    if (a->block_size < 0 || a->max_prefix < 0) return fail(EAGLE_ERR_INVALID, "negative block_size or max_prefix");
+    if (a->block_size > 0) {
+        if (a->max_blocks < 1) return fail(EAGLE_ERR_INVALID, "paged cache needs max_blocks >= 1");
+        if (a->dtype == EAGLE_BF16 && a->block_size % 8 != 0)
+            return fail(EAGLE_ERR_UNSUPPORTED, "bf16 paged cache needs block_size %% 8 == 0");
+        if ((long long)a->max_blocks * a->block_size > (1ll << 30))
+            return fail(EAGLE_ERR_UNSUPPORTED, "paged capacity above 2^30 keys");
+    }
+    if (!(a->scale == a->scale) || std::isinf(a->scale)) return fail(EAGLE_ERR_INVALID, "scale is not finite");
+    return EAGLE_OK;
+}
+
+size_t eagle_tree_attn_workspace_size(const eagle_attn_params *a, int32_t batch)
+{
+    if (check_attn_params(a, batch) != EAGLE_OK) return 0;
+    return attn_plan(a, batch).total;
+}
+
+eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const void *q,
+                             const void *k_draft, const void *v_draft, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *prefix_len, const uint64_t *anc_mask,
+                             const int32_t *num_nodes, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    eagle_status s = check_attn_params(a, batch);
+    if (s != EAGLE_OK) return s;
+    const bool no_cache = a->block_size == 0 && a->max_prefix == 0;   // empty contiguous cache
+    if (!q || !k_draft || !v_draft || (!no_cache && (!k_cache || !v_cache)) || !prefix_len || !anc_mask ||
+        !num_nodes || !out)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (a->block_size > 0 && !block_table) return fail(EAGLE_ERR_INVALID, "paged cache needs a block table");
+    if (a->dtype == EAGLE_BF16 &&
+        !(aligned16(q) && aligned16(k_draft) && aligned16(v_draft) && aligned16(k_cache) && aligned16(v_cache) &&
+          aligned16(out)))
+        return fail(EAGLE_ERR_UNSUPPORTED, "bf16 tensors must be 16-byte aligned");
+    const AttnPlan P = attn_plan(a, batch);
+    s = check_workspace(workspace, workspace_bytes, P.total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_tree_attn(a, P, batch, q, k_draft, v_draft, k_cache, v_cache, block_table,
+                                       prefix_len, anc_mask, num_nodes, out, workspace, (hipStream_t)stream),
+                      "tree_attn launch");
+}
+
+size_t eagle_accept_workspace_size(const eagle_accept_params *a, int32_t batch)
+{
+    (void)a;
+    (void)batch;
+    return kWsHeader;
+}
+
+eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const void *target_logits,
+                          eagle_dtype dtype, int64_t row_stride, const int32_t *tokens,
+                          const int32_t *parent, const int32_t *num_nodes,
+                          const uint32_t *rand_words, int32_t *accepted, int32_t *accept_len,
+                          int32_t *bonus_token, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!a) return fail(EAGLE_ERR_INVALID, "accept params are NULL");
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (a->mode != EAGLE_ACCEPT_GREEDY && a->mode != EAGLE_ACCEPT_SAMPLE)
+        return fail(EAGLE_ERR_INVALID, "accept mode %d", (int)a->mode);
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (a->mode == EAGLE_ACCEPT_SAMPLE && !(a->temperature > 0.0f && std::isfinite(a->temperature)))
+        return fail(EAGLE_ERR_INVALID, "sampling needs a finite temperature > 0");
+    if (a->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", a->vocab);
+    if (a->vocab > kMaxVocab) return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d > %d", a->vocab, kMaxVocab);
+    if (a->m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", a->m_max);
+    if (a->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", a->m_max, kMaxMMax);
+    if (a->max_accept < 1) return fail(EAGLE_ERR_INVALID, "max_accept %d < 1", a->max_accept);
+    if (row_stride < a->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, a->vocab);
+    if (!target_logits || !tokens || !parent || !num_nodes || !accepted || !accept_len || !bonus_token)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (a->mode == EAGLE_ACCEPT_SAMPLE && !rand_words) return fail(EAGLE_ERR_INVALID, "sampling needs rand_words");
+    eagle_status s = check_workspace(workspace, workspace_bytes, kWsHeader);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_accept(a, batch, target_logits, dtype, row_stride, tokens, parent, num_nodes, rand_words,
+                                    accepted, accept_len, bonus_token, static_cast<uint32_t *>(workspace),
+                                    (hipStream_t)stream),
+                      "accept launch");
+}
+
+}  // extern "C"

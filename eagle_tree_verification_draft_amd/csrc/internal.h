@@ -1,0 +1,89 @@
+// internal.h -- kernel argument blocks, workspace layouts and launchers of
+// libeagle (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/eagle.h"
+
+namespace eagle {
+
+constexpr int kMaxCand = 1024;   // generated candidates per dynamic tree
+constexpr int kMaxTopk = 64;     // nodes expanded per depth
+constexpr int kMaxDepth = 64;
+
+// ---- tree build ----------------------------------------------------------
+struct RowStatsArgs {
+    const void *logits;
+    int64_t row_stride;
+    int r_max, vocab, children, chain_k, rows_dyn;
+    const int32_t *kind;
+    float *M;
+    double *W;
+    int32_t *top_id;
+    double *top_w;
+    uint32_t *err;
+    bool vec_ok;
+};
+
+struct TreeSelectArgs {
+    const int32_t *kind;
+    int depth_max, topk, children, m, chain_k, m_max, r_max;
+    const double *W;
+    const int32_t *top_id;
+    const double *top_w;
+    int32_t *tokens, *parent, *depth;
+    double *score;
+    int32_t *src_row, *num_nodes;
+    uint32_t *err;
+};
+
+struct BuildLayout {
+    size_t off_M, off_W, off_id, off_w, total;
+};
+BuildLayout build_layout(const eagle_tree_params *p, int32_t batch);
+int row_vectors(int vocab, int vec);
+int row_threads(int vocab, int vec);
+
+hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const void *logits,
+                             eagle_dtype dt, int64_t row_stride, const int32_t *kind,
+                             int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                             int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st);
+
+// ---- mask ----------------------------------------------------------------
+hipError_t launch_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent,
+                            const int32_t *num_nodes, const int32_t *prefix_len, uint64_t *anc,
+                            int32_t *pos, uint32_t *err, hipStream_t st);
+
+// ---- attention -----------------------------------------------------------
+struct AttnPlan {
+    int G;              // q heads per kv head
+    int rows;           // m_max * G query rows per (sequence, kv head)
+    int row_groups;     // workgroups along the query rows
+    int waves;          // waves per workgroup (32 rows each, bf16 path)
+    int chunk;          // keys per split
+    int nsplit;         // splits per (sequence, kv head)
+    int max_prefix;     // cache capacity: every prefix_len is clamped to it
+    size_t off_part, off_ml, off_cnt, total;
+};
+AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch);
+
+hipError_t launch_tree_attn(const eagle_attn_params *a, const AttnPlan &P, int32_t batch,
+                            const void *q, const void *k_draft, const void *v_draft,
+                            const void *k_cache, const void *v_cache, const int32_t *block_table,
+                            const int32_t *prefix_len, const uint64_t *anc, const int32_t *num_nodes,
+                            void *out, void *ws, hipStream_t st);
+
+// ---- accept --------------------------------------------------------------
+hipError_t launch_accept(const eagle_accept_params *a, int32_t batch, const void *target,
+                         eagle_dtype dt, int64_t row_stride, const int32_t *tokens,
+                         const int32_t *parent, const int32_t *num_nodes, const uint32_t *words,
+                         int32_t *accepted, int32_t *accept_len, int32_t *bonus, uint32_t *err,
+                         hipStream_t st);
+
+// ---- misc ----------------------------------------------------------------
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+}  // namespace eagle

@@ -1,0 +1,248 @@
+/*
+ * eagle.h -- C ABI of libeagle.so: one EAGLE-2 draft-tree verification step
+ * on an MI355X (gfx950), as four asynchronous calls on one HIP stream:
+ *
+ *   eagle_build_tree   draft logits -> dynamic draft tree (or a K-token chain)
+ *   eagle_tree_mask    tree -> packed ancestor bitmasks and positions
+ *   eagle_tree_attn    tree-masked attention of the draft queries
+ *   eagle_accept       greedy or rejection-sampling acceptance walk
+ *
+ * Conventions shared by every call
+ *   - Pointers named in the signatures are DEVICE pointers owned by the
+ *     caller, unless a comment says "host".  The library allocates, frees
+ *     and synchronises nothing inside these calls; every call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated on the host before anything is launched; a
+ *     call that returns an error launched nothing.  eagle_last_error()
+ *     returns a thread-local description of the last failure.
+ *   - Faults that only the device can see (non-finite logits, a prefix
+ *     longer than the cache, an accepted path longer than the output width)
+ *     set bits in the 32-bit error word at the start of that call's
+ *     workspace; they never trap.  Read them with eagle_read_errors().
+ *   - Padding slots of every integer output are written as -1, the padding
+ *     value of paged KV-cache slot maps (P-EAGLE in vLLM, "KV cache and CUDA
+ *     graphs").
+ *   - dtype: fp32 or bf16 (raw IEEE bfloat16, row-major).
+ *   - v1 limits (EAGLE_ERR_UNSUPPORTED otherwise): m_max <= 64 (one 64-bit
+ *     mask word per node), children <= 16, vocab <= 131072 (keeps the
+ *     softmax weight sums exact), head_dim in {64, 128} (bf16: 128 only).
+ *
+ * Softmax weights.  Every decision the step takes from floating point (the
+ * confidences that rank the tree, the rejection-sampling tests) uses integer
+ * weights w_v = floor(exp_s(x_v) * 2^35), x_v = (l_v - max_u l_u) / T in fp32,
+ * where exp_s is exp2 range reduction with a degree-6 Taylor polynomial of 2^f
+ * (fp32 Horner with fused multiply-adds, coefficients rounded once from
+ * ln2^j/j!), and x is clamped below at -32.  Row sums of these weights are
+ * exact in fp64, so trees, masks and accepts are reproducible bit for bit.
+ */
+#ifndef EAGLE_H
+#define EAGLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EAGLE_OK = 0,
+    EAGLE_ERR_INVALID = -1,     /* null pointer, size out of range, inconsistent shapes */
+    EAGLE_ERR_UNSUPPORTED = -2, /* outside the v1 limits above */
+    EAGLE_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
+    EAGLE_ERR_HIP = -4          /* a HIP launch failed; see eagle_last_error() */
+} eagle_status;
+
+typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
+typedef enum { EAGLE_TREE_DYNAMIC = 0, EAGLE_TREE_CHAIN = 1 } eagle_tree_kind;
+typedef enum { EAGLE_ACCEPT_GREEDY = 0, EAGLE_ACCEPT_SAMPLE = 1 } eagle_accept_mode;
+
+/* device error bits (sticky until the workspace is re-initialised) */
+#define EAGLE_DEVERR_NONFINITE_ROW 0x1u  /* a logit row had a NaN, +Inf or all -Inf */
+#define EAGLE_DEVERR_CLOSURE 0x2u        /* a selected node's ancestor was not selected (never, by construction) */
+#define EAGLE_DEVERR_PREFIX 0x4u         /* prefix_len < 0 or above the cache capacity (clamped) */
+#define EAGLE_DEVERR_PATH 0x8u           /* accepted path longer than max_accept (truncated) */
+#define EAGLE_DEVERR_TREE 0x10u          /* malformed tree input (parent index out of range) */
+
+/* Workspaces hold per-call scratch and the error word.  Allocate at least the
+ * queried size (256-byte aligned) and clear it once with eagle_workspace_init
+ * before first use; the calls leave it reusable. */
+eagle_status eagle_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Copies the error word of a workspace to *host_bits and clears it.
+ * Synchronises `stream`; meant for tests and debugging, not the hot path. */
+eagle_status eagle_read_errors(void *workspace, void *stream, uint32_t *host_bits);
+
+/* ------------------------------------------------------------------ */
+/* Tree construction                                                   */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (EAGLE-2 explainer, "Draft model calibration" and "Dynamic draft
+ * tree construction", equation for V_i and its Python concept sketch):
+ *   c  = draft softmax probability of a token under its parent's row;
+ *   V_i = product of c over the root path of node i (V_root = 1);
+ *   expansion: at each depth d = 1..D-1 the k depth-d nodes with the largest V
+ *   get children; the p-th of them (rank p) owns draft row 1 + (d-1)k + p, and
+ *   its children are the `children` tokens of that row with the largest logits;
+ *   the root owns row 0 and its children are depth 1;
+ *   rerank: the m candidates with the largest V among all generated ones;
+ *   connected tree: ancestors of selected nodes are selected (already true,
+ *   because V never increases along a path and ancestors come first).
+ * Orders: children by (logit desc, token id asc); top-k and top-m by (V desc,
+ * creation index asc), creation index = BFS order (depth, parent's expansion
+ * rank, child rank).  Chain sequences (P-EAGLE, "Parallel drafting": all K
+ * tokens from one pass) take token i = argmax of row i (ties -> smallest id),
+ * parent i-1, and own row i+1.
+ */
+typedef struct {
+    int32_t depth;      /* D >= 1: draft tokens sit at depths 1..D */
+    int32_t topk;       /* k >= 1: nodes expanded per depth */
+    int32_t children;   /* C in [1, 16]: children per expanded node */
+    int32_t m;          /* nodes kept for dynamic trees, 1 <= m <= min(m_max, C + (D-1)kC) */
+    int32_t chain_k;    /* K for chain sequences, 0 if there are none; K <= m_max */
+    int32_t vocab;      /* V in [C, 131072] */
+    int32_t m_max;      /* output slots per sequence, <= 64 */
+    int32_t r_max;      /* draft rows per sequence in draft_logits (>= rows used) */
+} eagle_tree_params;
+
+size_t eagle_build_tree_workspace_size(const eagle_tree_params *p, int32_t batch);
+
+/*
+ * draft_logits [batch][r_max][row_stride] (dtype); row_stride >= vocab, in
+ *   elements; rows used: 1 + (D-1)k for dynamic trees, K for chains.
+ * kind [batch] eagle_tree_kind, or NULL for all-dynamic.
+ * Outputs [batch][m_max], in rank order (topological: parent index < child
+ * index), padded with -1 (score 0):
+ *   tokens   token ids;            parent   parent's index (-1 = root)
+ *   depth    1..D (chains 1..K);   score    V as fp64
+ *   src_row  draft row owned by the node if it was expanded, else -1
+ * num_nodes [batch]: m for dynamic trees, K for chains.
+ * Errors: EAGLE_ERR_INVALID for null pointers, m > candidates, rows > r_max;
+ * EAGLE_ERR_UNSUPPORTED past the v1 limits; EAGLE_ERR_WORKSPACE if the
+ * workspace is smaller than eagle_build_tree_workspace_size().
+ */
+eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                              eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
+                              int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                              int32_t *src_row, int32_t *num_nodes, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Ancestor mask                                                       */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (EAGLE-2 explainer, "Attention mask adjustment"): a draft token may
+ * attend only to its own ancestors (and itself, as a causal chain does), so
+ * branches share no information.
+ * parent [batch][m_max], num_nodes [batch], prefix_len [batch] (inputs);
+ * anc_mask [batch][m_max] uint64: bit j of node i is set iff j is i or an
+ * ancestor of i (0 for padding rows); pos [batch][m_max]: prefix_len + depth - 1
+ * (the root is the last prefix token), -1 for padding rows.
+ * Errors: EAGLE_ERR_INVALID for null pointers or m_max outside [1, 64].
+ */
+/* workspace may be NULL (then malformed-tree errors are not reported). */
+eagle_status eagle_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent,
+                             const int32_t *num_nodes, const int32_t *prefix_len,
+                             uint64_t *anc_mask, int32_t *pos, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Tree attention                                                      */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (EAGLE-1 explainer, "Role of Tree Attention": all branches are
+ * verified in one pass; EAGLE-2 explainer, "Attention mask adjustment"):
+ * for sequence b, node i < num_nodes[b] and query head h (kv head h / G,
+ * G = num_q_heads / num_kv_heads),
+ *   out[b][i][h] = softmax_j(scale * q . k_j) v_j over the prefix keys
+ *   0..prefix_len[b]-1 and the draft keys j whose bit is set in anc_mask[b][i];
+ * rows i >= num_nodes[b] are written as zeros.
+ * Layouts (row-major):
+ *   q, out            [batch][m_max][num_q_heads][head_dim]
+ *   k_draft, v_draft  [batch][m_max][num_kv_heads][head_dim]
+ *   contiguous cache (block_size == 0):
+ *     k_cache [batch][num_kv_heads][max_prefix][head_dim]
+ *     v_cache [batch][num_kv_heads][head_dim][max_prefix]   (V stored transposed)
+ *   paged cache (block_size > 0), block_table [batch][max_blocks] (-1 = unused):
+ *     k_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *     v_cache [num_blocks][num_kv_heads][head_dim][block_size]
+ * Keys past prefix_len inside the last page are never read into the result
+ * (they may hold anything, NaN included).  fp32 accumulation throughout; bf16
+ * inputs use bf16 matrix-core products for q.k and p.v.
+ * k_cache / v_cache may be NULL for a contiguous cache with max_prefix 0.
+ * Errors: EAGLE_ERR_INVALID for null pointers, num_q_heads % num_kv_heads != 0,
+ * a missing block table in paged mode; EAGLE_ERR_UNSUPPORTED past the v1
+ * limits; EAGLE_ERR_WORKSPACE for a short workspace.
+ */
+typedef struct {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t m_max;       /* <= 64 */
+    int32_t block_size;  /* 0 = contiguous cache */
+    int32_t max_blocks;  /* block_table row length (paged) */
+    int32_t max_prefix;  /* contiguous: cache capacity; paged: bound on prefix_len (<= max_blocks*block_size) */
+    float scale;         /* <= 0 selects 1/sqrt(head_dim) */
+    eagle_dtype dtype;
+} eagle_attn_params;
+
+size_t eagle_tree_attn_workspace_size(const eagle_attn_params *a, int32_t batch);
+
+eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const void *q,
+                             const void *k_draft, const void *v_draft, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *prefix_len, const uint64_t *anc_mask,
+                             const int32_t *num_nodes, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Acceptance                                                          */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (EAGLE-1 explainer, "Verification"; EAGLE-2 explainer, "Key
+ * contributions": lossless by rejection sampling).  Target row 0 belongs to
+ * the root, row i + 1 to node i.
+ * GREEDY: from the root, accept the child whose token is the target argmax
+ *   (ties -> smallest id) of the current node's row; bonus = that argmax at
+ *   the last accepted node.
+ * SAMPLE (temperature T > 0): the children are the draft's deterministic
+ *   top choices, so the draft is a point mass on each of them.  At node u with
+ *   weights w of row u at temperature T and residual R = sum of w: children x
+ *   in index order are accepted iff r_x * R < w_tok(x) * 2^32 (exact integers,
+ *   r_x = rand_words[b][x]); a rejection subtracts w_tok(x) from R and removes
+ *   that token.  If none is accepted, the bonus is the smallest token v whose
+ *   inclusive cumulative residual weight exceeds floor(r * R / 2^32) with
+ *   r = rand_words[b][m_max].  The emitted tokens follow the target softmax.
+ * Inputs: target_logits [batch][m_max+1][row_stride]; tokens, parent
+ *   [batch][m_max] and num_nodes [batch] as produced by eagle_build_tree;
+ *   rand_words [batch][m_max+1] uint32 (SAMPLE only, may be NULL for GREEDY).
+ * Outputs: accepted [batch][max_accept] node ids root-first, -1 padded;
+ *   accept_len [batch]; bonus_token [batch].
+ * Errors: EAGLE_ERR_INVALID for null pointers, T <= 0 in SAMPLE mode;
+ * EAGLE_ERR_UNSUPPORTED past the v1 limits.
+ */
+typedef struct {
+    eagle_accept_mode mode;
+    float temperature;   /* SAMPLE only */
+    int32_t m_max;       /* <= 64 */
+    int32_t vocab;       /* <= 131072 */
+    int32_t max_accept;  /* width of `accepted`, >= the deepest node */
+} eagle_accept_params;
+
+size_t eagle_accept_workspace_size(const eagle_accept_params *a, int32_t batch);
+
+eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const void *target_logits,
+                          eagle_dtype dtype, int64_t row_stride, const int32_t *tokens,
+                          const int32_t *parent, const int32_t *num_nodes,
+                          const uint32_t *rand_words, int32_t *accepted, int32_t *accept_len,
+                          int32_t *bonus_token, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* ------------------------------------------------------------------ */
+const char *eagle_status_string(eagle_status s);
+const char *eagle_last_error(void); /* thread-local; never NULL */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_H */

@@ -283,3 +283,15 @@ def small_workload(base: int = 2, **over) -> Workload:
     if "kinds" not in over and len(w.kinds) != w.batch:
         w.kinds = [w.kinds[b % len(w.kinds)] for b in range(w.batch)]
     return w
+
+
+def step_dims(w: Workload, attn: AttnInputs) -> dict:
+    """Plain dimensions of one step for this workload and its attention inputs."""
+    return dict(
+        batch=w.batch, vocab=w.vocab, depth=w.depth, topk=w.topk, children=w.children, m=w.m,
+        chain_k=w.chain_k, m_max=w.m_max, r_max=w.r_max, max_accept=w.max_accept,
+        num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+        block_size=attn.block_size,
+        max_blocks=0 if attn.block_table is None else int(attn.block_table.shape[1]),
+        max_prefix=attn.max_prefix if attn.block_table is None else 0,
+        dtype=w.dtype, accept_mode=w.accept_mode, temperature=w.temperature)

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: libeagle.so loads, exports every function
+include/eagle.h declares, and rejects invalid arguments before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import eagle_tree_verification_draft_amd as E
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "eagle.h")
+
+
+def _declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"\b(eagle_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_match_header():
+    L = E.lib()
+    decl = _declared()
+    assert sorted(E.EXPORTS) == decl
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = E.lib()
+    for s in (0, -1, -2, -3, -4):
+        assert L.eagle_status_string(s)
+
+
+def _tree(**over):
+    d = dict(depth=6, topk=10, children=10, m=60, chain_k=0, vocab=32000, m_max=60, r_max=51)
+    d.update(over)
+    return E.TreeParams(**d)
+
+
+def _call_build(p, batch=1, logits=1 << 20, dtype=E.EAGLE_BF16, stride=None, ws=1 << 21, wsb=1 << 30):
+    L = E.lib()
+    out = C.c_void_p(1 << 24)
+    return L.eagle_build_tree(C.byref(p), batch, C.c_void_p(logits) if logits else None, dtype,
+                              p.vocab if stride is None else stride, None, out, out, out, out, out, out,
+                              C.c_void_p(ws) if ws else None, wsb, None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(m=0), E.EAGLE_ERR_INVALID),
+    (dict(m=61), E.EAGLE_ERR_INVALID),
+    (dict(m_max=65, m=60), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(children=17), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(vocab=(1 << 17) + 1), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(r_max=50), E.EAGLE_ERR_INVALID),
+    (dict(depth=0), E.EAGLE_ERR_INVALID),
+    (dict(chain_k=61), E.EAGLE_ERR_INVALID),
+    (dict(depth=8, topk=16, children=16, m=60), E.EAGLE_ERR_UNSUPPORTED),   # 1808 candidates
+])
+def test_build_tree_rejects_bad_params(over, want):
+    assert _call_build(_tree(**over)) == want
+    assert E.lib().eagle_last_error()
+
+
+def test_build_tree_rejects_null_stride_and_workspace():
+    p = _tree()
+    assert _call_build(p, logits=0) == E.EAGLE_ERR_INVALID
+    assert _call_build(p, stride=31999) == E.EAGLE_ERR_INVALID
+    assert _call_build(p, ws=0) == E.EAGLE_ERR_WORKSPACE
+    assert _call_build(p, wsb=16) == E.EAGLE_ERR_WORKSPACE
+    assert _call_build(p, ws=(1 << 21) + 8) == E.EAGLE_ERR_WORKSPACE          # misaligned
+    assert _call_build(p, dtype=7) == E.EAGLE_ERR_UNSUPPORTED
+    assert _call_build(_tree(vocab=100000), dtype=E.EAGLE_F32) == E.EAGLE_ERR_UNSUPPORTED
+    assert E.lib().eagle_build_tree_workspace_size(C.byref(_tree(m=0)), 1) == 0
+    assert E.lib().eagle_build_tree_workspace_size(C.byref(p), 4) > 0
+
+
+def _attn(**over):
+    d = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, m_max=60, block_size=16, max_blocks=4,
+             max_prefix=0, scale=0.0, dtype=E.EAGLE_BF16)
+    d.update(over)
+    return E.AttnParams(**d)
+
+
+def _call_attn(a, bt=True, align=0, ws=1 << 21, wsb=1 << 30):
+    L = E.lib()
+    p = C.c_void_p((1 << 24) + align)
+    return L.eagle_tree_attn(C.byref(a), 2, p, p, p, p, p, C.c_void_p(1 << 22) if bt else None,
+                             p, p, p, p, C.c_void_p(ws), wsb, None)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(num_q_heads=30), E.EAGLE_ERR_INVALID),
+    (dict(head_dim=64), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(dtype=E.EAGLE_F32, head_dim=96), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(m_max=65), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(block_size=12), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(max_blocks=0), E.EAGLE_ERR_INVALID),
+    (dict(scale=float("nan")), E.EAGLE_ERR_INVALID),
+])
+def test_tree_attn_rejects_bad_params(over, want):
+    assert _call_attn(_attn(**over)) == want
+
+
+def test_tree_attn_rejects_missing_table_misalignment_and_workspace():
+    assert _call_attn(_attn(), bt=False) == E.EAGLE_ERR_INVALID
+    assert _call_attn(_attn(), align=2) == E.EAGLE_ERR_UNSUPPORTED
+    assert _call_attn(_attn(), wsb=8) == E.EAGLE_ERR_WORKSPACE
+    assert E.lib().eagle_tree_attn_workspace_size(C.byref(_attn()), 2) >= 256
+
+
+def test_accept_and_mask_reject_bad_params():
+    L = E.lib()
+    p = C.c_void_p(1 << 24)
+    ws = C.c_void_p(1 << 21)
+    bad_t = E.AcceptParams(E.EAGLE_ACCEPT_SAMPLE, 0.0, 60, 32000, 6)
+    assert L.eagle_accept(C.byref(bad_t), 1, p, 1, 32000, p, p, p, p, p, p, p, ws, 256, None) == E.EAGLE_ERR_INVALID
+    no_words = E.AcceptParams(E.EAGLE_ACCEPT_SAMPLE, 1.0, 60, 32000, 6)
+    assert L.eagle_accept(C.byref(no_words), 1, p, 1, 32000, p, p, p, None, p, p, p, ws, 256, None) == E.EAGLE_ERR_INVALID
+    big = E.AcceptParams(E.EAGLE_ACCEPT_GREEDY, 1.0, 65, 32000, 6)
+    assert L.eagle_accept(C.byref(big), 1, p, 1, 32000, p, p, p, None, p, p, p, ws, 256, None) == E.EAGLE_ERR_UNSUPPORTED
+    ok = E.AcceptParams(E.EAGLE_ACCEPT_GREEDY, 1.0, 60, 32000, 6)
+    assert L.eagle_accept(C.byref(ok), 1, p, 1, 31999, p, p, p, None, p, p, p, ws, 256, None) == E.EAGLE_ERR_INVALID
+    assert L.eagle_accept(C.byref(ok), 1, p, 1, 32000, p, p, p, None, p, p, p, ws, 8, None) == E.EAGLE_ERR_WORKSPACE
+    assert L.eagle_tree_mask(1, 65, p, p, p, p, p, None, 0, None) == E.EAGLE_ERR_UNSUPPORTED
+    assert L.eagle_tree_mask(1, 60, None, p, p, p, p, None, 0, None) == E.EAGLE_ERR_INVALID
+    assert L.eagle_workspace_init(None, 0, None) == E.EAGLE_ERR_WORKSPACE
+
+
+def test_zero_batch_launches_nothing():
+    # batch 0 is valid and returns before touching any pointer or the GPU
+    L = E.lib()
+    p = _tree()
+    out = C.c_void_p(1 << 24)
+    assert L.eagle_build_tree(C.byref(p), 0, out, 1, 32000, None, out, out, out, out, out, out,
+                              C.c_void_p(1 << 21), 1 << 20, None) == E.EAGLE_OK

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Trees, masks and accepts must be bit-exact; attention
+within max-abs 2e-2 (bf16 inputs, fp32 accumulation) or 1e-5 (fp32)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import eagle_tree_verification_draft_amd as E
+import oracle
+import synth
+from conftest import to_np
+from gpu_harness import (BF16_TOL, F32_TOL, assert_accept_equal, assert_tree_equal, check_attn_rows,
+                         make_case, oracle_mask, run_gpu, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(w):
+    return F32_TOL if w.dtype == torch.float32 else BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module", params=[1, 2, 3, 4, 5])
+def full_case(request):
+    n = request.param
+    say(f"[full workload {n}] generating inputs")
+    w = synth.workload(n)
+    c = make_case(w, seed=100 + n)
+    say(f"[full workload {n}] running the step on the GPU")
+    run_gpu(c)
+    yield c
+    del c
+    torch.cuda.empty_cache()
+
+
+def test_full_tree(full_case):
+    assert_tree_equal(full_case)
+
+
+def test_full_mask(full_case):
+    c = full_case
+    anc, pos = oracle_mask(c)
+    assert np.array_equal(c.step.anc.cpu().numpy().view(np.uint64), anc)
+    assert np.array_equal(c.step.pos.cpu().numpy(), pos)
+
+
+def test_full_attention(full_case):
+    c = full_case
+    rng = np.random.default_rng(c.seed)
+    nn = c.otree["num_nodes"]
+    if int(nn.sum()) * c.w.num_q_heads <= 4096:      # every row
+        sel = [(b, i, h) for b in range(c.w.batch) for i in range(int(nn[b])) for h in range(c.w.num_q_heads)]
+    else:
+        sel = sample_rows(c, 192, rng)
+    # every node of sequence 0 for two heads, so every depth and branch is covered
+    for i in range(int(c.otree["num_nodes"][0])):
+        sel.append((0, i, 0))
+        sel.append((0, i, c.w.num_q_heads - 1))
+    err = check_attn_rows(c, sel, _tol(c.w))
+    say(f"[{c.w.name}] attention max-abs error {err:.3g} over {len(sel)} rows")
+    # padding rows are zeros
+    nn = c.otree["num_nodes"]
+    out = c.step.out.to(torch.float32).cpu().numpy()
+    for b in range(c.w.batch):
+        assert (out[b, int(nn[b]):] == 0).all()
+
+
+def test_full_accept(full_case):
+    alen = assert_accept_equal(full_case)
+    say(f"[{full_case.w.name}] mean accepted length {alen.mean():.2f}")
+
+
+def test_full_no_device_errors(full_case):
+    assert full_case.step.errors() == 0
+
+
+# ---------------------------------------------------------------------------
+# smaller cases: every code path, ragged sizes, degenerate inputs
+# ---------------------------------------------------------------------------
+def _small(base, **over):
+    w = synth.small_workload(base, **over)
+    return w
+
+
+SMALL = {
+    # fp32, vocab not a multiple of the vector width, ragged prefix
+    "f32-v1003-L77": lambda: _small(1, vocab=1003, prefix=77),
+    # fp32 GQA, head_dim 128, paged with poisoned tails
+    "f32-gqa-paged": lambda: _small(1, num_q_heads=8, num_kv_heads=2, head_dim=128, prefix=(1, 300),
+                                    block_size=16, batch=3, kinds=[0, 0, 0], poison_tail=True),
+    # bf16 contiguous, prefix shorter than one tile, and empty prefix
+    "bf16-L13": lambda: _small(2, prefix=13, vocab=5000),
+    "bf16-L0": lambda: _small(2, prefix=0, vocab=5000),
+    # bf16, many key splits for one sequence (ragged last split)
+    "bf16-split-L9000": lambda: _small(2, prefix=9001, vocab=4096, num_q_heads=4, num_kv_heads=4),
+    # GQA with two row groups (rows = 48 * 8 = 384)
+    "bf16-gqa8-rowgroups": lambda: _small(4, batch=2, prefix=700, vocab=3000),
+    # paged, mixed trees and chains, ragged lengths, poisoned tails
+    "bf16-paged-mixed": lambda: _small(5, batch=6, vocab=7001, prefix=(1, 5000),
+                                       kinds=[0, 1, 0, 1, 1, 0]),
+    # sampling at temperature 0.7
+    "bf16-rs-T0.7": lambda: dataclasses.replace(_small(3, batch=3, prefix=300, vocab=2000), temperature=0.7),
+    # tiny vocabulary: fewer elements than one thread block, exact fallback top-C
+    "f32-tiny-vocab": lambda: _small(1, vocab=37, children=16, depth=3, topk=4, m=40, prefix=40),
+    # chain only, K = depth 64 is not allowed (m_max <= 64), use K = 64 nodes
+    "bf16-chain64": lambda: _small(5, batch=2, kinds=[1, 1], chain_k=64, vocab=3000, prefix=(50, 200)),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def small_case(request):
+    w = SMALL[request.param]()
+    say(f"[small {request.param}] {w}")
+    c = make_case(w, seed=7, plant=(w.accept_mode == synth.ACCEPT_GREEDY))
+    run_gpu(c)
+    return c
+
+
+def test_small_all_outputs(small_case):
+    c = small_case
+    assert_tree_equal(c)
+    anc, pos = oracle_mask(c)
+    assert np.array_equal(c.step.anc.cpu().numpy().view(np.uint64), anc)
+    assert np.array_equal(c.step.pos.cpu().numpy(), pos)
+    sel = [(b, i, h) for b in range(c.w.batch) for i in range(int(c.otree["num_nodes"][b]))
+           for h in range(c.w.num_q_heads)]
+    check_attn_rows(c, sel, _tol(c.w))
+    assert_accept_equal(c)
+    assert c.step.errors() == 0
+
+
+def test_planted_paths_reach_full_depth():
+    w = _small(2, batch=2, vocab=6000, prefix=100)
+    c = make_case(w, seed=3, plant=True)
+    run_gpu(c)
+    alen = assert_accept_equal(c)
+    assert (alen == w.depth).all()
+
+
+def test_heavy_ties_use_exact_fallback():
+    # rows of only a few distinct values: thousands of candidates tie at the max
+    w = _small(2, batch=1, vocab=8192, prefix=64)
+    c = make_case(w, seed=5)
+    d = torch.zeros_like(c.draft)
+    d[:, :, ::3] = 1.0
+    d[:, :, 7::11] = -2.0
+    c.draft.copy_(d)
+    c.otree = oracle.build_tree(to_np(c.draft), w.depth, w.topk, w.children, w.m, m_max=w.m_max)
+    c.step.build(c.draft, c.kinds)
+    torch.cuda.synchronize()
+    assert_tree_equal(c)
+
+
+def test_determinism():
+    w = _small(5, batch=4, vocab=9000, prefix=(100, 3000), kinds=[0, 1, 0, 0])
+    c = make_case(w, seed=11)
+    outs = []
+    for _ in range(3):
+        run_gpu(c)
+        outs.append([t.clone() for t in (c.step.tokens, c.step.score, c.step.anc, c.step.out, c.step.accepted,
+                                         c.step.bonus)])
+    for o in outs[1:]:
+        for x, y in zip(outs[0], o):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+
+
+def test_device_error_bits():
+    w = _small(2, batch=2, vocab=4000, prefix=100)
+    c = make_case(w, seed=13)
+    c.draft[1, 3, 17] = float("nan")
+    c.step.build(c.draft, c.kinds)
+    torch.cuda.synchronize()
+    assert E.read_errors(c.step.ws_tree) & E.DEVERR_NONFINITE_ROW
+    # prefix longer than the cache: clamped and reported
+    bad = c.attn.prefix_len.clone()
+    bad[0] = c.attn.max_prefix + 5
+    c.step.mask(bad)
+    c.step.attention(c.attn.q, c.attn.k_draft, c.attn.v_draft, c.attn.k_cache, c.attn.v_cache, None, bad)
+    torch.cuda.synchronize()
+    assert E.read_errors(c.step.ws_attn) & E.DEVERR_PREFIX
+    assert E.read_errors(c.step.ws_attn) == 0   # reading clears
+
+
+# ---------------------------------------------------------------------------
+# rejection sampling on the GPU: 10^6 trials, bit-exact and distribution
+# ---------------------------------------------------------------------------
+def test_rejection_sampling_million_trials():
+    import scipy.stats
+    V, n = 8, 1_000_000
+    rng = np.random.default_rng(21)
+    target1 = (rng.standard_normal((1, 4, V)) * 1.5).astype(np.float32)
+    tok = np.array([[2, 5, 7]], np.int32)
+    par = np.array([[-1, -1, 0]], np.int32)
+    words = rng.integers(0, 1 << 32, size=(n, 4), dtype=np.uint64).astype(np.uint32)
+    tg = np.ascontiguousarray(np.broadcast_to(target1, (n, 4, V)))
+    toks = np.ascontiguousarray(np.broadcast_to(tok, (n, 3)))
+    pars = np.ascontiguousarray(np.broadcast_to(par, (n, 3)))
+    nn = np.full(n, 3, np.int32)
+    o_acc, o_len, o_bon = oracle.accept(1, tg, toks, pars, nn, 2, rand_words=words)
+    dev = "cuda"
+    a = E.AcceptParams(E.EAGLE_ACCEPT_SAMPLE, 1.0, 3, V, 2)
+    ws = torch.empty(E.accept_workspace_size(a, n), dtype=torch.uint8, device=dev)
+    E.workspace_init(ws)
+    acc = torch.empty((n, 2), dtype=torch.int32, device=dev)
+    alen = torch.empty(n, dtype=torch.int32, device=dev)
+    bon = torch.empty(n, dtype=torch.int32, device=dev)
+    E.accept(a, n, torch.from_numpy(tg).to(dev), torch.from_numpy(toks).to(dev), torch.from_numpy(pars).to(dev),
+             torch.from_numpy(nn).to(dev), torch.from_numpy(words.view(np.int32)).to(dev), acc, alen, bon, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), o_acc)
+    assert np.array_equal(alen.cpu().numpy(), o_len)
+    assert np.array_equal(bon.cpu().numpy(), o_bon)
+    first = np.where(o_len > 0, tok[0][np.maximum(o_acc[:, 0], 0)], o_bon)
+    lf = target1[0, 0]
+    p = np.exp(lf.astype(np.float64) - lf.max())
+    p /= p.sum()
+    chi = scipy.stats.chisquare(np.bincount(first, minlength=V), p * n)
+    assert chi.pvalue > 1e-3
