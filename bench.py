@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of one EAGLE-2 draft-tree verification step on one MI355X.
+
+A step is the whole hot path on one stream: eagle_build_tree (draft-row
+softmax statistics, top-C children, expansion, rerank, compaction),
+eagle_tree_mask, eagle_tree_attn and eagle_accept, over one batch of
+synthetic inputs already resident in HBM.  The default workload is the
+Llama-2-7B-shaped one (batch 1, bf16, 32 heads x 128, prefix 2048, vocab
+32000, depth 6, k = 10, m = 60, greedy).  Prints one JSON line.
+
+Inputs: seeded synthetic draft/target logits and Q/K/V (random numbers stand
+in for trained models and text benchmarks).  The timed steps rotate over
+enough independent input sets to exceed the 256 MB Infinity Cache, so every
+step reads its inputs from HBM ("cold"); a warm figure (one set repeated) is
+reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config N]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: enough to exceed the MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only", action="store_true", help="time only eagle_tree_attn (for profiling runs)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_algorithmic(w, attn, num_nodes):
+    """HBM bytes and flops the attention call must move/do: every prefix K/V
+    byte once per kv head, the draft K/V, Q and the output once; flops of
+    q.k and p.v over prefix + ancestor keys."""
+    import torch
+    esz = 4 if w.dtype == torch.float32 else 2
+    d, Hq, Hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
+    L = attn.prefix_len.to("cpu").to(torch.int64)
+    nn = num_nodes.to("cpu").to(torch.int64)
+    kv = int(L.sum()) * Hkv * d * 2 * esz
+    qo = int(nn.sum()) * Hq * d * esz * 2
+    dkv = int(nn.sum()) * Hkv * d * 2 * esz
+    flops = 4 * d * Hq * int((nn * L).sum())
+    return kv + qo + dkv, flops
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification step of one "
+              "sequence batch does not span GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import eagle_tree_verification_draft_amd as E
+    import synth
+
+    dev = "cuda"
+    w = synth.workload(args.config)
+    base_seed = 5000 + 100 * args.config
+
+    # ---- input sets ----------------------------------------------------
+    def make_set(i, step):
+        seed = base_seed + i
+        draft = synth.draft_logits(w, seed, dev)
+        attn = synth.attn_inputs(w, seed, dev, prefix_seed=base_seed)
+        step.build(draft, kinds)
+        torch.cuda.synchronize()
+        target = synth.target_logits(w, seed, draft, step.src_row.cpu(), step.num_nodes.cpu(), dev)
+        words = synth.rand_words(w, seed, dev) if w.accept_mode == synth.ACCEPT_SAMPLE else None
+        return dict(draft=draft, attn=attn, target=target, words=words)
+
+    kinds = synth.kinds_tensor(w, dev)
+    log(f"[bench] workload {w.name}: generating inputs")
+    attn0 = synth.attn_inputs(w, base_seed, dev, prefix_seed=base_seed)
+    step = E.VerifyStep(E.StepShape(**synth.step_dims(w, attn0)), dev)
+    first = dict(draft=synth.draft_logits(w, base_seed, dev), attn=attn0)
+    step.build(first["draft"], kinds)
+    torch.cuda.synchronize()
+    first["target"] = synth.target_logits(w, base_seed, first["draft"], step.src_row.cpu(), step.num_nodes.cpu(), dev)
+    first["words"] = synth.rand_words(w, base_seed, dev) if w.accept_mode == synth.ACCEPT_SAMPLE else None
+    set_bytes = sum(t.numel() * t.element_size() for t in
+                    (first["draft"], first["target"], attn0.q, attn0.k_draft, attn0.v_draft, attn0.k_cache,
+                     attn0.v_cache))
+    nsets = args.sets or max(2, math.ceil(2 * MALL_BYTES / set_bytes))
+    nsets = min(nsets, 64)
+    sets = [first] + [make_set(i, step) for i in range(1, nsets)]
+    tokens_per_step = int(step.num_nodes.sum().item())
+    log(f"[bench] {nsets} input sets of {set_bytes / 1e6:.1f} MB; {tokens_per_step} verified tokens per step")
+
+    def run_step(S, ev=None):
+        a = S["attn"]
+        if not args.attn_only:
+            step.build(S["draft"], kinds)
+            step.mask(a.prefix_len)
+        if ev is not None:
+            ev[0].record()
+        step.attention(a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table, a.prefix_len)
+        if ev is not None:
+            ev[1].record()
+        if not args.attn_only:
+            step.accept(S["target"], S["words"])
+
+    # ---- warm-up and the timed region (cold: sets rotate) ----------------
+    for k in range(args.warmup):
+        run_step(sets[k % nsets])
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        run_step(sets[k % nsets], evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_ms = float(np.mean(attn_ms))
+    log(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us")
+
+    # ---- per-stage breakdown (separate loop, events between the calls) ---
+    stage_names = ["build_tree", "tree_mask", "tree_attn", "accept"]
+    n_stage = min(K, 100)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_stage)]
+    for k in range(n_stage):
+        S = sets[k % nsets]
+        a = S["attn"]
+        e = sev[k]
+        e[0].record()
+        step.build(S["draft"], kinds)
+        e[1].record()
+        step.mask(a.prefix_len)
+        e[2].record()
+        step.attention(a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table, a.prefix_len)
+        e[3].record()
+        step.accept(S["target"], S["words"])
+        e[4].record()
+    torch.cuda.synchronize()
+    stage_us = {n: float(np.median([sev[k][j].elapsed_time(sev[k][j + 1]) for k in range(n_stage)])) * 1e3
+                for j, n in enumerate(stage_names)}
+
+    # ---- warm: one set repeated ------------------------------------------
+    for _ in range(5):
+        run_step(sets[0])
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    for _ in range(K):
+        run_step(sets[0])
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - tw0) * 1e3 / K
+
+    errs = step.errors()
+    if errs:
+        log(f"[bench] WARNING: device error bits {errs:#x}")
+
+    nbytes, flops = attn_algorithmic(w, attn0, step.num_nodes)
+    achieved = nbytes / (attn_avg_ms * 1e-3) / 1e9
+    mfma_frac = flops / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    value = tokens_per_step / (ms_per_step * 1e-3)
+
+    # ---- the oracle on the host cores (bounded sample) -------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, sets[0], base_seed, tokens_per_step, args.cpu_seconds)
+
+    out = {
+        "metric": "verified tree tokens/s (build+tree-attn+accept), % of HBM/MFMA peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "vocab": w.vocab, "depth": w.depth, "topk": w.topk,
+                   "m": w.m, "heads": f"{w.num_q_heads}q/{w.num_kv_heads}kv x {w.head_dim}",
+                   "prefix": w.prefix if isinstance(w.prefix, int) else list(w.prefix),
+                   "kv_layout": "paged16" if w.block_size else "contiguous",
+                   "accept": "greedy" if w.accept_mode == synth.ACCEPT_GREEDY else f"sample T={w.temperature}",
+                   "input_sets": nsets, "cold": True},
+        "roofline": {"kernel": "k_tree_attn_bf16" if w.dtype == torch.bfloat16 else "k_tree_attn_f32",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes, "avg_us": round(attn_avg_ms * 1e3, 2),
+                     "mfma_frac": round(mfma_frac, 4)},
+        "cpu_baseline": cpu,
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
+        "tokens_per_step": tokens_per_step,
+        "device": torch.cuda.get_device_name(0),
+        "device_errors": errs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, S, seed, tokens_per_step, budget_s):
+    """The oracle as it stands, timed on the host cores on the same inputs
+    (host copies of input set 0): full steps until the budget is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    def h(t):
+        t = t.detach().to("cpu").contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    a = S["attn"]
+    draft, q, kd, vd = h(S["draft"]), h(a.q), h(a.k_draft), h(a.v_draft)
+    kc, vc = h(a.k_cache), h(a.v_cache)
+    bt = None if a.block_table is None else h(a.block_table)
+    plen = h(a.prefix_len)
+    words = None if S["words"] is None else h(S["words"])
+    # the oracle's own tree defines the target rows it verifies against
+    ot = oracle.build_tree(draft, w.depth, w.topk, w.children, w.m, chain_k=w.chain_k, kinds=w.kinds, m_max=w.m_max)
+    target = h(synth.target_logits(w, seed, S["draft"].cpu(), torch.from_numpy(ot["src_row"]),
+                                   torch.from_numpy(ot["num_nodes"])))
+    n_steps, t0 = 0, time.perf_counter()
+    while True:
+        t = oracle.build_tree(draft, w.depth, w.topk, w.children, w.m, chain_k=w.chain_k, kinds=w.kinds,
+                              m_max=w.m_max)
+        anc, pos = oracle.tree_mask(t["parent"], t["num_nodes"], plen)
+        oracle.tree_attn(q, kd, vd, kc, vc, bt, plen, anc, t["num_nodes"])
+        oracle.accept(w.accept_mode, target, t["tokens"], t["parent"], t["num_nodes"], w.max_accept,
+                      rand_words=words, T=w.temperature)
+        n_steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (n_steps >= 1 and el * (n_steps + 1) / n_steps > 3 * budget_s):
+            break
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(tokens_per_step * n_steps / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_steps} full oracle steps (tree build, mask, fp64 attention over every row, accept) "
+                      f"on input set 0 in {el:.1f} s",
+            "host_cpu": cpu_model or platform.processor(), "nproc": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

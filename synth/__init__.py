@@ -220,10 +220,12 @@ class AttnInputs:
     max_prefix: int
 
 
-def attn_inputs(w: Workload, seed: int, device="cpu") -> AttnInputs:
-    """Q, draft K/V and the KV prefix, all N(0,1) in the workload dtype."""
+def attn_inputs(w: Workload, seed: int, device="cpu", prefix_seed: Optional[int] = None) -> AttnInputs:
+    """Q, draft K/V and the KV prefix, all N(0,1) in the workload dtype.
+    prefix_seed (default: seed) draws the prefix lengths and the block table."""
     B, M, Hq, Hkv, d = w.batch, w.m_max, w.num_q_heads, w.num_kv_heads, w.head_dim
-    plen = prefix_lengths(w, seed)
+    pseed = seed if prefix_seed is None else prefix_seed
+    plen = prefix_lengths(w, pseed)
     q = _normal((B, M, Hq, d), 1.0, w.dtype, _gen(seed, "q", device), device)
     gdk = _gen(seed, "draft_kv", device)
     k_draft = _normal((B, M, Hkv, d), 1.0, w.dtype, gdk, device)
@@ -238,7 +240,7 @@ def attn_inputs(w: Workload, seed: int, device="cpu") -> AttnInputs:
     nblk = [(int(x) + bs - 1) // bs for x in plen]
     total = sum(nblk)
     maxb = max(nblk)
-    gperm = _gen(seed, "blocks", "cpu")
+    gperm = _gen(pseed, "blocks", "cpu")
     perm = torch.randperm(total, generator=gperm).to(torch.int32)
     table = torch.full((B, maxb), -1, dtype=torch.int32)
     o = 0
