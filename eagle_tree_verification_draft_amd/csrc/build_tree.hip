@@ -19,7 +19,9 @@ namespace eagle {
 //   block argmax over the row select exactly.
 // ---------------------------------------------------------------------------
 constexpr int kCandCap = 2048;
-constexpr int kRowThreadsMax = 512;
+
+// threads per row: up to 1024 while a row fits 8 vectors per thread, 512 above
+template <int kNV> struct RowMaxThreads { static constexpr int n = kNV <= 8 ? 1024 : 512; };
 
 template <typename T> struct Vec;
 template <> struct Vec<float> { static constexpr int n = 4; };
@@ -87,7 +89,7 @@ struct RowStatsSmem {
 };
 
 template <typename T, int kNV>
-__global__ __launch_bounds__(kRowThreadsMax) void k_row_stats(RowStatsArgs a)
+__global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArgs a)
 {
     constexpr int VEC = Vec<T>::n;
     __shared__ RowStatsSmem sm;
@@ -207,58 +209,46 @@ __global__ __launch_bounds__(kRowThreadsMax) void k_row_stats(RowStatsArgs a)
 
 // ---------------------------------------------------------------------------
 // Kernel 2: one workgroup per sequence.  Candidates live in LDS in creation
-// order; sorting by (V desc, creation asc) is a bottom-up merge sort whose
-// merge step places each element by a binary search in its partner run.
+// order.  Depth by depth: each depth-d candidate's rank among depth-d
+// candidates in (V desc, creation asc) is counted by all threads at once (the
+// comparisons are split into groups whose partial counts are added with LDS
+// atomics); the top-k by that rank are expanded; then the depth's sorted list
+// is merged into the running sorted list of the best m candidates seen so far
+// (each element finds its merged position by a binary search in the other
+// list).  After the last depth that list is the rerank's top-m in rank order.
 // ---------------------------------------------------------------------------
-struct Key {
-    double v;
-    int i;
-    int pad;
-};
-
-__device__ __forceinline__ bool key_before(const Key &a, const Key &b)
-{
-    return a.v > b.v || (a.v == b.v && a.i < b.i);
-}
-
-// Sorts keys[0..n) in place (scratch holds n more).  Returns the buffer that
-// holds the result (keys or scratch).
-__device__ Key *merge_sort_keys(Key *keys, Key *scratch, int n)
-{
-    Key *src = keys, *dst = scratch;
-    for (int width = 1; width < n; width <<= 1) {
-        for (int e = threadIdx.x; e < n; e += blockDim.x) {
-            const int start = (e / (2 * width)) * (2 * width);
-            const int mid = min(start + width, n), end = min(start + 2 * width, n);
-            const Key me = src[e];
-            int lo, hi, own;
-            if (e < mid) { lo = mid; hi = end; own = e - start; }
-            else { lo = start; hi = mid; own = e - mid; }
-            // count elements of [lo, hi) that come before `me` (a prefix of the run)
-            int a = lo, c = hi;
-            while (a < c) {
-                const int md = (a + c) >> 1;
-                if (key_before(src[md], me)) a = md + 1; else c = md;
-            }
-            dst[start + own + (a - lo)] = me;
-        }
-        __syncthreads();
-        Key *t = src; src = dst; dst = t;
-    }
-    return src;
-}
-
 struct TreeSmem {
-    Key keys[kMaxCand];
-    Key scratch[kMaxCand];
     double V[kMaxCand];
     int tok[kMaxCand];
     int par[kMaxCand];
     int dep[kMaxCand];
     int row[kMaxCand];
     int rank_of[kMaxCand];
+    int rankd[kMaxCand];
+    int sortedD[kMaxCand];
+    double rowW[kMaxRows];                  // W of every row this sequence uses
+    double rowCw[kMaxRows * kMaxChildren];  // top-C weights
+    int rowCid[kMaxRows * kMaxChildren];    // top-C token ids
+    int S[kMaxMMax];
+    int Snew[kMaxMMax];
     int exp_par[kMaxTopk];
 };
+
+__device__ __forceinline__ bool cand_before(const TreeSmem &sm, int a, int b)
+{
+    return sm.V[a] > sm.V[b] || (sm.V[a] == sm.V[b] && a < b);
+}
+
+// number of leading entries of list[0..len) that come before candidate x
+__device__ __forceinline__ int count_before(const TreeSmem &sm, const int *list, int len, int x)
+{
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int md = (lo + hi) >> 1;
+        if (cand_before(sm, list[md], x)) lo = md + 1; else hi = md;
+    }
+    return lo;
+}
 
 __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
 {
@@ -293,61 +283,95 @@ __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
     }
 
     const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
+    // all row statistics of this sequence -> LDS in one parallel pass
+    const int R = 1 + (D - 1) * k;
+    for (int i = tid; i < R * C; i += NT) {
+        const int r = i / C, j = i % C;
+        sm.rowCw[i] = a.top_w[(rb + r) * Cw + j];
+        sm.rowCid[i] = a.top_id[(rb + r) * Cw + j];
+    }
+    for (int r = tid; r < R; r += NT) sm.rowW[r] = a.W[rb + r];
+    __syncthreads();
     // depth 1: children of the root's row 0
     for (int j = tid; j < C; j += NT) {
-        sm.V[j] = a.top_w[rb * Cw + j] / a.W[rb];
-        sm.tok[j] = a.top_id[rb * Cw + j];
+        sm.V[j] = sm.rowCw[j] / sm.rowW[0];
+        sm.tok[j] = sm.rowCid[j];
         sm.par[j] = -1;
         sm.dep[j] = 1;
         sm.row[j] = -1;
     }
-    __syncthreads();
-    int begin = 0, end = C;
-    for (int d = 1; d <= D - 1; ++d) {
-        const int cnt = end - begin;
-        for (int i = tid; i < cnt; i += NT) sm.keys[i] = Key{sm.V[begin + i], begin + i, 0};
+    int begin = 0, end = C, sN = 0;
+    for (int d = 1; d <= D; ++d) {
+        const int nd = end - begin;
+        for (int i = tid; i < nd; i += NT) sm.rankd[i] = 0;
         __syncthreads();
-        const Key *sorted = merge_sort_keys(sm.keys, sm.scratch, cnt);
-        const int ne = cnt < k ? cnt : k;
-        for (int p = tid; p < ne; p += NT) {
-            const int pidx = sorted[p].i;
-            sm.exp_par[p] = pidx;
-            sm.row[pidx] = 1 + (d - 1) * k + p;
+        // ---- rank within the depth: groups of comparisons per candidate ----
+        const int G = max(1, min(nd, NT / max(nd, 1)));
+        const int per = (nd + G - 1) / G;
+        for (int t = tid; t < nd * G; t += NT) {
+            const int i = t % nd, g = t / nd;
+            const int j0 = g * per, j1 = min(nd, j0 + per);
+            const int xi = begin + i;
+            int cnt = 0;
+            for (int j = j0; j < j1; ++j) cnt += cand_before(sm, begin + j, xi) ? 1 : 0;
+            if (cnt) atomicAdd(&sm.rankd[i], cnt);
         }
         __syncthreads();
-        for (int t = tid; t < ne * C; t += NT) {
-            const int p = t / C, j = t % C;
-            const int pidx = sm.exp_par[p];
-            const size_t r = rb + 1 + (size_t)(d - 1) * k + p;
-            const double c = a.top_w[r * Cw + j] / a.W[r];
-            sm.V[end + t] = sm.V[pidx] * c;
-            sm.tok[end + t] = a.top_id[r * Cw + j];
-            sm.par[end + t] = pidx;
-            sm.dep[end + t] = d + 1;
-            sm.row[end + t] = -1;
+        for (int i = tid; i < nd; i += NT) sm.sortedD[sm.rankd[i]] = begin + i;
+        __syncthreads();
+        // ---- expansion: the p-th best depth-d node owns row 1 + (d-1)k + p ----
+        int ne = 0;
+        if (d < D) {
+            ne = nd < k ? nd : k;
+            for (int p = tid; p < ne; p += NT) {
+                const int pidx = sm.sortedD[p];
+                sm.exp_par[p] = pidx;
+                sm.row[pidx] = 1 + (d - 1) * k + p;
+            }
+            __syncthreads();
+            for (int t = tid; t < ne * C; t += NT) {
+                const int p = t / C, j = t % C;
+                const int pidx = sm.exp_par[p];
+                const int r = 1 + (d - 1) * k + p;
+                const double c = sm.rowCw[r * C + j] / sm.rowW[r];
+                sm.V[end + t] = sm.V[pidx] * c;
+                sm.tok[end + t] = sm.rowCid[r * C + j];
+                sm.par[end + t] = pidx;
+                sm.dep[end + t] = d + 1;
+                sm.row[end + t] = -1;
+            }
         }
+        // ---- merge this depth's sorted list into the best-m list ----
+        for (int p = tid; p < nd; p += NT) {
+            const int x = sm.sortedD[p];
+            const int pos = p + count_before(sm, sm.S, sN, x);
+            if (pos < m) sm.Snew[pos] = x;
+        }
+        for (int q = tid; q < sN; q += NT) {
+            const int y = sm.S[q];
+            const int pos = q + count_before(sm, sm.sortedD, nd, y);
+            if (pos < m) sm.Snew[pos] = y;
+        }
+        sN = min(m, sN + nd);
+        __syncthreads();
+        for (int q = tid; q < sN; q += NT) sm.S[q] = sm.Snew[q];
         __syncthreads();
         begin = end;
         end += ne * C;
     }
-    const int N = end;
-    // rerank: the first m of all candidates in (V desc, creation asc)
-    for (int i = tid; i < N; i += NT) {
-        sm.keys[i] = Key{sm.V[i], i, 0};
-        sm.rank_of[i] = -1;
-    }
+    const int N = begin;
+    for (int i = tid; i < N; i += NT) sm.rank_of[i] = -1;
     __syncthreads();
-    const Key *sorted = merge_sort_keys(sm.keys, sm.scratch, N);
-    for (int r = tid; r < m; r += NT) sm.rank_of[sorted[r].i] = r;
+    for (int r = tid; r < m; r += NT) sm.rank_of[sm.S[r]] = r;
     __syncthreads();
     // connected tree check (holds by construction: V never grows along a path)
     for (int r = tid; r < m; r += NT) {
-        int q = sm.par[sorted[r].i];
+        const int i = sm.S[r];
+        int q = sm.par[i];
         while (q >= 0) {
             if (sm.rank_of[q] < 0) { raise_error(a.err, EAGLE_DEVERR_CLOSURE); break; }
             q = sm.par[q];
         }
-        const int i = sorted[r].i;
         tokens[r] = sm.tok[i];
         parent[r] = sm.par[i] < 0 ? -1 : sm.rank_of[sm.par[i]];
         depth[r] = sm.dep[i];
@@ -376,12 +400,14 @@ BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
     return L;
 }
 
-// vectors per thread (16 or 32) and threads per row so one row fits the
-// registers of at most kRowThreadsMax threads; 0 if it does not fit
+// vectors per thread (4, 8, 16 or 32) and threads per row so that one row
+// fits the registers of one workgroup; 0 if it does not fit
 int row_vectors(int vocab, int vec)
 {
-    if (vocab <= kRowThreadsMax * 16 * vec) return 16;
-    if (vocab <= kRowThreadsMax * 32 * vec) return 32;
+    if (vocab <= 1024 * 4 * vec) return 4;
+    if (vocab <= 1024 * 8 * vec) return 8;
+    if (vocab <= 512 * 16 * vec) return 16;
+    if (vocab <= 512 * 32 * vec) return 32;
     return 0;
 }
 
@@ -422,14 +448,20 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     if (batch > 0 && p->r_max > 0) {
         const int vec = dt == EAGLE_F32 ? 4 : 8;
         const dim3 blk(row_threads(p->vocab, vec));
-        const bool nv16 = row_vectors(p->vocab, vec) == 16;
+        const int nv = row_vectors(p->vocab, vec);
+#define EAGLE_ROWS(T, NV) hipLaunchKernelGGL((k_row_stats<T, NV>), g1, blk, 0, st, ra)
         if (dt == EAGLE_F32) {
-            if (nv16) hipLaunchKernelGGL((k_row_stats<float, 16>), g1, blk, 0, st, ra);
-            else hipLaunchKernelGGL((k_row_stats<float, 32>), g1, blk, 0, st, ra);
+            if (nv == 4) EAGLE_ROWS(float, 4);
+            else if (nv == 8) EAGLE_ROWS(float, 8);
+            else if (nv == 16) EAGLE_ROWS(float, 16);
+            else EAGLE_ROWS(float, 32);
         } else {
-            if (nv16) hipLaunchKernelGGL((k_row_stats<uint16_t, 16>), g1, blk, 0, st, ra);
-            else hipLaunchKernelGGL((k_row_stats<uint16_t, 32>), g1, blk, 0, st, ra);
+            if (nv == 4) EAGLE_ROWS(uint16_t, 4);
+            else if (nv == 8) EAGLE_ROWS(uint16_t, 8);
+            else if (nv == 16) EAGLE_ROWS(uint16_t, 16);
+            else EAGLE_ROWS(uint16_t, 32);
         }
+#undef EAGLE_ROWS
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -453,7 +485,7 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ta.num_nodes = num_nodes;
     ta.err = ra.err;
     if (batch > 0) {
-        hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(256), 0, st, ta);
+        hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(512), 0, st, ta);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -63,6 +63,7 @@ eagle_status check_tree_params(const eagle_tree_params *p, int32_t batch)
     if (p->m < 1 || p->m > p->m_max || p->m > N)
         return fail(EAGLE_ERR_INVALID, "m %d not in [1, min(m_max %d, candidates %lld)]", p->m, p->m_max, N);
     const long long rows_dyn = 1 + (long long)(p->depth - 1) * p->topk;
+    if (rows_dyn > kMaxRows) return fail(EAGLE_ERR_UNSUPPORTED, "dynamic trees use %lld rows > %d", rows_dyn, kMaxRows);
     if (rows_dyn > p->r_max) return fail(EAGLE_ERR_INVALID, "dynamic trees use %lld rows > r_max %d", rows_dyn, p->r_max);
     if (p->chain_k < 0 || p->chain_k > p->m_max || p->chain_k > p->r_max)
         return fail(EAGLE_ERR_INVALID, "chain_k %d not in [0, min(m_max, r_max)]", p->chain_k);

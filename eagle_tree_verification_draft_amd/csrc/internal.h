@@ -13,6 +13,7 @@ namespace eagle {
 constexpr int kMaxCand = 1024;   // generated candidates per dynamic tree
 constexpr int kMaxTopk = 64;     // nodes expanded per depth
 constexpr int kMaxDepth = 64;
+constexpr int kMaxRows = 128;    // draft rows one dynamic tree uses: 1 + (D-1)k
 
 // ---- tree build ----------------------------------------------------------
 struct RowStatsArgs {

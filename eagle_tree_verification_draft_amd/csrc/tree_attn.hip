@@ -68,16 +68,49 @@ __device__ __forceinline__ const T *v_elem(const AttnArgs &a, int b, int kvh, in
     return vc + (((size_t)blk * a.Hkv + kvh) * a.d + e) * (size_t)a.block_size + key % a.block_size;
 }
 
+constexpr int kTileChunks = kTK * kHD * 2 / 16;   // 16-byte chunks per K (or V^T) tile: 1024
+constexpr int kMaxPages = 4096 / 8 + 2;             // pages of one split (chunk <= 4096, page >= 8)
+
+typedef unsigned int u32x4a __attribute__((ext_vector_type(4)));
+
+// One LDS buffer: K tile [64 keys][128 dims] and V^T tile [128 dims][64 keys],
+// bf16, rows unpadded.  Row r of K holds key swap23(r); its 16-byte chunk J
+// (dims 8J..8J+7) sits at position J ^ (r & 15).  Row e of V^T holds keys
+// chunk J (keys 8J..8J+7) at position J ^ ((e >> 1) & 7).  With these XOR
+// swizzles the MFMA operand reads (32 rows, one chunk each) hit distinct banks
+// in every group of 8 lanes, and every wave's direct global->LDS load writes
+// 1 KB contiguously.
+struct AttnBuf {
+    u32x4a K[kTK * 16];
+    u32x4a Vt[kHD * 8];
+};
+
 struct AttnSmem {
-    uint16_t K[kTK * kKS];
-    uint16_t Vt[kHD * kVS];
+    union {
+        AttnBuf buf[2];
+        float wgt[2 * (kTK * 16 + kHD * 8) * 4];     // combine: per-split weights of each row
+    } u;
+    int bt[kMaxPages];
     int last;
 };
+
+__device__ __forceinline__ int kpos(int r, int J) { return r * 16 + (J ^ (r & 15)); }
+__device__ __forceinline__ int vpos(int e, int J) { return e * 8 + (J ^ ((e >> 1) & 7)); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4a v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
+// (dst must be the same for the whole wave)
+__device__ __forceinline__ void load_lds16(const void *src, void *dst_wave)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst_wave, 16, 0, 0);
+}
 
 __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
 {
     __shared__ AttnSmem sm;
-    const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = NT >> 6;
     const int ln = lane & 31, hh = lane >> 5;
     // block -> (split, row group, sequence/kv head); all splits and row groups
     // of one (sequence, kv head) share blockIdx mod 8 when units0 % 8 == 0,
@@ -100,10 +133,20 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
     if (s >= nsplit_b) return;
     const int key_lo = s * a.chunk, key_hi = min(L, key_lo + a.chunk);
     const bool has_draft = (s == nsplit_b - 1);
+    const bool paged = a.block_size != 0;
+    const int bs = a.block_size;
+    const int page0 = paged ? key_lo / bs : 0;
+
+    // pages of this split -> LDS
+    if (paged && key_hi > key_lo) {
+        const int np = (key_hi - 1) / bs - page0 + 1;
+        for (int i = tid; i < np; i += NT) sm.bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
+    }
 
     const int row0 = rg * a.rows_pg + wv * 32;          // first row of this wave
     const int rows_valid = n * G;                        // rows with a real node
     const bool wave_active = row0 < rows_valid && wv * 32 < a.rows_pg;
+    const bool wave_full = row0 + 32 <= rows_valid;
     const int my_row = row0 + ln;
     const int my_node = my_row / G;
     const bool row_ok = my_row < rows_valid;
@@ -111,142 +154,197 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
     // Q fragments (B operand of S^T = K Q^T): lane holds q[my_row][16ks + 8hh .. +7]
     bf16x8 qf[8];
     {
-        const uint16_t *qb = static_cast<const uint16_t *>(a.q);
-        const int h = kvh * G + (my_row % G);
+        const u32x4a *qrow = reinterpret_cast<const u32x4a *>(
+            static_cast<const uint16_t *>(a.q) +
+            (((size_t)b * m_max + (my_node < m_max ? my_node : 0)) * a.Hq + kvh * G + (my_row % G)) * kHD);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (wave_active && my_node < m_max)
-                v = *reinterpret_cast<const uint4 *>(qb + (((size_t)b * m_max + my_node) * a.Hq + h) * kHD +
-                                                     16 * ks + 8 * hh);
-            qf[ks] = __builtin_bit_cast(bf16x8, v);
+            u32x4a v = {0, 0, 0, 0};
+            if (wave_active && my_node < m_max) v = qrow[2 * ks + hh];
+            qf[ks] = as_bf16x8(v);
         }
     }
     uint64_t my_anc = 0;
     if (row_ok) my_anc = a.anc[(size_t)b * m_max + my_node];
+    __syncthreads();   // sm.bt visible
+
+    const uint16_t *kc = static_cast<const uint16_t *>(a.kc);
+    const uint16_t *vc = static_cast<const uint16_t *>(a.vc);
+    const size_t kvbase = (size_t)b * a.Hkv + kvh;      // contiguous cache: (b, kvh) slab
+    const uint16_t *kslab = paged ? kc : kc + kvbase * (size_t)a.cap * kHD;
+    const uint16_t *vslab = paged ? vc : vc + kvbase * (size_t)kHD * a.cap;
+
+    const int nprefix = (key_hi - key_lo + kTK - 1) / kTK;
+    const int ntiles = nprefix + (has_draft ? 1 : 0);
+    // a tile goes global->LDS directly when all 64 keys are valid (and, for a
+    // contiguous cache, V^T rows are 16-byte aligned); otherwise it is staged
+    // through registers with explicit zeros
+    auto direct = [&](int tile) {
+        return tile < nprefix && key_lo + (tile + 1) * kTK <= key_hi && (paged || a.v_vec);
+    };
+    auto k_src = [&](int key, int J) -> const uint16_t * {
+        if (!paged) return kslab + (size_t)key * kHD + J * 8;
+        const int blk = sm.bt[key / bs - page0];
+        return kc + (((size_t)blk * a.Hkv + kvh) * bs + key % bs) * kHD + J * 8;
+    };
+    auto v_src = [&](int e, int key) -> const uint16_t * {
+        if (!paged) return vslab + (size_t)e * a.cap + key;
+        const int blk = sm.bt[key / bs - page0];
+        return vc + (((size_t)blk * a.Hkv + kvh) * kHD + e) * bs + key % bs;
+    };
+    // direct loads of a full tile into buffer `bi`: slot = 64 * it + lane
+    auto issue_direct = [&](int tile, int bi) {
+        const int k0 = key_lo + tile * kTK;
+        AttnBuf &B = sm.u.buf[bi];
+        for (int it = wv; it < kTileChunks / 64; it += NW) {
+            const int slot = it * 64 + lane;
+            const int r = slot >> 4, P = slot & 15;
+            load_lds16(k_src(k0 + swap23(r), P ^ (r & 15)), &B.K[it * 64]);
+            const int e = slot >> 3, Q = slot & 7;
+            load_lds16(v_src(e, k0 + 8 * (Q ^ ((e >> 1) & 7))), &B.Vt[it * 64]);
+        }
+    };
+    // register-staged load and store of a tail or draft tile into buffer `bi`
+    auto stage_regs = [&](int tile, int bi) {
+        AttnBuf &B = sm.u.buf[bi];
+        const bool draft = has_draft && tile == ntiles - 1;
+        const int k0 = key_lo + tile * kTK;
+        uint16_t *vt16 = reinterpret_cast<uint16_t *>(B.Vt);
+        for (int c = tid; c < kTileChunks; c += NT) {
+            const int t = c >> 4, J = c & 15;
+            u32x4a kv = {0, 0, 0, 0};
+            if (draft) {
+                u32x4a vv = {0, 0, 0, 0};
+                if (t < n) {
+                    const size_t o = (((size_t)b * m_max + t) * a.Hkv + kvh) * kHD + J * 8;
+                    kv = *reinterpret_cast<const u32x4a *>(static_cast<const uint16_t *>(a.kd) + o);
+                    vv = *reinterpret_cast<const u32x4a *>(static_cast<const uint16_t *>(a.vd) + o);
+                }
+                // draft V arrives key-major: transpose into V^T (dims 8J..8J+7 of key t)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int e = 8 * J + q;
+                    const uint16_t h = (uint16_t)((vv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+                    vt16[vpos(e, t >> 3) * 8 + (t & 7)] = h;
+                }
+            } else {
+                if (k0 + t < key_hi) kv = *reinterpret_cast<const u32x4a *>(k_src(k0 + t, J));
+                const int e = c >> 3, Jv = c & 7, key = k0 + 8 * Jv;
+                u32x4a vv = {0, 0, 0, 0};
+                if (key < key_hi) {
+                    const uint16_t *vp = v_src(e, key);
+                    uint32_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t lo = (key + 2 * q < key_hi) ? vp[2 * q] : 0u;
+                        const uint32_t hi = (key + 2 * q + 1 < key_hi) ? vp[2 * q + 1] : 0u;
+                        w[q] = lo | (hi << 16);
+                    }
+                    vv = u32x4a{w[0], w[1], w[2], w[3]};
+                }
+                B.Vt[vpos(e, Jv)] = vv;
+            }
+            const int r = swap23(t);
+            B.K[kpos(r, J)] = kv;
+        }
+    };
 
     f32x16 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    // running max in raw score units and running sum; scores enter exp2 as
+    // fma(s, c, -m c) with c = scale * log2(e) > 0
+    const float c2 = a.scale_log2;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
-    const int ntiles = (key_hi - key_lo + kTK - 1) / kTK + (has_draft ? 1 : 0);
+    if (ntiles > 0 && direct(0)) issue_direct(0, 0);
     for (int tile = 0; tile < ntiles; ++tile) {
+        const int bi = tile & 1;
         const bool draft = has_draft && tile == ntiles - 1;
         const int k0 = key_lo + tile * kTK;
-        // ---- stage K and V^T in LDS ----
-        if (!draft) {
-            for (int c = tid; c < kTK * 16; c += NT) {
-                const int t = c >> 4, col = (c & 15) * 8;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (k0 + t < key_hi) v = *reinterpret_cast<const uint4 *>(k_row<uint16_t>(a, b, kvh, k0 + t) + col);
-                *reinterpret_cast<uint4 *>(&sm.K[swap23(t) * kKS + col]) = v;
-            }
-            for (int c = tid; c < kHD * 8; c += NT) {
-                const int e = c >> 3, kk = (c & 7) * 8;
-                const int key = k0 + kk;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (key + 8 <= key_hi && (a.block_size != 0 || a.v_vec)) {
-                    v = *reinterpret_cast<const uint4 *>(v_elem<uint16_t>(a, b, kvh, e, key));
-                } else if (key < key_hi) {
-                    uint16_t h8[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) h8[j] = (key + j < key_hi) ? *v_elem<uint16_t>(a, b, kvh, e, key + j) : 0;
-                    v = make_uint4(h8[0] | ((uint32_t)h8[1] << 16), h8[2] | ((uint32_t)h8[3] << 16),
-                                   h8[4] | ((uint32_t)h8[5] << 16), h8[6] | ((uint32_t)h8[7] << 16));
-                }
-                *reinterpret_cast<uint4 *>(&sm.Vt[e * kVS + kk]) = v;
-            }
-        } else {
-            const uint16_t *kd = static_cast<const uint16_t *>(a.kd);
-            const uint16_t *vd = static_cast<const uint16_t *>(a.vd);
-            for (int c = tid; c < kTK * 16; c += NT) {
-                const int j = c >> 4, col = (c & 15) * 8;
-                uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-                if (j < n) {
-                    const size_t o = (((size_t)b * m_max + j) * a.Hkv + kvh) * kHD + col;
-                    kv = *reinterpret_cast<const uint4 *>(kd + o);
-                    vv = *reinterpret_cast<const uint4 *>(vd + o);
-                }
-                *reinterpret_cast<uint4 *>(&sm.K[swap23(j) * kKS + col]) = kv;
-                const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    sm.Vt[(col + 2 * q) * kVS + j] = (uint16_t)(w4[q] & 0xffffu);
-                    sm.Vt[(col + 2 * q + 1) * kVS + j] = (uint16_t)(w4[q] >> 16);
-                }
-            }
-        }
-        __syncthreads();
+        if (!direct(tile)) stage_regs(tile, bi);
+        __builtin_amdgcn_s_waitcnt(0);        // this wave's loads into buffer bi have landed
+        __syncthreads();                      // ... and everyone's; tile - 1 is fully consumed
+        if (tile + 1 < ntiles && direct(tile + 1)) issue_direct(tile + 1, bi ^ 1);
+        const AttnBuf &B = sm.u.buf[bi];
 
         if (wave_active) {
-            // ---- S^T = K Q^T for the two 32-key halves ----
-            f32x16 sacc[2];
+            // ---- S^T = K Q^T: two independent 32-key accumulators ----
+            f32x16 s0, s1;
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
+            for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[sh][r] = 0.0f;
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 a0 = as_bf16x8(B.K[kpos(ln, 2 * ks + hh)]);
+                const bf16x8 a1 = as_bf16x8(B.K[kpos(32 + ln, 2 * ks + hh)]);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+            }
+            // s0/s1[8t + q] is the raw score of tile key 32sh + 16t + 8hh + q for row my_row
+            const bool fast = !draft && k0 + kTK <= key_hi && wave_full;
+            if (!fast) {
+                if (draft) {
+                    const uint32_t m0 = (uint32_t)my_anc >> (8 * hh), m1 = (uint32_t)(my_anc >> 32) >> (8 * hh);
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&sm.K[(32 * sh + ln) * kKS + 16 * ks + 8 * hh]);
-                    sacc[sh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[sh], 0, 0, 0);
+                    for (int r = 0; r < 16; ++r) {
+                        const int bit = 16 * (r >> 3) + (r & 7);
+                        s0[r] = (row_ok && ((m0 >> bit) & 1u)) ? s0[r] : -__builtin_inff();
+                        s1[r] = (row_ok && ((m1 >> bit) & 1u)) ? s1[r] : -__builtin_inff();
+                    }
+                } else {
+                    const int lim = key_hi - k0 - 8 * hh;    // tile keys below lim + 8hh are valid
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kq = 16 * (r >> 3) + (r & 7);
+                        s0[r] = (row_ok && kq < lim) ? s0[r] : -__builtin_inff();
+                        s1[r] = (row_ok && 32 + kq < lim) ? s1[r] : -__builtin_inff();
+                    }
                 }
             }
-            // sacc[sh][8t + q] is the score of tile key 32sh + 16t + 8hh + q for row my_row
             float tmax = -__builtin_inff();
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * sh + 16 * (r >> 3) + 8 * hh + (r & 7);
-                    bool ok = row_ok;
-                    if (draft) ok = ok && key < n && ((my_anc >> key) & 1ull);
-                    else ok = ok && (k0 + key < key_hi);
-                    const float v = ok ? sacc[sh][r] * a.scale_log2 : -__builtin_inff();
-                    sacc[sh][r] = v;
-                    tmax = fmaxf(tmax, v);
-                }
-            }
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float m_new = fmaxf(m_run, tmax);
             const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-            const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+            const float mc = m_use * c2;
+            const float corr = __builtin_amdgcn_exp2f(m_run * c2 - mc);
             float lsum = 0.0f;
             bf16x8 pf[2][2];
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[sh][r] - m_use);
-                    lsum += p;
-                    pf[sh][r >> 3][r & 7] = (__bf16)p;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, -mc));
+                lsum += p0 + p1;
+                pf[0][r >> 3][r & 7] = (__bf16)p0;
+                pf[1][r >> 3][r & 7] = (__bf16)p1;
             }
             lsum += __shfl_xor(lsum, 32);
             l_run = l_run * corr + lsum;
             m_run = m_new;
+            if (__any(corr != 1.0f)) {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
-            // ---- O^T += V^T P^T ----
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
+            }
+            // ---- O^T += V^T P^T: four independent accumulators per k-step ----
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
+            for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
-                for (int sh = 0; sh < 2; ++sh) {
+                for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(
-                            &sm.Vt[(32 * dt + ln) * kVS + 32 * sh + 16 * t + 8 * hh]);
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const bf16x8 av = as_bf16x8(B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)]);
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[sh][t], oacc[dt], 0, 0, 0);
                     }
                 }
             }
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- epilogue ----
     // oacc[dt][r] is O^T[d = 32dt + 8(r>>2) + 4hh + (r&3)][my_row]
@@ -283,7 +381,8 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
                 *reinterpret_cast<float4 *>(po + d0) =
                     make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
             }
-        if (hh == 0) a.part_ml[pbase + row_local] = make_float2(row_ok ? m_run : -__builtin_inff(), row_ok ? l_run : 0.0f);
+        // partial max in log2 units (raw max times c), as the merge below expects
+        if (hh == 0) a.part_ml[pbase + row_local] = make_float2(row_ok ? m_run * c2 : -__builtin_inff(), row_ok ? l_run : 0.0f);
     }
     __threadfence();
     __syncthreads();
@@ -294,28 +393,59 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
     __syncthreads();
     if (!sm.last) return;
     __threadfence();
-    for (int idx = tid; idx < a.rows_pg * 32; idx += NT) {
+    // ---- merge the splits: per-row weights w_s = exp2(m_s - M) / sum_s exp2(m_s - M) l_s ----
+    const int R = a.rows_pg;
+    const size_t ubase = (size_t)unit * a.nsplit * R;
+    const bool staged = nsplit_b * R <= (int)(sizeof(sm.u.wgt) / sizeof(float));
+    if (staged) {
+        for (int rl = tid; rl < R; rl += NT) {
+            float M = -__builtin_inff();
+#pragma unroll 8
+            for (int sp = 0; sp < nsplit_b; ++sp) M = fmaxf(M, a.part_ml[ubase + (size_t)sp * R + rl].x);
+            const float Mu = M == -__builtin_inff() ? 0.0f : M;
+            float den = 0.0f;
+#pragma unroll 8
+            for (int sp = 0; sp < nsplit_b; ++sp) {
+                const float2 ml = a.part_ml[ubase + (size_t)sp * R + rl];
+                const float e = __builtin_amdgcn_exp2f(ml.x - Mu);
+                sm.u.wgt[sp * R + rl] = e;
+                den += e * ml.y;
+            }
+            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+            for (int sp = 0; sp < nsplit_b; ++sp) sm.u.wgt[sp * R + rl] *= inv;
+        }
+        __syncthreads();
+    }
+    for (int idx = tid; idx < R * 32; idx += NT) {
         const int rl = idx >> 5, d4 = (idx & 31) * 4;
-        const int row = rg * a.rows_pg + rl, node = row / G;
+        const int row = rg * R + rl, node = row / G;
         if (node >= m_max) continue;
         const int h = kvh * G + (row % G);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (node < n) {
-            float M = -__builtin_inff();
-            for (int sp = 0; sp < nsplit_b; ++sp)
-                M = fmaxf(M, a.part_ml[((size_t)unit * a.nsplit + sp) * a.rows_pg + rl].x);
-            const float Mu = M == -__builtin_inff() ? 0.0f : M;
-            float den = 0.0f;
-            for (int sp = 0; sp < nsplit_b; ++sp) {
-                const size_t pr = ((size_t)unit * a.nsplit + sp) * a.rows_pg + rl;
-                const float2 ml = a.part_ml[pr];
-                const float wgt = __builtin_amdgcn_exp2f(ml.x - Mu);
-                den += wgt * ml.y;
-                const float4 o4 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d4);
-                acc.x += wgt * o4.x; acc.y += wgt * o4.y; acc.z += wgt * o4.z; acc.w += wgt * o4.w;
+            if (staged) {
+#pragma unroll 8
+                for (int sp = 0; sp < nsplit_b; ++sp) {
+                    const float wgt = sm.u.wgt[sp * R + rl];
+                    const float4 o4 = *reinterpret_cast<const float4 *>(a.part_o + (ubase + (size_t)sp * R + rl) * kHD + d4);
+                    acc.x += wgt * o4.x; acc.y += wgt * o4.y; acc.z += wgt * o4.z; acc.w += wgt * o4.w;
+                }
+            } else {
+                float M = -__builtin_inff();
+                for (int sp = 0; sp < nsplit_b; ++sp) M = fmaxf(M, a.part_ml[ubase + (size_t)sp * R + rl].x);
+                const float Mu = M == -__builtin_inff() ? 0.0f : M;
+                float den = 0.0f;
+                for (int sp = 0; sp < nsplit_b; ++sp) {
+                    const size_t pr = ubase + (size_t)sp * R + rl;
+                    const float2 ml = a.part_ml[pr];
+                    const float wgt = __builtin_amdgcn_exp2f(ml.x - Mu);
+                    den += wgt * ml.y;
+                    const float4 o4 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d4);
+                    acc.x += wgt * o4.x; acc.y += wgt * o4.y; acc.z += wgt * o4.z; acc.w += wgt * o4.w;
+                }
+                const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+                acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
             }
-            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-            acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
         }
         uint2 w;
         w.x = f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
