@@ -14,8 +14,7 @@
 // (8 consecutive keys), so no shuffles are needed between the two products.
 // The draft tokens form one extra tile (at most 64 keys) masked by the
 // ancestor bits.  With several key splits, each writes an unnormalised
-// partial (O, max, sum); the last split to finish (device-scope counter)
-// merges them.
+// partial (O, max, sum) and a second kernel merges them.
 #include "common.h"
 #include "internal.h"
 
@@ -37,7 +36,7 @@ struct AttnArgs {
     void *out;
     float *part_o;
     float2 *part_ml;
-    uint32_t *cnt, *err;
+    uint32_t *err;
     int Hq, Hkv, G, d, m_max, block_size, max_blocks, cap, chunk, nsplit, RG, rows_pg, units0;
     float scale_log2;
     bool v_vec;   // contiguous V^T rows are 16-byte aligned
@@ -88,10 +87,8 @@ struct AttnBuf {
 struct AttnSmem {
     union {
         AttnBuf buf[2];
-        float wgt[2 * (kTK * 16 + kHD * 8) * 4];     // combine: per-split weights of each row
     } u;
     int bt[kMaxPages];
-    int last;
 };
 
 __device__ __forceinline__ int kpos(int r, int J) { return r * 16 + (J ^ (r & 15)); }
@@ -381,78 +378,66 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
                 *reinterpret_cast<float4 *>(po + d0) =
                     make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
             }
-        // partial max in log2 units (raw max times c), as the merge below expects
+        // partial max in log2 units (raw max times c), as the merge expects
         if (hh == 0) a.part_ml[pbase + row_local] = make_float2(row_ok ? m_run * c2 : -__builtin_inff(), row_ok ? l_run : 0.0f);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(&a.cnt[unit], 1u);
-        sm.last = prev == (unsigned)(nsplit_b - 1);
-    }
-    __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
-    // ---- merge the splits: per-row weights w_s = exp2(m_s - M) / sum_s exp2(m_s - M) l_s ----
-    const int R = a.rows_pg;
-    const size_t ubase = (size_t)unit * a.nsplit * R;
-    const bool staged = nsplit_b * R <= (int)(sizeof(sm.u.wgt) / sizeof(float));
-    if (staged) {
-        for (int rl = tid; rl < R; rl += NT) {
-            float M = -__builtin_inff();
-#pragma unroll 8
-            for (int sp = 0; sp < nsplit_b; ++sp) M = fmaxf(M, a.part_ml[ubase + (size_t)sp * R + rl].x);
-            const float Mu = M == -__builtin_inff() ? 0.0f : M;
-            float den = 0.0f;
-#pragma unroll 8
-            for (int sp = 0; sp < nsplit_b; ++sp) {
-                const float2 ml = a.part_ml[ubase + (size_t)sp * R + rl];
-                const float e = __builtin_amdgcn_exp2f(ml.x - Mu);
-                sm.u.wgt[sp * R + rl] = e;
-                den += e * ml.y;
-            }
-            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-            for (int sp = 0; sp < nsplit_b; ++sp) sm.u.wgt[sp * R + rl] *= inv;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the key splits (launched right after the main kernel on the same
+// stream, so the kernel boundary makes every partial visible): for each row,
+// O = sum_s w_s O_s with w_s = exp2(m_s - M) / sum_s exp2(m_s - M) l_s.
+// One workgroup per (unit, 16 rows); thread = (row, 8 dims).
+// ---------------------------------------------------------------------------
+constexpr int kMergeRows = 16;
+
+__global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a)
+{
+    const int tid = threadIdx.x;
+    const int blocks_per_unit = (a.rows_pg + kMergeRows - 1) / kMergeRows;
+    const int unit = blockIdx.x / blocks_per_unit;
+    const int rl = (blockIdx.x % blocks_per_unit) * kMergeRows + (tid >> 4);
+    const int d8 = (tid & 15) * 8;
+    const int rg = unit % a.RG, u0 = unit / a.RG;
+    const int b = u0 / a.Hkv, kvh = u0 % a.Hkv;
+    const int G = a.G, m_max = a.m_max;
+    int L = a.prefix_len[b];
+    L = L < 0 ? 0 : (L > a.cap ? a.cap : L);
+    const int nsplit_b = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+    if (nsplit_b == 1 || rl >= a.rows_pg) return;          // written by the main kernel
+    const int row = rg * a.rows_pg + rl, node = row / G;
+    if (node >= m_max) return;
+    int n = a.num_nodes[b];
+    n = n < 0 ? 0 : (n > m_max ? m_max : n);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (node < n) {
+        const size_t base = (size_t)unit * a.nsplit * a.rows_pg + rl;
+        float M = -__builtin_inff();
+        for (int sp = 0; sp < nsplit_b; ++sp) M = fmaxf(M, a.part_ml[base + (size_t)sp * a.rows_pg].x);
+        const float Mu = M == -__builtin_inff() ? 0.0f : M;
+        float den = 0.0f;
+#pragma unroll 4
+        for (int sp = 0; sp < nsplit_b; ++sp) {
+            const size_t pr = base + (size_t)sp * a.rows_pg;
+            const float2 ml = a.part_ml[pr];
+            const float w = __builtin_amdgcn_exp2f(ml.x - Mu);
+            den += w * ml.y;
+            const float4 o0 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8);
+            const float4 o1 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8 + 4);
+            acc[0] += w * o0.x; acc[1] += w * o0.y; acc[2] += w * o0.z; acc[3] += w * o0.w;
+            acc[4] += w * o1.x; acc[5] += w * o1.y; acc[6] += w * o1.z; acc[7] += w * o1.w;
         }
-        __syncthreads();
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] *= inv;
     }
-    for (int idx = tid; idx < R * 32; idx += NT) {
-        const int rl = idx >> 5, d4 = (idx & 31) * 4;
-        const int row = rg * R + rl, node = row / G;
-        if (node >= m_max) continue;
-        const int h = kvh * G + (row % G);
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (node < n) {
-            if (staged) {
-#pragma unroll 8
-                for (int sp = 0; sp < nsplit_b; ++sp) {
-                    const float wgt = sm.u.wgt[sp * R + rl];
-                    const float4 o4 = *reinterpret_cast<const float4 *>(a.part_o + (ubase + (size_t)sp * R + rl) * kHD + d4);
-                    acc.x += wgt * o4.x; acc.y += wgt * o4.y; acc.z += wgt * o4.z; acc.w += wgt * o4.w;
-                }
-            } else {
-                float M = -__builtin_inff();
-                for (int sp = 0; sp < nsplit_b; ++sp) M = fmaxf(M, a.part_ml[ubase + (size_t)sp * R + rl].x);
-                const float Mu = M == -__builtin_inff() ? 0.0f : M;
-                float den = 0.0f;
-                for (int sp = 0; sp < nsplit_b; ++sp) {
-                    const size_t pr = ubase + (size_t)sp * R + rl;
-                    const float2 ml = a.part_ml[pr];
-                    const float wgt = __builtin_amdgcn_exp2f(ml.x - Mu);
-                    den += wgt * ml.y;
-                    const float4 o4 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d4);
-                    acc.x += wgt * o4.x; acc.y += wgt * o4.y; acc.z += wgt * o4.z; acc.w += wgt * o4.w;
-                }
-                const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-                acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-            }
-        }
-        uint2 w;
-        w.x = f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-        w.y = f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-        *reinterpret_cast<uint2 *>(out + (((size_t)b * m_max + node) * a.Hq + h) * kHD + d4) = w;
-    }
-    if (tid == 0) a.cnt[unit] = 0;
+    uint4 w4;
+    w4.x = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    w4.y = f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    w4.z = f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    w4.w = f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    const int h = kvh * G + (row % G);
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + (((size_t)b * m_max + node) * a.Hq + h) * kHD + d8) = w4;
 }
 
 // ---------------------------------------------------------------------------
@@ -576,7 +561,7 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
     size_t o = kWsHeader;
     P.off_part = o; o = align_up(o + (P.nsplit > 1 ? rows_alloc * kHD * sizeof(float) : 0), 256);
     P.off_ml = o;   o = align_up(o + (P.nsplit > 1 ? rows_alloc * sizeof(float2) : 0), 256);
-    P.off_cnt = o;  o = align_up(o + (size_t)units * sizeof(uint32_t), 256);
+    P.off_cnt = o;
     P.total = o;
     return P;
 }
@@ -595,7 +580,6 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     a.out = out;
     a.part_o = reinterpret_cast<float *>(base + P.off_part);
     a.part_ml = reinterpret_cast<float2 *>(base + P.off_ml);
-    a.cnt = reinterpret_cast<uint32_t *>(base + P.off_cnt);
     a.err = reinterpret_cast<uint32_t *>(base);
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = P.G; a.d = p->head_dim;
     a.m_max = p->m_max; a.block_size = p->block_size; a.max_blocks = p->max_blocks;
@@ -613,6 +597,12 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
         hipLaunchKernelGGL(k_tree_attn_bf16, g, dim3(64 * P.waves), 0, st, a);
+        if (P.nsplit > 1) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int bpu = (a.rows_pg + kMergeRows - 1) / kMergeRows;
+            hipLaunchKernelGGL(k_tree_attn_merge, dim3((unsigned)(a.units0 * P.row_groups * bpu)), dim3(256), 0, st, a);
+        }
     }
     return hipGetLastError();
 }
