@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only eagle_tree_attn (for profiling runs)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of hipGraph replays")
     return ap.parse_args()
 
 
@@ -127,22 +128,60 @@ def main():
         if not args.attn_only:
             step.accept(S["target"], S["words"])
 
+    # ---- one captured graph per input set (the four calls of one step) ----
+    graphs = None
+    if not args.eager:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for k in range(3):
+                run_step(sets[k % nsets])
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graphs = []
+        for S in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(S)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def timed_steps(K):
+        """K steps (sets rotate), bracketed by device synchronisation."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            if graphs is not None:
+                graphs[k % nsets].replay()
+            else:
+                run_step(sets[k % nsets])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
     # ---- warm-up and the timed region (cold: sets rotate) ----------------
     for k in range(args.warmup):
-        run_step(sets[k % nsets])
-    torch.cuda.synchronize()
+        if graphs is not None:
+            graphs[k % nsets].replay()
+        else:
+            run_step(sets[k % nsets])
     K = args.steps
+    ms_per_step = timed_steps(K)
+    eager_ms = ms_per_step if graphs is None else None
+    log(f"[bench] timed {K} steps ({'graph replays' if graphs is not None else 'eager'}): "
+        f"{ms_per_step * 1e3:.1f} us/step")
+
+    # ---- attention duration: HIP events around the call, eager loop ------
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    te0 = time.perf_counter()
     for k in range(K):
         run_step(sets[k % nsets], evs[k])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
+    if eager_ms is None:
+        eager_ms = (time.perf_counter() - te0) * 1e3 / K
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg_ms = float(np.mean(attn_ms))
-    log(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us")
+    log(f"[bench] eager {eager_ms * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us")
 
     # ---- per-stage breakdown (separate loop, events between the calls) ---
     stage_names = ["build_tree", "tree_mask", "tree_attn", "accept"]
@@ -167,11 +206,11 @@ def main():
 
     # ---- warm: one set repeated ------------------------------------------
     for _ in range(5):
-        run_step(sets[0])
+        graphs[0].replay() if graphs is not None else run_step(sets[0])
     torch.cuda.synchronize()
     tw0 = time.perf_counter()
     for _ in range(K):
-        run_step(sets[0])
+        graphs[0].replay() if graphs is not None else run_step(sets[0])
     torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - tw0) * 1e3 / K
 
@@ -207,7 +246,8 @@ def main():
                    "prefix": w.prefix if isinstance(w.prefix, int) else list(w.prefix),
                    "kv_layout": "paged16" if w.block_size else "contiguous",
                    "accept": "greedy" if w.accept_mode == synth.ACCEPT_GREEDY else f"sample T={w.temperature}",
-                   "input_sets": nsets, "cold": True},
+                   "input_sets": nsets, "cold": True,
+                   "launch": "graph" if graphs is not None else "eager"},
         "roofline": {"kernel": "k_tree_attn_bf16" if w.dtype == torch.bfloat16 else "k_tree_attn_f32",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -216,6 +256,8 @@ def main():
         "cpu_baseline": cpu,
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
+        "launch": "hipGraph replay per step" if graphs is not None else "eager",
+        "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
         "tokens_per_step": tokens_per_step,
         "device": torch.cuda.get_device_name(0),
         "device_errors": errs,

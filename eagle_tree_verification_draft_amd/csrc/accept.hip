@@ -83,12 +83,24 @@ __device__ __forceinline__ void for_each_elem(const T *row, int V, bool vec_ok, 
     constexpr int VEC = AVec<T>::n;
     const int NT = blockDim.x, tid = threadIdx.x;
     const int nvec = vec_ok ? V / VEC : 0;
-    for (int j = tid; j < nvec; j += NT) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(row + (size_t)j * VEC);
-        float f[VEC];
-        unpack_a<T>(u, f);
+    // batches of 4 independent 16-byte loads per thread
+    for (int j0 = tid; j0 < nvec; j0 += 4 * NT) {
+        uint4 u[4];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) fn(f[e], j * VEC + e);
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + q * NT;
+            u[q] = j < nvec ? *reinterpret_cast<const uint4 *>(row + (size_t)j * VEC) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + q * NT;
+            if (j < nvec) {
+                float f[VEC];
+                unpack_a<T>(u[q], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) fn(f[e], j * VEC + e);
+            }
+        }
     }
     for (int v = nvec * VEC + tid; v < V; v += NT) fn(ld1<T>(row + v), v);
 }
@@ -228,6 +240,81 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Greedy acceptance for small batches: the argmax of every row a walk could
+// visit (row 0 and the rows of the sequence's nodes) is computed in parallel,
+// one workgroup per row; a second kernel walks each tree over those argmaxes.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(1024) void k_row_argmax(AcceptArgs a, int32_t *g)
+{
+    __shared__ BlockScratch red;
+    const int m1 = a.m_max + 1;
+    const int b = blockIdx.x / m1, u = blockIdx.x % m1;
+    int n = a.num_nodes[b];
+    n = n < 0 ? 0 : (n > a.m_max ? a.m_max : n);
+    if (u > n) return;
+    const T *row = static_cast<const T *>(a.target) + ((size_t)b * m1 + u) * (size_t)a.row_stride;
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    bool nan = false;
+    for_each_elem<T>(row, a.vocab, a.vec_ok, [&](float f, int id) {
+        nan |= (f != f);
+        if (before(f, id, bv, bi)) { bv = f; bi = id; }
+    });
+    if (__any(nan) && (threadIdx.x & 63) == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+    block_best(bv, bi, red);
+    if (threadIdx.x == 0) g[(size_t)b * m1 + u] = bi;
+}
+
+__global__ __launch_bounds__(64) void k_greedy_walk(AcceptArgs a, const int32_t *g)
+{
+    // one wave per sequence; lane i holds node i (m_max <= 64), and the child
+    // whose token matches the current argmax is found by a ballot
+    __shared__ int gs[kMaxMMax + 1];
+    const int b = blockIdx.x, lane = threadIdx.x, m_max = a.m_max;
+    int n = a.num_nodes[b];
+    if (n < 0 || n > m_max) {
+        if (lane == 0) raise_error(a.err, EAGLE_DEVERR_TREE);
+        n = n < 0 ? 0 : m_max;
+    }
+    const int tok = lane < n ? a.tokens[(size_t)b * m_max + lane] : -1;
+    const int par = lane < n ? a.parent[(size_t)b * m_max + lane] : -2;
+    for (int u = lane; u <= n; u += 64) gs[u] = g[(size_t)b * (m_max + 1) + u];
+    __syncthreads();
+    int32_t *acc = a.accepted + (size_t)b * a.max_accept;
+    int cur = -1, len = 0, bonus = -1;
+    while (true) {
+        const int gg = gs[cur + 1];
+        const unsigned long long hit = __ballot(par == cur && tok == gg);
+        if (!hit) { bonus = gg; break; }
+        const int next = __builtin_ctzll(hit);
+        if (len >= a.max_accept) {
+            if (lane == 0) raise_error(a.err, EAGLE_DEVERR_PATH);
+            break;
+        }
+        if (lane == 0) acc[len] = next;
+        ++len;
+        cur = next;
+    }
+    for (int j = len + lane; j < a.max_accept; j += 64) acc[j] = -1;
+    if (lane == 0) {
+        a.accept_len[b] = len;
+        a.bonus[b] = bonus;
+    }
+}
+
+// rows below which greedy acceptance reads every row in parallel
+constexpr int kParallelGreedyRows = 512;
+
+size_t accept_layout_bytes(const eagle_accept_params *p, int32_t batch)
+{
+    size_t o = kWsHeader;
+    if (p && p->mode == EAGLE_ACCEPT_GREEDY && (size_t)batch * (p->m_max + 1) <= (size_t)kParallelGreedyRows)
+        o = align_up(o + (size_t)batch * (p->m_max + 1) * sizeof(int32_t), 256);
+    return o;
+}
+
 hipError_t launch_accept(const eagle_accept_params *p, int32_t batch, const void *target,
                          eagle_dtype dt, int64_t row_stride, const int32_t *tokens,
                          const int32_t *parent, const int32_t *num_nodes, const uint32_t *words,
@@ -257,6 +344,18 @@ hipError_t launch_accept(const eagle_accept_params *p, int32_t batch, const void
     const int vec = dt == EAGLE_F32 ? 4 : 8;
     int nt = (p->vocab / vec + 63) / 64 * 64;
     nt = nt < 64 ? 64 : (nt > kAcceptThreads ? kAcceptThreads : nt);
+    if (p->mode == EAGLE_ACCEPT_GREEDY && (size_t)batch * (p->m_max + 1) <= (size_t)kParallelGreedyRows) {
+        int32_t *g = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(err) + kWsHeader);
+        const dim3 grid((unsigned)(batch * (p->m_max + 1)));
+        if (dt == EAGLE_F32)
+            hipLaunchKernelGGL(k_row_argmax<float>, grid, dim3(nt), 0, st, a, g);
+        else
+            hipLaunchKernelGGL(k_row_argmax<uint16_t>, grid, dim3(nt), 0, st, a, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_greedy_walk, dim3(batch), dim3(64), 0, st, a, (const int32_t *)g);
+        return hipGetLastError();
+    }
     if (dt == EAGLE_F32)
         hipLaunchKernelGGL(k_accept<float>, dim3(batch), dim3(nt), 0, st, a);
     else

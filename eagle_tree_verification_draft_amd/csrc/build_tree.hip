@@ -81,8 +81,9 @@ __device__ __forceinline__ void load_row(const T *row, int V, bool vec_ok, uint4
 
 struct RowStatsSmem {
     BlockScratch red;
-    float cand_v[kCandCap];
-    int cand_i[kCandCap];
+    float cand_v[kCandCap + 16];   // +16: segment reads may run past the count
+    int cand_i[kCandCap + 16];
+    int rank[kCandCap];
     int sel[kMaxChildren];
     float thr[16];
     int count;
@@ -161,15 +162,28 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
     const int total = sm.count;
 
     if (tid < kMaxChildren) sm.sel[tid] = 0;
-    __syncthreads();
     if (use_list && total <= kCandCap) {
-        for (int i = tid; i < total; i += NT) {
+        // rank of every candidate: comparisons split into segments of 16, one
+        // (segment, candidate) pair per thread; the lanes of a wave share a
+        // segment, so their LDS reads broadcast; partial counts meet in LDS atomics
+        for (int i = tid; i < total; i += NT) sm.rank[i] = 0;
+        __syncthreads();
+        const int nseg = (total + 15) / 16;
+        for (int t = tid; t < total * nseg; t += NT) {
+            const int g = t / total, i = t % total;
             const float vi = sm.cand_v[i];
             const int ii = sm.cand_i[i];
-            int rank = 0;
-            for (int j = 0; j < total && rank < C; ++j) rank += before(sm.cand_v[j], sm.cand_i[j], vi, ii) ? 1 : 0;
-            if (rank < C) sm.sel[rank] = i;
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int j = 16 * g + q;
+                cnt += (j < total && before(sm.cand_v[j], sm.cand_i[j], vi, ii)) ? 1 : 0;
+            }
+            if (cnt) atomicAdd(&sm.rank[i], cnt);
         }
+        __syncthreads();
+        for (int i = tid; i < total; i += NT)
+            if (sm.rank[i] < C) sm.sel[sm.rank[i]] = i;
         __syncthreads();
         if (tid < C) {
             const int i = sm.sel[tid];
@@ -209,14 +223,21 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
 
 // ---------------------------------------------------------------------------
 // Kernel 2: one workgroup per sequence.  Candidates live in LDS in creation
-// order.  Depth by depth: each depth-d candidate's rank among depth-d
-// candidates in (V desc, creation asc) is counted by all threads at once (the
-// comparisons are split into groups whose partial counts are added with LDS
-// atomics); the top-k by that rank are expanded; then the depth's sorted list
-// is merged into the running sorted list of the best m candidates seen so far
-// (each element finds its merged position by a binary search in the other
-// list).  After the last depth that list is the rerank's top-m in rank order.
+// order; every confidence c = w / W is computed once, in parallel, up front.
+// Depth by depth, one pass of comparisons (split into segments of kSeg, one
+// segment per thread, partial counts added with LDS atomics) yields for each
+// depth-d candidate its rank among the depth (the top-k are expanded) and the
+// number of entries of the running best-m list that precede it, and for each
+// entry of that list the number of depth-d candidates that precede it.
+// Those counts are the positions of the merged list, which after the last
+// depth is the rerank's top-m in rank order.
 // ---------------------------------------------------------------------------
+struct Key {
+    double v;
+    int i;
+    int pad;
+};
+
 struct TreeSmem {
     double V[kMaxCand];
     int tok[kMaxCand];
@@ -224,30 +245,41 @@ struct TreeSmem {
     int dep[kMaxCand];
     int row[kMaxCand];
     int rank_of[kMaxCand];
-    int rankd[kMaxCand];
-    int sortedD[kMaxCand];
-    double rowW[kMaxRows];                  // W of every row this sequence uses
-    double rowCw[kMaxRows * kMaxChildren];  // top-C weights
-    int rowCid[kMaxRows * kMaxChildren];    // top-C token ids
-    int S[kMaxMMax];
-    int Snew[kMaxMMax];
+    Key KD[kMaxCand + 16];                  // keys of the current depth (+16: segment reads)
+    float FD[kMaxCand + 16];                // the same V rounded to fp32 (order-preserving prefilter)
+    int rankD[kMaxCand];                    // rank of a depth-d candidate within its depth
+    int cntS[kMaxCand];                     // best-m entries preceding a depth-d candidate
+    double conf[kMaxRows * kMaxChildren];   // c of every (row, child)
+    int rowCid[kMaxRows * kMaxChildren];    // token of every (row, child)
+    Key KS[kMaxMMax + 16];                  // running best-m list
+    float FS[kMaxMMax + 16];
+    Key KSn[kMaxMMax];
+    int cntD[kMaxMMax];                     // depth-d candidates preceding a list entry
     int exp_par[kMaxTopk];
 };
 
-__device__ __forceinline__ bool cand_before(const TreeSmem &sm, int a, int b)
+// (V desc, creation asc)
+__device__ __forceinline__ bool kbefore(double va, int ia, double vb, int ib)
 {
-    return sm.V[a] > sm.V[b] || (sm.V[a] == sm.V[b] && a < b);
+    return va > vb || (va == vb && ia < ib);
 }
 
-// number of leading entries of list[0..len) that come before candidate x
-__device__ __forceinline__ int count_before(const TreeSmem &sm, const int *list, int len, int x)
+// Entries j in [j0, j0 + 16) of (F, K)[0..len) that come before x.  Rounding
+// to fp32 is monotone, so F_j > F_x implies V_j > V_x; only equal fp32 keys
+// need the exact (V, creation) comparison.
+__device__ __forceinline__ int count_seg(const float *F, const Key *K, int len, int j0, float fx, double vx,
+                                         int ix)
 {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int md = (lo + hi) >> 1;
-        if (cand_before(sm, list[md], x)) lo = md + 1; else hi = md;
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int j = j0 + q;
+        const float fj = F[j];
+        int c = fj > fx ? 1 : 0;
+        if (fj == fx) c = kbefore(K[j].v, K[j].i, vx, ix) ? 1 : 0;
+        cnt += j < len ? c : 0;
     }
-    return lo;
+    return cnt;
 }
 
 __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
@@ -283,78 +315,98 @@ __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
     }
 
     const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
-    // all row statistics of this sequence -> LDS in one parallel pass
     const int R = 1 + (D - 1) * k;
+    // confidences of every (row, child), in parallel
     for (int i = tid; i < R * C; i += NT) {
         const int r = i / C, j = i % C;
-        sm.rowCw[i] = a.top_w[(rb + r) * Cw + j];
+        sm.conf[i] = a.top_w[(rb + r) * Cw + j] / a.W[rb + r];
         sm.rowCid[i] = a.top_id[(rb + r) * Cw + j];
     }
-    for (int r = tid; r < R; r += NT) sm.rowW[r] = a.W[rb + r];
     __syncthreads();
     // depth 1: children of the root's row 0
     for (int j = tid; j < C; j += NT) {
-        sm.V[j] = sm.rowCw[j] / sm.rowW[0];
+        sm.V[j] = sm.conf[j];
+        sm.KD[j] = Key{sm.conf[j], j, 0};
+        sm.FD[j] = (float)sm.conf[j];
+        sm.rankD[j] = 0;
+        sm.cntS[j] = 0;
         sm.tok[j] = sm.rowCid[j];
         sm.par[j] = -1;
         sm.dep[j] = 1;
         sm.row[j] = -1;
     }
+    __syncthreads();
     int begin = 0, end = C, sN = 0;
     for (int d = 1; d <= D; ++d) {
         const int nd = end - begin;
-        for (int i = tid; i < nd; i += NT) sm.rankd[i] = 0;
-        __syncthreads();
-        // ---- rank within the depth: groups of comparisons per candidate ----
-        const int G = max(1, min(nd, NT / max(nd, 1)));
-        const int per = (nd + G - 1) / G;
-        for (int t = tid; t < nd * G; t += NT) {
-            const int i = t % nd, g = t / nd;
-            const int j0 = g * per, j1 = min(nd, j0 + per);
-            const int xi = begin + i;
-            int cnt = 0;
-            for (int j = j0; j < j1; ++j) cnt += cand_before(sm, begin + j, xi) ? 1 : 0;
-            if (cnt) atomicAdd(&sm.rankd[i], cnt);
-        }
-        __syncthreads();
-        for (int i = tid; i < nd; i += NT) sm.sortedD[sm.rankd[i]] = begin + i;
-        __syncthreads();
-        // ---- expansion: the p-th best depth-d node owns row 1 + (d-1)k + p ----
-        int ne = 0;
-        if (d < D) {
-            ne = nd < k ? nd : k;
-            for (int p = tid; p < ne; p += NT) {
-                const int pidx = sm.sortedD[p];
-                sm.exp_par[p] = pidx;
-                sm.row[pidx] = 1 + (d - 1) * k + p;
-            }
-            __syncthreads();
-            for (int t = tid; t < ne * C; t += NT) {
-                const int p = t / C, j = t % C;
-                const int pidx = sm.exp_par[p];
-                const int r = 1 + (d - 1) * k + p;
-                const double c = sm.rowCw[r * C + j] / sm.rowW[r];
-                sm.V[end + t] = sm.V[pidx] * c;
-                sm.tok[end + t] = sm.rowCid[r * C + j];
-                sm.par[end + t] = pidx;
-                sm.dep[end + t] = d + 1;
-                sm.row[end + t] = -1;
+        // ---- counts: rank within the depth, and the merge positions ----
+        // items: (segment of D, x in D), (segment of S, x in D), (segment of D, y in S);
+        // consecutive threads share a segment
+        const int segD = (nd + 15) / 16, segS = (sN + 15) / 16;
+        const int itA = segD * nd, itB = segS * nd, itC = segD * sN;
+        for (int t = tid; t < itA + itB + itC; t += NT) {
+            if (t < itA + itB) {
+                const bool vsD = t < itA;
+                const int u = vsD ? t : t - itA;
+                const int g = u / nd, i = u % nd;
+                const Key x = sm.KD[i];
+                const float fx = sm.FD[i];
+                if (vsD) {
+                    const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, fx, x.v, x.i);
+                    if (c) atomicAdd(&sm.rankD[i], c);
+                } else {
+                    const int c = count_seg(sm.FS, sm.KS, sN, 16 * g, fx, x.v, x.i);
+                    if (c) atomicAdd(&sm.cntS[i], c);
+                }
+            } else {
+                const int u = t - itA - itB;
+                const int g = u / sN, q = u % sN;
+                const Key y = sm.KS[q];
+                const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, sm.FS[q], y.v, y.i);
+                if (c) atomicAdd(&sm.cntD[q], c);
             }
         }
-        // ---- merge this depth's sorted list into the best-m list ----
-        for (int p = tid; p < nd; p += NT) {
-            const int x = sm.sortedD[p];
-            const int pos = p + count_before(sm, sm.S, sN, x);
-            if (pos < m) sm.Snew[pos] = x;
+        __syncthreads();
+        // ---- positions: merged list, expansion ----
+        const int ne = d < D ? min(k, nd) : 0;
+        for (int t = tid; t < nd + sN; t += NT) {
+            if (t < nd) {
+                const int rd = sm.rankD[t], pos = rd + sm.cntS[t];
+                const Key x = sm.KD[t];
+                if (pos < m) sm.KSn[pos] = x;
+                if (rd < ne) {
+                    sm.exp_par[rd] = x.i;
+                    sm.row[x.i] = 1 + (d - 1) * k + rd;
+                }
+            } else {
+                const int q = t - nd, pos = q + sm.cntD[q];
+                if (pos < m) sm.KSn[pos] = sm.KS[q];
+            }
         }
-        for (int q = tid; q < sN; q += NT) {
-            const int y = sm.S[q];
-            const int pos = q + count_before(sm, sm.sortedD, nd, y);
-            if (pos < m) sm.Snew[pos] = y;
+        __syncthreads();
+        // ---- children of the expanded nodes (the next depth's keys); new list ----
+        for (int t = tid; t < ne * C; t += NT) {
+            const int p = t / C, j = t % C;
+            const int pidx = sm.exp_par[p];
+            const int r = 1 + (d - 1) * k + p;
+            const double v = sm.V[pidx] * sm.conf[r * C + j];
+            sm.V[end + t] = v;
+            sm.KD[t] = Key{v, end + t, 0};
+            sm.FD[t] = (float)v;
+            sm.rankD[t] = 0;
+            sm.cntS[t] = 0;
+            sm.tok[end + t] = sm.rowCid[r * C + j];
+            sm.par[end + t] = pidx;
+            sm.dep[end + t] = d + 1;
+            sm.row[end + t] = -1;
         }
         sN = min(m, sN + nd);
-        __syncthreads();
-        for (int q = tid; q < sN; q += NT) sm.S[q] = sm.Snew[q];
+        for (int q = tid; q < sN; q += NT) {
+            const Key kq = sm.KSn[q];
+            sm.KS[q] = kq;
+            sm.FS[q] = (float)kq.v;
+            sm.cntD[q] = 0;
+        }
         __syncthreads();
         begin = end;
         end += ne * C;
@@ -362,11 +414,11 @@ __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
     const int N = begin;
     for (int i = tid; i < N; i += NT) sm.rank_of[i] = -1;
     __syncthreads();
-    for (int r = tid; r < m; r += NT) sm.rank_of[sm.S[r]] = r;
+    for (int r = tid; r < m; r += NT) sm.rank_of[sm.KS[r].i] = r;
     __syncthreads();
     // connected tree check (holds by construction: V never grows along a path)
     for (int r = tid; r < m; r += NT) {
-        const int i = sm.S[r];
+        const int i = sm.KS[r].i;
         int q = sm.par[i];
         while (q >= 0) {
             if (sm.rank_of[q] < 0) { raise_error(a.err, EAGLE_DEVERR_CLOSURE); break; }

@@ -215,9 +215,8 @@ eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const vo
 
 size_t eagle_accept_workspace_size(const eagle_accept_params *a, int32_t batch)
 {
-    (void)a;
-    (void)batch;
-    return kWsHeader;
+    if (!a || batch < 0 || a->m_max < 1 || a->m_max > kMaxMMax) return kWsHeader;
+    return accept_layout_bytes(a, batch);
 }
 
 eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const void *target_logits,
@@ -242,7 +241,7 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
     if (!target_logits || !tokens || !parent || !num_nodes || !accepted || !accept_len || !bonus_token)
         return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
     if (a->mode == EAGLE_ACCEPT_SAMPLE && !rand_words) return fail(EAGLE_ERR_INVALID, "sampling needs rand_words");
-    eagle_status s = check_workspace(workspace, workspace_bytes, kWsHeader);
+    eagle_status s = check_workspace(workspace, workspace_bytes, accept_layout_bytes(a, batch));
     if (s != EAGLE_OK) return s;
     if (batch == 0) return ok();
     return hip_status(launch_accept(a, batch, target_logits, dtype, row_stride, tokens, parent, num_nodes, rand_words,

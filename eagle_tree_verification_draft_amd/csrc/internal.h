@@ -84,6 +84,8 @@ hipError_t launch_accept(const eagle_accept_params *a, int32_t batch, const void
                          int32_t *accepted, int32_t *accept_len, int32_t *bonus, uint32_t *err,
                          hipStream_t st);
 
+size_t accept_layout_bytes(const eagle_accept_params *p, int32_t batch);
+
 // ---- misc ----------------------------------------------------------------
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 

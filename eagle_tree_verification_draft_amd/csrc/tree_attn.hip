@@ -412,20 +412,32 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a)
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (node < n) {
         const size_t base = (size_t)unit * a.nsplit * a.rows_pg + rl;
-        float M = -__builtin_inff();
-        for (int sp = 0; sp < nsplit_b; ++sp) M = fmaxf(M, a.part_ml[base + (size_t)sp * a.rows_pg].x);
-        const float Mu = M == -__builtin_inff() ? 0.0f : M;
-        float den = 0.0f;
-#pragma unroll 4
-        for (int sp = 0; sp < nsplit_b; ++sp) {
-            const size_t pr = base + (size_t)sp * a.rows_pg;
-            const float2 ml = a.part_ml[pr];
-            const float w = __builtin_amdgcn_exp2f(ml.x - Mu);
-            den += w * ml.y;
-            const float4 o0 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8);
-            const float4 o1 = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8 + 4);
-            acc[0] += w * o0.x; acc[1] += w * o0.y; acc[2] += w * o0.z; acc[3] += w * o0.w;
-            acc[4] += w * o1.x; acc[5] += w * o1.y; acc[6] += w * o1.z; acc[7] += w * o1.w;
+        float M = -__builtin_inff(), den = 0.0f;
+        // batches of 4 splits: all loads of a batch are issued before use
+        for (int s0 = 0; s0 < nsplit_b; s0 += 4) {
+            float2 ml[4];
+            float4 o0[4], o1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const size_t pr = base + (size_t)min(s0 + q, nsplit_b - 1) * a.rows_pg;
+                ml[q] = a.part_ml[pr];
+                o0[q] = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8);
+                o1[q] = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8 + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (s0 + q >= nsplit_b) break;
+                // online merge in log2 units
+                const float Mn = fmaxf(M, ml[q].x);
+                const float Mu = Mn == -__builtin_inff() ? 0.0f : Mn;
+                const float sc = __builtin_amdgcn_exp2f(M - Mu), w = __builtin_amdgcn_exp2f(ml[q].x - Mu);
+                den = den * sc + w * ml[q].y;
+                acc[0] = acc[0] * sc + w * o0[q].x; acc[1] = acc[1] * sc + w * o0[q].y;
+                acc[2] = acc[2] * sc + w * o0[q].z; acc[3] = acc[3] * sc + w * o0[q].w;
+                acc[4] = acc[4] * sc + w * o1[q].x; acc[5] = acc[5] * sc + w * o1[q].y;
+                acc[6] = acc[6] * sc + w * o1[q].z; acc[7] = acc[7] * sc + w * o1[q].w;
+                M = Mn;
+            }
         }
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll

@@ -16,18 +16,19 @@ __global__ __launch_bounds__(64) void k_tree_mask(int m_max, const int32_t *pare
     __shared__ uint64_t s_acc[2][kMaxMMax];
     __shared__ int s_jmp[2][kMaxMMax];
     const int b = blockIdx.x, i = threadIdx.x;
+    // independent loads first
     int n = num_nodes[b];
+    const int L = prefix_len[b];
+    int p = i < m_max ? parent[(size_t)b * m_max + i] : -1;
     if (n < 0 || n > m_max) {
         if (i == 0) raise_error(err, EAGLE_DEVERR_TREE);
         n = n < 0 ? 0 : m_max;
     }
-    int p = -1;
-    if (i < n) {
-        p = parent[(size_t)b * m_max + i];
-        if (p >= i || p < -1) {           // rank order is topological: parent < child
-            raise_error(err, EAGLE_DEVERR_TREE);
-            p = -1;
-        }
+    if (i >= n) {
+        p = -1;
+    } else if (p >= i || p < -1) {          // rank order is topological: parent < child
+        raise_error(err, EAGLE_DEVERR_TREE);
+        p = -1;
     }
     s_acc[0][i] = i < n ? (uint64_t)1 << i : 0;
     s_jmp[0][i] = p;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(64) void k_tree_mask(int m_max, const int32_t *pare
     if (i < m_max) {
         const uint64_t a = s_acc[cur][i];
         anc[(size_t)b * m_max + i] = a;
-        pos[(size_t)b * m_max + i] = i < n ? prefix_len[b] + __popcll(a) - 1 : -1;
+        pos[(size_t)b * m_max + i] = i < n ? L + __popcll(a) - 1 : -1;
     }
 }
 

@@ -223,3 +223,37 @@ def test_rejection_sampling_million_trials():
     p /= p.sum()
     chi = scipy.stats.chisquare(np.bincount(first, minlength=V), p * n)
     assert chi.pvalue > 1e-3
+
+
+def test_graph_replay_matches_eager():
+    """The four calls captured into one graph, replayed several times with
+    eager work and synchronisations in between; every replay must equal the
+    eager result bit for bit (no memset nodes, self-contained workspaces)."""
+    w = _small(5, batch=4, vocab=6000, prefix=(100, 4000), kinds=[0, 1, 0, 1])
+    c = make_case(w, seed=17)
+    run_gpu(c)
+    outs = [t.clone() for t in (c.step.tokens, c.step.score, c.step.anc, c.step.pos, c.step.out,
+                                c.step.accepted, c.step.accept_len, c.step.bonus)]
+    a = c.attn
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        run_gpu(c)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c.step.run(c.draft, c.kinds, a.prefix_len, a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache,
+                   a.block_table, c.target, None)
+    for rep in range(4):
+        for t in (c.step.tokens, c.step.out, c.step.accepted):
+            t.zero_()                                   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        now = (c.step.tokens, c.step.score, c.step.anc, c.step.pos, c.step.out, c.step.accepted,
+               c.step.accept_len, c.step.bonus)
+        for x, y in zip(outs, now):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), f"replay {rep}"
+    assert c.step.errors() == 0
