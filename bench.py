@@ -46,7 +46,43 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only eagle_tree_attn (for profiling runs)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of hipGraph replays")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain fp32 copy kernel (torch.neg) over BYTES, for counter calibration")
     return ap.parse_args()
+
+
+ATTN_SOURCES = ("eagle_tree_verification_draft_amd/csrc/tree_attn.hip",
+                "eagle_tree_verification_draft_amd/csrc/common.h",
+                "eagle_tree_verification_draft_amd/csrc/internal.h")
+
+
+def traffic_note(w):
+    """HBM bytes per attention call from the committed counter note for this
+    workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    no note or the kernel source changed since its counters were taken."""
+    from eagle_tree_verification_draft_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"tree_attn.{w.name}.traffic.txt")
+    if not os.path.exists(path):
+        return None, "no counter note for this workload"
+    note = profiling.read_note(path)
+    srcs = [os.path.join(ROOT, s) for s in note.get("source", "").split(",") if s]
+    if not srcs or any(not os.path.exists(s) for s in srcs) or \
+            profiling.source_hash(srcs) != note.get("source_sha256"):
+        return None, "kernel source changed since the counters were taken"
+    return float(note["traffic_bytes_per_call"]), os.path.relpath(path, ROOT)
+
+
+def copy_calibration(nbytes):
+    """A plain copy of known size (read nbytes, write nbytes) for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "kernel": "torch.neg fp32", "dispatches": 3}), flush=True)
 
 
 def log(msg):
@@ -75,6 +111,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification step of one "
               "sequence batch does not span GPUs in this build", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -170,7 +210,7 @@ def main():
     log(f"[bench] timed {K} steps ({'graph replays' if graphs is not None else 'eager'}): "
         f"{ms_per_step * 1e3:.1f} us/step")
 
-    # ---- attention duration: HIP events around the call, eager loop ------
+    # ---- eager steps (context), events around each attention call -----
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     te0 = time.perf_counter()
@@ -179,9 +219,31 @@ def main():
     torch.cuda.synchronize()
     if eager_ms is None:
         eager_ms = (time.perf_counter() - te0) * 1e3 / K
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg_ms = float(np.mean(attn_ms))
-    log(f"[bench] eager {eager_ms * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us")
+    attn_eager_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # ---- attention duration: HIP events around graph replays of back-to-back
+    # attention calls (one per input set) on the stream they run on ----------
+    if graphs is not None:
+        ag = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ag):
+            for S in sets:
+                a = S["attn"]
+                step.attention(a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table, a.prefix_len)
+        ag.replay()
+        reps = max(1, math.ceil(K / nsets))
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record()
+        for _ in range(reps):
+            ag.replay()
+        eb.record()
+        torch.cuda.synchronize()
+        attn_avg_ms = ea.elapsed_time(eb) / (reps * nsets)
+        attn_calls = reps * nsets
+    else:
+        attn_avg_ms, attn_calls = attn_eager_ms, K
+    log(f"[bench] eager {eager_ms * 1e3:.1f} us/step; attention {attn_avg_ms * 1e3:.2f} us/call "
+        f"(eager with events {attn_eager_ms * 1e3:.2f})")
 
     # ---- per-stage breakdown (separate loop, events between the calls) ---
     stage_names = ["build_tree", "tree_mask", "tree_attn", "accept"]
@@ -219,9 +281,18 @@ def main():
         log(f"[bench] WARNING: device error bits {errs:#x}")
 
     nbytes, flops = attn_algorithmic(w, attn0, step.num_nodes)
-    achieved = nbytes / (attn_avg_ms * 1e-3) / 1e9
-    mfma_frac = flops / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    gbs = nbytes / (attn_avg_ms * 1e-3) / 1e9
+    tflops = flops / (attn_avg_ms * 1e-3) / 1e12
+    mfma_frac = tflops / MFMA_BF16_PEAK_TFLOPS
+    # bound: MFMA when the call's arithmetic intensity is past the bf16 ridge
+    # (2.5 PFLOP/s / 8 TB/s = 312 flop/B), HBM otherwise
+    mfma_bound = w.dtype == torch.bfloat16 and flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
+    if mfma_bound:
+        bound, achieved, peak, unit = "mfma", tflops, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
     value = tokens_per_step / (ms_per_step * 1e-3)
+    traffic, traffic_src = traffic_note(w)
 
     # ---- the oracle on the host cores (bounded sample) -------------------
     cpu = None
@@ -249,10 +320,16 @@ def main():
                    "input_sets": nsets, "cold": True,
                    "launch": "graph" if graphs is not None else "eager"},
         "roofline": {"kernel": "k_tree_attn_bf16" if w.dtype == torch.bfloat16 else "k_tree_attn_f32",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": nbytes, "avg_us": round(attn_avg_ms * 1e3, 2),
-                     "mfma_frac": round(mfma_frac, 4)},
+                     "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "traffic_source": traffic_src,
+                     "call": "eagle_tree_attn (k_tree_attn_* plus k_tree_attn_merge when the keys are split)",
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                     "avg_us": round(attn_avg_ms * 1e3, 2), "timed_calls": attn_calls,
+                     "eager_event_us": round(attn_eager_ms * 1e3, 2),
+                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "tflops": round(tflops, 2), "mfma_frac": round(mfma_frac, 4)},
         "cpu_baseline": cpu,
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
