@@ -246,13 +246,13 @@ struct TreeSmem {
     int row[kMaxCand];
     int rank_of[kMaxCand];
     Key KD[kMaxCand + 16];                  // keys of the current depth (+16: segment reads)
-    float FD[kMaxCand + 16];                // the same V rounded to fp32 (order-preserving prefilter)
+    __attribute__((aligned(16))) float FD[kMaxCand + 16];   // the same V rounded to fp32 (order-preserving prefilter)
     int rankD[kMaxCand];                    // rank of a depth-d candidate within its depth
     int cntS[kMaxCand];                     // best-m entries preceding a depth-d candidate
     double conf[kMaxRows * kMaxChildren];   // c of every (row, child)
     int rowCid[kMaxRows * kMaxChildren];    // token of every (row, child)
     Key KS[kMaxMMax + 16];                  // running best-m list
-    float FS[kMaxMMax + 16];
+    __attribute__((aligned(16))) float FS[kMaxMMax + 16];
     Key KSn[kMaxMMax];
     int cntD[kMaxMMax];                     // depth-d candidates preceding a list entry
     int exp_par[kMaxTopk];
@@ -264,20 +264,34 @@ __device__ __forceinline__ bool kbefore(double va, int ia, double vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
-// Entries j in [j0, j0 + 16) of (F, K)[0..len) that come before x.  Rounding
-// to fp32 is monotone, so F_j > F_x implies V_j > V_x; only equal fp32 keys
-// need the exact (V, creation) comparison.
-__device__ __forceinline__ int count_seg(const float *F, const Key *K, int len, int j0, float fx, double vx,
-                                         int ix)
+// Entries j in [j0, j0 + 16) of (F, K)[0..len), j != self, that come before
+// x.  Rounding to fp32 is monotone, so F_j > F_x implies V_j > V_x; only
+// equal fp32 keys (rare) need the exact (V, creation) comparison.  The 16
+// fp32 keys are read as four 16-byte vectors before any comparison, so the
+// segment costs one LDS round trip.
+__device__ __forceinline__ int count_seg(const float *F, const Key *K, int len, int j0, int self, float fx,
+                                         double vx, int ix)
 {
+    const float4 *F4 = reinterpret_cast<const float4 *>(F + j0);
+    float f[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = F4[q];
+        f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+    }
     int cnt = 0;
+    uint32_t eq = 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const int j = j0 + q;
-        const float fj = F[j];
-        int c = fj > fx ? 1 : 0;
-        if (fj == fx) c = kbefore(K[j].v, K[j].i, vx, ix) ? 1 : 0;
-        cnt += j < len ? c : 0;
+        const bool in = j0 + q < len && j0 + q != self;
+        cnt += (in && f[q] > fx) ? 1 : 0;
+        eq |= (in && f[q] == fx) ? (1u << q) : 0u;
+    }
+    while (eq) {
+        const int q = __builtin_ctz(eq);
+        eq &= eq - 1;
+        const Key kj = K[j0 + q];
+        cnt += kbefore(kj.v, kj.i, vx, ix) ? 1 : 0;
     }
     return cnt;
 }
@@ -352,17 +366,17 @@ __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
                 const Key x = sm.KD[i];
                 const float fx = sm.FD[i];
                 if (vsD) {
-                    const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, fx, x.v, x.i);
+                    const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, i, fx, x.v, x.i);
                     if (c) atomicAdd(&sm.rankD[i], c);
                 } else {
-                    const int c = count_seg(sm.FS, sm.KS, sN, 16 * g, fx, x.v, x.i);
+                    const int c = count_seg(sm.FS, sm.KS, sN, 16 * g, -1, fx, x.v, x.i);
                     if (c) atomicAdd(&sm.cntS[i], c);
                 }
             } else {
                 const int u = t - itA - itB;
                 const int g = u / sN, q = u % sN;
                 const Key y = sm.KS[q];
-                const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, sm.FS[q], y.v, y.i);
+                const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, -1, sm.FS[q], y.v, y.i);
                 if (c) atomicAdd(&sm.cntD[q], c);
             }
         }
