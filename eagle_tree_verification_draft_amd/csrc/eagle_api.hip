@@ -169,6 +169,10 @@ static eagle_status check_attn_params(const eagle_attn_params *a, int32_t batch)
     if (a->m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", a->m_max);
     if (a->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", a->m_max, kMaxMMax);
     if (a->block_size < 0 || a->max_prefix < 0) return fail(EAGLE_ERR_INVALID, "negative block_size or max_prefix");
+    if (a->dtype == EAGLE_BF16 && a->block_size == 0 && a->max_prefix % 8 != 0)
+        return fail(EAGLE_ERR_UNSUPPORTED, "bf16 contiguous cache needs max_prefix %% 8 == 0");
+    if (a->block_size == 0 && a->max_prefix > (1 << 24))
+        return fail(EAGLE_ERR_UNSUPPORTED, "contiguous cache above 2^24 keys");
     if (a->block_size > 0) {
         if (a->max_blocks < 1) return fail(EAGLE_ERR_INVALID, "paged cache needs max_blocks >= 1");
         if (a->dtype == EAGLE_BF16 && a->block_size % 8 != 0)

@@ -25,8 +25,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTK = 64;            // keys per tile
 constexpr int kHD = 128;           // head dim of the bf16 path
-constexpr int kKS = kHD + 8;       // LDS row of the K tile, bf16 elements (272 B)
-constexpr int kVS = kTK + 8;       // LDS row of the V^T tile, bf16 elements (144 B)
 constexpr int kMaxWaves = 8;
 
 struct AttnArgs {
@@ -39,7 +37,6 @@ struct AttnArgs {
     uint32_t *err;
     int Hq, Hkv, G, d, m_max, block_size, max_blocks, cap, chunk, nsplit, RG, rows_pg, units0;
     float scale_log2;
-    bool v_vec;   // contiguous V^T rows are 16-byte aligned
 };
 
 __device__ __forceinline__ int swap23(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
@@ -69,6 +66,8 @@ __device__ __forceinline__ const T *v_elem(const AttnArgs &a, int b, int kvh, in
 
 constexpr int kTileChunks = kTK * kHD * 2 / 16;   // 16-byte chunks per K (or V^T) tile: 1024
 constexpr int kMaxPages = 4096 / 8 + 2;             // pages of one split (chunk <= 4096, page >= 8)
+constexpr int kNBuf = 4;                            // LDS ring of K / V^T tiles
+constexpr int kAhead = kNBuf - 1;                   // tiles in flight ahead of the one in use
 
 typedef unsigned int u32x4a __attribute__((ext_vector_type(4)));
 
@@ -85,9 +84,8 @@ struct AttnBuf {
 };
 
 struct AttnSmem {
-    union {
-        AttnBuf buf[2];
-    } u;
+    AttnBuf buf[kNBuf];
+    u32x4a dv[kTK * 16];   // draft V rows as they arrive (key-major, swizzled like K)
     int bt[kMaxPages];
 };
 
@@ -104,10 +102,33 @@ __device__ __forceinline__ void load_lds16(const void *src, void *dst_wave)
                                      (__attribute__((address_space(3))) void *)dst_wave, 16, 0, 0);
 }
 
-__global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
+// s_waitcnt with vmcnt = n and the other counters left free (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
 {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Work items of one workgroup, in processing order: the draft tile (last key
+// split only, when the sequence has nodes), then the prefix tiles of the
+// split.  Every item reaches LDS by direct global->LDS loads, kAhead items
+// ahead of the one being computed, so every wave issues the same number of
+// loads per item and a partial wait (vmcnt) separates the items in flight:
+//   - prefix tile: K rows and V^T chunks; keys at or past prefix_len read the
+//     last valid key (finite data; the scores of those keys are masked), and
+//     V^T entries of those keys are zeroed in LDS before use, since the chunk
+//     that straddles prefix_len may carry anything past it;
+//   - draft tile: K rows of the draft tokens, and their V rows key-major into
+//     sm.dv, transposed to V^T in LDS (zeros for keys >= num_nodes) before use.
+template <int kNW>
+__global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
+{
+    constexpr int kPer = kTileChunks / 64 / kNW;   // 16-byte slots per wave per operand per tile
+    constexpr int kLw = 2 * kPer;                  // loads per wave per item
     __shared__ AttnSmem sm;
-    const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wv = tid >> 6, NW = NT >> 6;
+    const int tid = threadIdx.x, NT = kNW * 64, lane = tid & 63, wv = tid >> 6;
     const int ln = lane & 31, hh = lane >> 5;
     // block -> (split, row group, sequence/kv head); all splits and row groups
     // of one (sequence, kv head) share blockIdx mod 8 when units0 % 8 == 0,
@@ -129,7 +150,7 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
     const int nsplit_b = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
     if (s >= nsplit_b) return;
     const int key_lo = s * a.chunk, key_hi = min(L, key_lo + a.chunk);
-    const bool has_draft = (s == nsplit_b - 1);
+    const bool last_split = (s == nsplit_b - 1);
     const bool paged = a.block_size != 0;
     const int bs = a.block_size;
     const int page0 = paged ? key_lo / bs : 0;
@@ -143,42 +164,24 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
     const int row0 = rg * a.rows_pg + wv * 32;          // first row of this wave
     const int rows_valid = n * G;                        // rows with a real node
     const bool wave_active = row0 < rows_valid && wv * 32 < a.rows_pg;
-    const bool wave_full = row0 + 32 <= rows_valid;
     const int my_row = row0 + ln;
     const int my_node = my_row / G;
-    const bool row_ok = my_row < rows_valid;
+    const bool row_ok = my_row < rows_valid && wv * 32 + ln < a.rows_pg;
 
-    // Q fragments (B operand of S^T = K Q^T): lane holds q[my_row][16ks + 8hh .. +7]
-    bf16x8 qf[8];
-    {
-        const u32x4a *qrow = reinterpret_cast<const u32x4a *>(
-            static_cast<const uint16_t *>(a.q) +
-            (((size_t)b * m_max + (my_node < m_max ? my_node : 0)) * a.Hq + kvh * G + (my_row % G)) * kHD);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            u32x4a v = {0, 0, 0, 0};
-            if (wave_active && my_node < m_max) v = qrow[2 * ks + hh];
-            qf[ks] = as_bf16x8(v);
-        }
-    }
-    uint64_t my_anc = 0;
-    if (row_ok) my_anc = a.anc[(size_t)b * m_max + my_node];
     __syncthreads();   // sm.bt visible
 
     const uint16_t *kc = static_cast<const uint16_t *>(a.kc);
     const uint16_t *vc = static_cast<const uint16_t *>(a.vc);
+    const uint16_t *kd = static_cast<const uint16_t *>(a.kd);
+    const uint16_t *vd = static_cast<const uint16_t *>(a.vd);
     const size_t kvbase = (size_t)b * a.Hkv + kvh;      // contiguous cache: (b, kvh) slab
     const uint16_t *kslab = paged ? kc : kc + kvbase * (size_t)a.cap * kHD;
     const uint16_t *vslab = paged ? vc : vc + kvbase * (size_t)kHD * a.cap;
 
+    const int ndraft = (last_split && n > 0) ? 1 : 0;
     const int nprefix = (key_hi - key_lo + kTK - 1) / kTK;
-    const int ntiles = nprefix + (has_draft ? 1 : 0);
-    // a tile goes global->LDS directly when all 64 keys are valid (and, for a
-    // contiguous cache, V^T rows are 16-byte aligned); otherwise it is staged
-    // through registers with explicit zeros
-    auto direct = [&](int tile) {
-        return tile < nprefix && key_lo + (tile + 1) * kTK <= key_hi && (paged || a.v_vec);
-    };
+    const int nitems = ndraft + nprefix;
+
     auto k_src = [&](int key, int J) -> const uint16_t * {
         if (!paged) return kslab + (size_t)key * kHD + J * 8;
         const int blk = sm.bt[key / bs - page0];
@@ -189,60 +192,68 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
         const int blk = sm.bt[key / bs - page0];
         return vc + (((size_t)blk * a.Hkv + kvh) * kHD + e) * bs + key % bs;
     };
-    // direct loads of a full tile into buffer `bi`: slot = 64 * it + lane
-    auto issue_direct = [&](int tile, int bi) {
-        const int k0 = key_lo + tile * kTK;
-        AttnBuf &B = sm.u.buf[bi];
-        for (int it = wv; it < kTileChunks / 64; it += NW) {
-            const int slot = it * 64 + lane;
-            const int r = slot >> 4, P = slot & 15;
-            load_lds16(k_src(k0 + swap23(r), P ^ (r & 15)), &B.K[it * 64]);
-            const int e = slot >> 3, Q = slot & 7;
-            load_lds16(v_src(e, k0 + 8 * (Q ^ ((e >> 1) & 7))), &B.Vt[it * 64]);
-        }
-    };
-    // register-staged load and store of a tail or draft tile into buffer `bi`
-    auto stage_regs = [&](int tile, int bi) {
-        AttnBuf &B = sm.u.buf[bi];
-        const bool draft = has_draft && tile == ntiles - 1;
-        const int k0 = key_lo + tile * kTK;
-        uint16_t *vt16 = reinterpret_cast<uint16_t *>(B.Vt);
-        for (int c = tid; c < kTileChunks; c += NT) {
-            const int t = c >> 4, J = c & 15;
-            u32x4a kv = {0, 0, 0, 0};
-            if (draft) {
-                u32x4a vv = {0, 0, 0, 0};
-                if (t < n) {
-                    const size_t o = (((size_t)b * m_max + t) * a.Hkv + kvh) * kHD + J * 8;
-                    kv = *reinterpret_cast<const u32x4a *>(static_cast<const uint16_t *>(a.kd) + o);
-                    vv = *reinterpret_cast<const u32x4a *>(static_cast<const uint16_t *>(a.vd) + o);
-                }
-                // draft V arrives key-major: transpose into V^T (dims 8J..8J+7 of key t)
+    const size_t drow = (size_t)b * m_max;               // draft rows of this sequence
+    // pages of 8, 16, 32 or 64 keys tile a 64-key tile exactly (power-of-two
+    // page index arithmetic); other page sizes take the general path
+    const bool fast_pages = !paged || (kTK % bs == 0);
+    const int bshift = paged ? __builtin_ctz(bs) : 0;
+    const size_t pstride = (size_t)a.Hkv * bs * kHD;     // elements per page (K and V^T alike)
+    const size_t kvh_off = (size_t)kvh * bs * kHD;
+    auto issue = [&](int item) {
+        AttnBuf &B = sm.buf[item % kNBuf];
+        if (item < ndraft) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int e = 8 * J + q;
-                    const uint16_t h = (uint16_t)((vv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
-                    vt16[vpos(e, t >> 3) * 8 + (t & 7)] = h;
+            for (int q = 0; q < kPer; ++q) {
+                const int it = wv * kPer + q, slot = it * 64 + lane;
+                const int r = slot >> 4, P = slot & 15;
+                const int t = swap23(r);
+                load_lds16(kd + ((drow + (t < n ? t : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &B.K[it * 64]);
+                load_lds16(vd + ((drow + (r < n ? r : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &sm.dv[it * 64]);
+            }
+        } else if (key_lo + (item - ndraft + 1) * kTK <= key_hi && fast_pages) {
+            // full tile: lane offsets from shifts and masks only
+            const int k0 = key_lo + (item - ndraft) * kTK;
+            if (!paged) {
+                const uint16_t *kt = kslab + (size_t)k0 * kHD, *vt = vslab + k0;
+#pragma unroll
+                for (int q = 0; q < kPer; ++q) {
+                    const int it = wv * kPer + q, slot = it * 64 + lane;
+                    const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
+                    load_lds16(kt + (swap23(r) * kHD + ((P ^ (r & 15)) << 3)), &B.K[it * 64]);
+                    load_lds16(vt + (e * a.cap + ((Q ^ ((e >> 1) & 7)) << 3)), &B.Vt[it * 64]);
                 }
             } else {
-                if (k0 + t < key_hi) kv = *reinterpret_cast<const u32x4a *>(k_src(k0 + t, J));
-                const int e = c >> 3, Jv = c & 7, key = k0 + 8 * Jv;
-                u32x4a vv = {0, 0, 0, 0};
-                if (key < key_hi) {
-                    const uint16_t *vp = v_src(e, key);
-                    uint32_t w[4];
+                const int tp = (k0 >> bshift) - page0;
+                int pk[kPer], pv[kPer];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t lo = (key + 2 * q < key_hi) ? vp[2 * q] : 0u;
-                        const uint32_t hi = (key + 2 * q + 1 < key_hi) ? vp[2 * q + 1] : 0u;
-                        w[q] = lo | (hi << 16);
-                    }
-                    vv = u32x4a{w[0], w[1], w[2], w[3]};
+                for (int q = 0; q < kPer; ++q) {
+                    const int it = wv * kPer + q, slot = it * 64 + lane;
+                    pk[q] = sm.bt[tp + (swap23(slot >> 4) >> bshift)];
+                    pv[q] = sm.bt[tp + ((((slot & 7) ^ ((slot >> 4) & 7)) << 3) >> bshift)];
                 }
-                B.Vt[vpos(e, Jv)] = vv;
+#pragma unroll
+                for (int q = 0; q < kPer; ++q) {
+                    const int it = wv * kPer + q, slot = it * 64 + lane;
+                    const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
+                    const int ko = swap23(r), vj = (Q ^ ((e >> 1) & 7)) << 3;
+                    load_lds16(kc + (size_t)pk[q] * pstride + kvh_off + (((ko & (bs - 1)) * kHD) + ((P ^ (r & 15)) << 3)),
+                               &B.K[it * 64]);
+                    load_lds16(vc + (size_t)pv[q] * pstride + kvh_off + (e * bs + (vj & (bs - 1))), &B.Vt[it * 64]);
+                }
             }
-            const int r = swap23(t);
-            B.K[kpos(r, J)] = kv;
+        } else {
+            const int k0 = key_lo + (item - ndraft) * kTK, klast = key_hi - 1;
+            const int vlast = k0 + ((klast - k0) & ~7);   // first key of the chunk holding klast
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                const int it = wv * kPer + q, slot = it * 64 + lane;
+                const int r = slot >> 4, P = slot & 15;
+                const int key = min(k0 + swap23(r), klast);
+                load_lds16(k_src(key, P ^ (r & 15)), &B.K[it * 64]);
+                const int e = slot >> 3, Q = slot & 7;
+                const int vk = min(k0 + 8 * (Q ^ ((e >> 1) & 7)), vlast);
+                load_lds16(v_src(e, vk), &B.Vt[it * 64]);
+            }
         }
     };
 
@@ -256,58 +267,159 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
     const float c2 = a.scale_log2;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
-    if (ntiles > 0 && direct(0)) issue_direct(0, 0);
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int bi = tile & 1;
-        const bool draft = has_draft && tile == ntiles - 1;
-        const int k0 = key_lo + tile * kTK;
-        if (!direct(tile)) stage_regs(tile, bi);
-        __builtin_amdgcn_s_waitcnt(0);        // this wave's loads into buffer bi have landed
-        __syncthreads();                      // ... and everyone's; tile - 1 is fully consumed
-        if (tile + 1 < ntiles && direct(tile + 1)) issue_direct(tile + 1, bi ^ 1);
-        const AttnBuf &B = sm.u.buf[bi];
+    // The first items' loads go out first; the Q fragments and the ancestor
+    // bits follow, and one full wait covers them all (the compiler cannot
+    // count loads across the data-dependent issue loops, so a later wait for
+    // the Q registers would be a full wait inside the pipeline).
+    for (int i = 0; i < kAhead && i < nitems; ++i) issue(i);
+    // Q fragments (B operand of S^T = K Q^T): lane holds q[my_row][16ks + 8hh .. +7]
+    bf16x8 qf[8];
+    {
+        const u32x4a *qrow = reinterpret_cast<const u32x4a *>(
+            static_cast<const uint16_t *>(a.q) +
+            (((size_t)b * m_max + (my_node < m_max ? my_node : 0)) * a.Hq + kvh * G + (my_row % G)) * kHD);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4a v = {0, 0, 0, 0};
+            if (row_ok) v = qrow[2 * ks + hh];
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+    uint64_t my_anc = 0;
+    if (row_ok) my_anc = a.anc[(size_t)b * m_max + my_node];
+    wait_vmcnt<0>();
+    for (int item = 0; item < nitems; ++item) {
+        // this wave's loads of `item` have landed once at most the loads of
+        // the (up to kAhead - 1) later items issued so far are outstanding
+        const int later = min(kAhead - 1, nitems - 1 - item);
+        if (later >= 2) wait_vmcnt<2 * kLw>();
+        else if (later == 1) wait_vmcnt<kLw>();
+        else wait_vmcnt<0>();
+        __syncthreads();                      // ... and every wave's; item - 1 is fully consumed
+        AttnBuf &B = sm.buf[item % kNBuf];
+        const bool draft = item < ndraft;
+        const int k0 = key_lo + (item - ndraft) * kTK;
+        if (draft) {
+            // draft V rows (key-major) -> V^T, zeros for keys >= n; thread =
+            // (8 dims, 8 keys): an 8x8 block of bf16 transposed in registers
+            if (tid < 128) {
+                const int e8 = tid & 15, kg = tid >> 4;
+                u32x4a rows[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = 8 * kg + u;
+                    rows[u] = t < n ? sm.dv[t * 16 + (e8 ^ (t & 15))] : u32x4a{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int sh = 16 * (q & 1), w = q >> 1;
+                    u32x4a o;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const uint32_t lo = (rows[2 * p][w] >> sh) & 0xffffu;
+                        const uint32_t hi = (rows[2 * p + 1][w] >> sh) & 0xffffu;
+                        o[p] = lo | (hi << 16);
+                    }
+                    B.Vt[vpos(8 * e8 + q, kg)] = o;
+                }
+            }
+            __syncthreads();
+        } else if (k0 + kTK > key_hi) {
+            // tail tile: zero V^T entries of keys >= key_hi in every chunk from
+            // the one holding key_hi on (those chunks were loaded from it)
+            const int lim = key_hi - k0, J0 = lim >> 3, nJ = 8 - J0;
+            for (int c = tid; c < kHD * nJ; c += NT) {
+                const int e = c / nJ, J = J0 + c % nJ;
+                u32x4a v = B.Vt[vpos(e, J)];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int key = 8 * J + 2 * p;
+                    const uint32_t keep = (key < lim ? 0xffffu : 0u) | (key + 1 < lim ? 0xffff0000u : 0u);
+                    v[p] &= keep;
+                }
+                B.Vt[vpos(e, J)] = v;
+            }
+            __syncthreads();
+        }
+        if (item + kAhead < nitems) issue(item + kAhead);
 
         if (wave_active) {
             // ---- S^T = K Q^T: two independent 32-key accumulators ----
+            // the K operands are read from LDS ahead of the products (all of
+            // them with 4 waves; in two halves with 8 waves, two per SIMD,
+            // whose registers hold only half), so the products issue back to
+            // back behind one LDS round trip per group
+            constexpr int kGroup = kNW == 8 ? 4 : 8;
             f32x16 s0, s1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 a0 = as_bf16x8(B.K[kpos(ln, 2 * ks + hh)]);
-                const bf16x8 a1 = as_bf16x8(B.K[kpos(32 + ln, 2 * ks + hh)]);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+            for (int g0 = 0; g0 < 8; g0 += kGroup) {
+                u32x4a ka[kGroup], kb[kGroup];
+#pragma unroll
+                for (int j = 0; j < kGroup; ++j) {
+                    ka[j] = B.K[kpos(ln, 2 * (g0 + j) + hh)];
+                    kb[j] = B.K[kpos(32 + ln, 2 * (g0 + j) + hh)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < kGroup; ++j) {
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[j]), qf[g0 + j], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[g0 + j], s1, 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // s0/s1[8t + q] is the raw score of tile key 32sh + 16t + 8hh + q for row my_row
-            const bool fast = !draft && k0 + kTK <= key_hi && wave_full;
-            if (!fast) {
-                if (draft) {
-                    const uint32_t m0 = (uint32_t)my_anc >> (8 * hh), m1 = (uint32_t)(my_anc >> 32) >> (8 * hh);
+            // the V^T operands of this tile, in flight during the softmax (with
+            // 8 waves, two per SIMD, the registers hold them only after it)
+            constexpr int kEarly = kNW == 8 ? 0 : 16;
+            u32x4a va[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int bit = 16 * (r >> 3) + (r & 7);
-                        s0[r] = (row_ok && ((m0 >> bit) & 1u)) ? s0[r] : -__builtin_inff();
-                        s1[r] = (row_ok && ((m1 >> bit) & 1u)) ? s1[r] : -__builtin_inff();
-                    }
-                } else {
-                    const int lim = key_hi - k0 - 8 * hh;    // tile keys below lim + 8hh are valid
+            for (int j = 0; j < kEarly; ++j) {
+                const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                va[j] = B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // s0/s1[8t + q] is the raw score of tile key 32sh + 16t + 8hh + q for
+            // row my_row.  Rows without a node have zero Q (finite scores, never
+            // written out), so only keys need masking: past prefix_len in the
+            // tail tile, and non-ancestors in the draft tile.
+            if (draft) {
+                const uint32_t m0 = (uint32_t)my_anc >> (8 * hh), m1 = (uint32_t)(my_anc >> 32) >> (8 * hh);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kq = 16 * (r >> 3) + (r & 7);
-                        s0[r] = (row_ok && kq < lim) ? s0[r] : -__builtin_inff();
-                        s1[r] = (row_ok && 32 + kq < lim) ? s1[r] : -__builtin_inff();
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int bit = 16 * (r >> 3) + (r & 7);
+                    s0[r] = ((m0 >> bit) & 1u) ? s0[r] : -__builtin_inff();
+                    s1[r] = ((m1 >> bit) & 1u) ? s1[r] : -__builtin_inff();
+                }
+            } else if (k0 + kTK > key_hi) {
+                const int lim = key_hi - k0 - 8 * hh;    // tile keys below lim + 8hh are valid
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kq = 16 * (r >> 3) + (r & 7);
+                    s0[r] = kq < lim ? s0[r] : -__builtin_inff();
+                    s1[r] = 32 + kq < lim ? s1[r] : -__builtin_inff();
                 }
             }
             float tmax = -__builtin_inff();
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            // Lazy rescaling: the exponent reference m_run moves (and O, l are
+            // rescaled) only when some row's max grew by more than 2^8 in exp2
+            // units; otherwise p = exp2((s - m_run) c) <= 2^8, which fp32 sums
+            // and bf16 products carry exactly as well, and O / l is unchanged.
             const float m_new = fmaxf(m_run, tmax);
-            const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-            const float mc = m_use * c2;
-            const float corr = __builtin_amdgcn_exp2f(m_run * c2 - mc);
+            if (__any((m_new - m_run) * c2 > 8.0f)) {
+                const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+                const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+                l_run *= corr;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
+                m_run = m_new;
+            }
+            const float mc = (m_run == -__builtin_inff() ? 0.0f : m_run) * c2;
             float lsum = 0.0f;
             bf16x8 pf[2][2];
 #pragma unroll
@@ -319,29 +431,33 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
                 pf[1][r >> 3][r & 7] = (__bf16)p1;
             }
             lsum += __shfl_xor(lsum, 32);
-            l_run = l_run * corr + lsum;
-            m_run = m_new;
-            if (__any(corr != 1.0f)) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
-            }
+            l_run += lsum;
             // ---- O^T += V^T P^T: four independent accumulators per k-step ----
+            if constexpr (kEarly == 16) {
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
+                for (int j = 0; j < 16; ++j) {
+                    const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[sh][t], oacc[dt], 0, 0, 0);
+                }
+            } else {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int g0 = 0; g0 < 16; g0 += 8) {
 #pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        const bf16x8 av = as_bf16x8(B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)]);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[sh][t], oacc[dt], 0, 0, 0);
+                    for (int j = g0; j < g0 + 8; ++j) {
+                        const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                        va[j] = B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = g0; j < g0 + 8; ++j) {
+                        const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[sh][t], oacc[dt], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
     }
-    __syncthreads();
 
     // ---- epilogue ----
     // oacc[dt][r] is O^T[d = 32dt + 8(r>>2) + 4hh + (r&3)][my_row]
@@ -365,10 +481,11 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
         }
         return;
     }
-    const int unit = u0 * a.RG + rg;
-    const size_t pbase = ((size_t)unit * a.nsplit + s) * a.rows_pg;
-    const int row_local = wv * 32 + ln;
-    if (row_local < a.rows_pg) {
+    // partials of the rows with a real node only (the merge reads no others)
+    if (row_ok) {
+        const int unit = u0 * a.RG + rg;
+        const size_t pbase = ((size_t)unit * a.nsplit + s) * a.rows_pg;
+        const int row_local = wv * 32 + ln;
         float *po = a.part_o + (pbase + row_local) * kHD;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -379,7 +496,7 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16(AttnArgs a)
                     make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
             }
         // partial max in log2 units (raw max times c), as the merge expects
-        if (hh == 0) a.part_ml[pbase + row_local] = make_float2(row_ok ? m_run * c2 : -__builtin_inff(), row_ok ? l_run : 0.0f);
+        if (hh == 0) a.part_ml[pbase + row_local] = make_float2(m_run * c2, l_run);
     }
 }
 
@@ -558,17 +675,29 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
     }
     P.row_groups = (P.rows + 32 * kMaxWaves - 1) / (32 * kMaxWaves);
     const int rows_pg = (P.rows + P.row_groups - 1) / P.row_groups;
-    P.waves = (rows_pg + 31) / 32;
-    if (P.waves < 4) P.waves = 4;   // extra waves only help stage K/V
+    // 4 or 8 waves (the load slots of a tile divide evenly); waves past the
+    // rows only help load
+    P.waves = rows_pg <= 128 ? 4 : 8;
     const int units = batch * a->num_kv_heads * P.row_groups;
-    const int Lb = P.max_prefix > 0 ? P.max_prefix : 1;
-    const int target = units > 0 ? (512 + units - 1) / units : 1;
-    int chunk = (Lb + target - 1) / target;
-    chunk = (chunk + kTK - 1) / kTK * kTK;
-    if (chunk < 256) chunk = 256;
-    if (chunk > 4096) chunk = 4096;
-    P.chunk = chunk;
-    P.nsplit = (Lb + chunk - 1) / chunk;
+    // Key splits: one workgroup per CU (the LDS ring fills most of it), so a
+    // launch runs in rounds of kCUs workgroups.  Pick the split count that
+    // minimises rounds x tiles per split (ties: fewer splits), with at most 64
+    // tiles (4096 keys) and, when the prefix allows, at least 4 tiles per split.
+    constexpr long long kCUs = 256;
+    const int tiles = P.max_prefix > 0 ? (P.max_prefix + kTK - 1) / kTK : 1;
+    const int ns_lo = (tiles + 63) / 64;
+    const int ns_hi = tiles >= 4 * ns_lo ? tiles / 4 : ns_lo;
+    int best = ns_lo;
+    long long best_cost = -1;
+    for (int ns = ns_lo; ns <= ns_hi; ++ns) {
+        const long long per = (tiles + ns - 1) / ns;
+        const long long rounds = ((long long)units * ns + kCUs - 1) / kCUs;
+        const long long cost = rounds * per;
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = ns; }
+    }
+    const int per = (tiles + best - 1) / best;
+    P.chunk = per * kTK;
+    P.nsplit = (tiles + per - 1) / per;
     const size_t rows_alloc = (size_t)units * P.nsplit * (size_t)(32 * ((rows_pg + 31) / 32));
     size_t o = kWsHeader;
     P.off_part = o; o = align_up(o + (P.nsplit > 1 ? rows_alloc * kHD * sizeof(float) : 0), 256);
@@ -602,13 +731,15 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     a.units0 = batch * p->num_kv_heads;
     const float scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.v_vec = (p->block_size > 0) || (p->max_prefix % 8 == 0);
     if (p->dtype == EAGLE_F32) {
         const dim3 g((unsigned)(batch * p->m_max * p->num_q_heads));
         hipLaunchKernelGGL(k_tree_attn_f32, g, dim3(64), 0, st, a);
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
-        hipLaunchKernelGGL(k_tree_attn_bf16, g, dim3(64 * P.waves), 0, st, a);
+        if (P.waves == 4)
+            hipLaunchKernelGGL(k_tree_attn_bf16<4>, g, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_tree_attn_bf16<8>, g, dim3(512), 0, st, a);
         if (P.nsplit > 1) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

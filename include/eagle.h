@@ -162,7 +162,9 @@ eagle_status eagle_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent
  *   k_draft, v_draft  [batch][m_max][num_kv_heads][head_dim]
  *   contiguous cache (block_size == 0):
  *     k_cache [batch][num_kv_heads][max_prefix][head_dim]
- *     v_cache [batch][num_kv_heads][head_dim][max_prefix]   (V stored transposed)
+ *     v_cache [batch][num_kv_heads][head_dim][max_prefix]   (V stored transposed;
+ *     bf16 needs max_prefix % 8 == 0 so that V^T rows are 16-byte aligned;
+ *     max_prefix <= 2^24)
  *   paged cache (block_size > 0), block_table [batch][max_blocks] (-1 = unused):
  *     k_cache [num_blocks][num_kv_heads][block_size][head_dim]
  *     v_cache [num_blocks][num_kv_heads][head_dim][block_size]

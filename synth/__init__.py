@@ -232,7 +232,8 @@ def attn_inputs(w: Workload, seed: int, device="cpu", prefix_seed: Optional[int]
     v_draft = _normal((B, M, Hkv, d), 1.0, w.dtype, gdk, device)
     gkv = _gen(seed, "kv", device)
     if w.block_size == 0:
-        L = int(plen.max())
+        # capacity = longest prefix rounded up to 8 keys (16-byte V^T rows in bf16)
+        L = (int(plen.max()) + 7) // 8 * 8
         k_cache = _normal((B, Hkv, L, d), 1.0, w.dtype, gkv, device)
         v_cache = _normal((B, Hkv, d, L), 1.0, w.dtype, gkv, device)
         return AttnInputs(q, k_draft, v_draft, k_cache, v_cache, None, plen.to(device), 0, L)

@@ -93,6 +93,7 @@ def _call_attn(a, bt=True, align=0, ws=1 << 21, wsb=1 << 30):
     (dict(dtype=E.EAGLE_F32, head_dim=96), E.EAGLE_ERR_UNSUPPORTED),
     (dict(m_max=65), E.EAGLE_ERR_UNSUPPORTED),
     (dict(block_size=12), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(block_size=0, max_blocks=0, max_prefix=13), E.EAGLE_ERR_UNSUPPORTED),
     (dict(max_blocks=0), E.EAGLE_ERR_INVALID),
     (dict(scale=float("nan")), E.EAGLE_ERR_INVALID),
 ])
