@@ -189,7 +189,7 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
             const int i = sm.sel[tid];
             const size_t o2 = ((size_t)b * a.r_max + r) * a.children + tid;
             a.top_id[o2] = sm.cand_i[i];
-            a.top_w[o2] = (double)weight_of(sm.cand_v[i], M);
+            a.conf[o2] = (double)weight_of(sm.cand_v[i], M) / W;
         }
     } else {
         // heavy ties or thr == -inf: C rounds of "best element after the
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
             if (tid == 0) {
                 const size_t o2 = ((size_t)b * a.r_max + r) * a.children + c;
                 a.top_id[o2] = bi;
-                a.top_w[o2] = (double)weight_of(bv, M);
+                a.conf[o2] = (double)weight_of(bv, M) / W;
             }
             pv = bv;
             pi = bi;
@@ -222,81 +222,38 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: one workgroup per sequence.  Candidates live in LDS in creation
-// order; every confidence c = w / W is computed once, in parallel, up front.
-// Depth by depth, one pass of comparisons (split into segments of kSeg, one
-// segment per thread, partial counts added with LDS atomics) yields for each
-// depth-d candidate its rank among the depth (the top-k are expanded) and the
-// number of entries of the running best-m list that precede it, and for each
-// entry of that list the number of depth-d candidates that precede it.
-// Those counts are the positions of the merged list, which after the last
-// depth is the rerank's top-m in rank order.
+// Kernel 2: one workgroup per sequence, everything in LDS.  Candidates are
+// numbered in creation order; the candidates of one depth form lists of C
+// (the children of one expanded node, or of the root), and every entry of a
+// list precedes every entry of a later list in creation order.  Per depth:
+//   - the rank of each candidate within its depth, by (V desc, creation asc),
+//     is the number of entries of every list of the depth that come first: one
+//     (candidate, list) pair per thread, partial counts added with LDS atomics
+//     (no ordering inside a list is assumed);
+//   - the candidates are scattered to rank order; the first k are expanded.
+// The rerank then merges the depths' rank-ordered lists: a candidate's overall
+// rank is its rank within its depth plus, for every other depth, how many of
+// that depth's first m entries come first (binary search: earlier depths win
+// ties, later depths lose them).  Ranks below m are the selected nodes.
 // ---------------------------------------------------------------------------
-struct Key {
-    double v;
-    int i;
-    int pad;
-};
-
 struct TreeSmem {
-    double V[kMaxCand];
+    double conf[kMaxRows * kMaxChildren];   // c of every (row, child)
+    int cid[kMaxRows * kMaxChildren];       // token of every (row, child)
+    double V[kMaxCand + kMaxChildren];      // by creation index (+ slack: whole-list reads)
+    double sV[kMaxCand];                    // V in rank order, each depth at its offset
+    int ord[kMaxCand];                      // creation index in rank order, each depth at its offset
     int tok[kMaxCand];
     int par[kMaxCand];
     int dep[kMaxCand];
     int row[kMaxCand];
-    int rank_of[kMaxCand];
-    Key KD[kMaxCand + 16];                  // keys of the current depth (+16: segment reads)
-    __attribute__((aligned(16))) float FD[kMaxCand + 16];   // the same V rounded to fp32 (order-preserving prefilter)
-    int rankD[kMaxCand];                    // rank of a depth-d candidate within its depth
-    int cntS[kMaxCand];                     // best-m entries preceding a depth-d candidate
-    double conf[kMaxRows * kMaxChildren];   // c of every (row, child)
-    int rowCid[kMaxRows * kMaxChildren];    // token of every (row, child)
-    Key KS[kMaxMMax + 16];                  // running best-m list
-    __attribute__((aligned(16))) float FS[kMaxMMax + 16];
-    Key KSn[kMaxMMax];
-    int cntD[kMaxMMax];                     // depth-d candidates preceding a list entry
-    int exp_par[kMaxTopk];
+    int rank_d[kMaxCand];                   // rank within the depth
+    int ahead[kMaxCand];                    // entries of other depths that come first
+    int rank_of[kMaxCand];                  // overall rank, -1 if not selected
+    int sel[kMaxMMax];                      // creation index by overall rank
+    int lvl_off[kMaxDepth + 1];             // first creation index of each depth, then N
 };
 
-// (V desc, creation asc)
-__device__ __forceinline__ bool kbefore(double va, int ia, double vb, int ib)
-{
-    return va > vb || (va == vb && ia < ib);
-}
-
-// Entries j in [j0, j0 + 16) of (F, K)[0..len), j != self, that come before
-// x.  Rounding to fp32 is monotone, so F_j > F_x implies V_j > V_x; only
-// equal fp32 keys (rare) need the exact (V, creation) comparison.  The 16
-// fp32 keys are read as four 16-byte vectors before any comparison, so the
-// segment costs one LDS round trip.
-__device__ __forceinline__ int count_seg(const float *F, const Key *K, int len, int j0, int self, float fx,
-                                         double vx, int ix)
-{
-    const float4 *F4 = reinterpret_cast<const float4 *>(F + j0);
-    float f[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float4 v = F4[q];
-        f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
-    }
-    int cnt = 0;
-    uint32_t eq = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const bool in = j0 + q < len && j0 + q != self;
-        cnt += (in && f[q] > fx) ? 1 : 0;
-        eq |= (in && f[q] == fx) ? (1u << q) : 0u;
-    }
-    while (eq) {
-        const int q = __builtin_ctz(eq);
-        eq &= eq - 1;
-        const Key kj = K[j0 + q];
-        cnt += kbefore(kj.v, kj.i, vx, ix) ? 1 : 0;
-    }
-    return cnt;
-}
-
-__global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
+__global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
 {
     __shared__ TreeSmem sm;
     const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x;
@@ -312,8 +269,7 @@ __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
         if (tid == 0) {
             double Vp = 1.0;
             for (int i = 0; i < K; ++i) {
-                const double c = a.top_w[(rb + i) * Cw] / a.W[rb + i];
-                Vp = Vp * c;
+                Vp = Vp * a.conf[(rb + i) * Cw];
                 tokens[i] = a.top_id[(rb + i) * Cw];
                 parent[i] = i - 1;
                 depth[i] = i + 1;
@@ -330,116 +286,146 @@ __global__ __launch_bounds__(512) void k_tree_select(TreeSelectArgs a)
 
     const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
     const int R = 1 + (D - 1) * k;
-    // confidences of every (row, child), in parallel
     for (int i = tid; i < R * C; i += NT) {
-        const int r = i / C, j = i % C;
-        sm.conf[i] = a.top_w[(rb + r) * Cw + j] / a.W[rb + r];
-        sm.rowCid[i] = a.top_id[(rb + r) * Cw + j];
+        const int r = i / C, j = i - r * C;
+        sm.conf[i] = a.conf[(rb + r) * Cw + j];
+        sm.cid[i] = a.top_id[(rb + r) * Cw + j];
+    }
+    for (int i = tid; i < kMaxCand; i += NT) {
+        sm.rank_d[i] = 0;
+        sm.ahead[i] = 0;
+        sm.rank_of[i] = -1;
     }
     __syncthreads();
-    // depth 1: children of the root's row 0
+    // depth 1: the children of the root's row 0, one list
     for (int j = tid; j < C; j += NT) {
         sm.V[j] = sm.conf[j];
-        sm.KD[j] = Key{sm.conf[j], j, 0};
-        sm.FD[j] = (float)sm.conf[j];
-        sm.rankD[j] = 0;
-        sm.cntS[j] = 0;
-        sm.tok[j] = sm.rowCid[j];
+        sm.tok[j] = sm.cid[j];
         sm.par[j] = -1;
         sm.dep[j] = 1;
         sm.row[j] = -1;
     }
+    if (tid == 0) sm.lvl_off[0] = 0;
     __syncthreads();
-    int begin = 0, end = C, sN = 0;
-    for (int d = 1; d <= D; ++d) {
-        const int nd = end - begin;
-        // ---- counts: rank within the depth, and the merge positions ----
-        // items: (segment of D, x in D), (segment of S, x in D), (segment of D, y in S);
-        // consecutive threads share a segment
-        const int segD = (nd + 15) / 16, segS = (sN + 15) / 16;
-        const int itA = segD * nd, itB = segS * nd, itC = segD * sN;
-        for (int t = tid; t < itA + itB + itC; t += NT) {
-            if (t < itA + itB) {
-                const bool vsD = t < itA;
-                const int u = vsD ? t : t - itA;
-                const int g = u / nd, i = u % nd;
-                const Key x = sm.KD[i];
-                const float fx = sm.FD[i];
-                if (vsD) {
-                    const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, i, fx, x.v, x.i);
-                    if (c) atomicAdd(&sm.rankD[i], c);
-                } else {
-                    const int c = count_seg(sm.FS, sm.KS, sN, 16 * g, -1, fx, x.v, x.i);
-                    if (c) atomicAdd(&sm.cntS[i], c);
+
+    int off = 0, n = C, nl = 1;   // this depth: first creation index, candidates, lists
+    for (int lv = 0; lv < D; ++lv) {
+        // ---- rank within the depth: pairs (candidate x, list q) ----
+        // consecutive threads take consecutive x of one list q, so the reads
+        // of q's entries are broadcasts; a thread keeps its x and steps q
+        {
+            const int lanes_x = n < NT ? n : NT;
+            const int qstep = NT / lanes_x;
+            const int x0 = tid % lanes_x, q0 = tid / lanes_x;
+            for (int x = x0; q0 < qstep && x < n; x += lanes_x) {
+                const int p = x / C, j = x - p * C;
+                const double vx = sm.V[off + x];
+                int c = 0;
+                for (int q = q0; q < nl; q += qstep) {
+                    // the whole list is read first (one LDS round trip); slots
+                    // past C are read but not counted
+                    const double *L = sm.V + off + q * C;
+                    double vl[kMaxChildren];
+#pragma unroll
+                    for (int i = 0; i < kMaxChildren; ++i) vl[i] = L[i];
+                    // bit i set: entry i of q precedes x when its V equals x's
+                    // (earlier lists entirely; in x's own list, entries before x)
+                    const uint32_t tie = q < p ? 0xffffu : (q == p ? (1u << j) - 1u : 0u);
+#pragma unroll
+                    for (int i = 0; i < kMaxChildren; ++i)
+                        c += (i < C && (vl[i] > vx || (vl[i] == vx && ((tie >> i) & 1u)))) ? 1 : 0;
                 }
-            } else {
-                const int u = t - itA - itB;
-                const int g = u / sN, q = u % sN;
-                const Key y = sm.KS[q];
-                const int c = count_seg(sm.FD, sm.KD, nd, 16 * g, -1, sm.FS[q], y.v, y.i);
-                if (c) atomicAdd(&sm.cntD[q], c);
+                if (c) atomicAdd(&sm.rank_d[off + x], c);
             }
         }
         __syncthreads();
-        // ---- positions: merged list, expansion ----
-        const int ne = d < D ? min(k, nd) : 0;
-        for (int t = tid; t < nd + sN; t += NT) {
-            if (t < nd) {
-                const int rd = sm.rankD[t], pos = rd + sm.cntS[t];
-                const Key x = sm.KD[t];
-                if (pos < m) sm.KSn[pos] = x;
-                if (rd < ne) {
-                    sm.exp_par[rd] = x.i;
-                    sm.row[x.i] = 1 + (d - 1) * k + rd;
-                }
-            } else {
-                const int q = t - nd, pos = q + sm.cntD[q];
-                if (pos < m) sm.KSn[pos] = sm.KS[q];
-            }
+        for (int x = tid; x < n; x += NT) {
+            const int r = sm.rank_d[off + x];
+            sm.ord[off + r] = off + x;
+            sm.sV[off + r] = sm.V[off + x];
         }
         __syncthreads();
-        // ---- children of the expanded nodes (the next depth's keys); new list ----
+        if (lv + 1 == D) break;
+        // ---- expansion: the first k in rank order own rows 1 + lv k + p ----
+        const int ne = min(k, n), noff = off + n;
         for (int t = tid; t < ne * C; t += NT) {
-            const int p = t / C, j = t % C;
-            const int pidx = sm.exp_par[p];
-            const int r = 1 + (d - 1) * k + p;
-            const double v = sm.V[pidx] * sm.conf[r * C + j];
-            sm.V[end + t] = v;
-            sm.KD[t] = Key{v, end + t, 0};
-            sm.FD[t] = (float)v;
-            sm.rankD[t] = 0;
-            sm.cntS[t] = 0;
-            sm.tok[end + t] = sm.rowCid[r * C + j];
-            sm.par[end + t] = pidx;
-            sm.dep[end + t] = d + 1;
-            sm.row[end + t] = -1;
+            const int p = t / C, j = t - p * C;
+            const int e = sm.ord[off + p], r = 1 + lv * k + p, g = noff + t;
+            sm.V[g] = sm.V[e] * sm.conf[r * C + j];
+            sm.tok[g] = sm.cid[r * C + j];
+            sm.par[g] = e;
+            sm.dep[g] = lv + 2;
+            sm.row[g] = -1;
+            if (j == 0) sm.row[e] = r;
         }
-        sN = min(m, sN + nd);
-        for (int q = tid; q < sN; q += NT) {
-            const Key kq = sm.KSn[q];
-            sm.KS[q] = kq;
-            sm.FS[q] = (float)kq.v;
-            sm.cntD[q] = 0;
-        }
+        if (tid == 0) sm.lvl_off[lv + 1] = noff;
         __syncthreads();
-        begin = end;
-        end += ne * C;
+        off = noff;
+        n = ne * C;
+        nl = ne;
     }
-    const int N = begin;
-    for (int i = tid; i < N; i += NT) sm.rank_of[i] = -1;
+    const int N = off + n;
+
+    // ---- rerank: merge the depths' rank-ordered lists (first m of each) ----
+    // item = (entry i < m of depth lv, other depth od); the depth sizes follow
+    // from (C, k) alone, so items are located without reading LDS
+    if (tid == 0) sm.lvl_off[D] = N;
     __syncthreads();
-    for (int r = tid; r < m; r += NT) sm.rank_of[sm.KS[r].i] = r;
-    __syncthreads();
-    // connected tree check (holds by construction: V never grows along a path)
-    for (int r = tid; r < m; r += NT) {
-        const int i = sm.KS[r].i;
-        int q = sm.par[i];
-        while (q >= 0) {
-            if (sm.rank_of[q] < 0) { raise_error(a.err, EAGLE_DEVERR_CLOSURE); break; }
-            q = sm.par[q];
+    int items = 0;
+    if (D > 1) {
+        int nn = C;
+        for (int lv = 0; lv < D; ++lv) {
+            items += min(nn, m) * (D - 1);
+            nn = min(k, nn) * C;
         }
+    }
+    for (int t = tid; t < items; t += NT) {
+        int lv = 0, nn = C, base = 0, o = 0;
+        while (base + min(nn, m) * (D - 1) <= t) {
+            base += min(nn, m) * (D - 1);
+            o += nn;
+            nn = min(k, nn) * C;
+            ++lv;
+        }
+        const int u = t - base, i = u / (D - 1);
+        int od = u - i * (D - 1);
+        od += od >= lv ? 1 : 0;
+        const double v = sm.sV[o + i];
+        const int so = sm.lvl_off[od];
+        const double *s = sm.sV + so;
+        const bool win_ties = od < lv;   // earlier depth: smaller creation indices
+        // the entries of od that come first are a prefix of its rank order
+        int lo = 0, hi = min(sm.lvl_off[od + 1] - so, m);
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const double y = s[mid];
+            if (y > v || (win_ties && y == v)) lo = mid + 1;
+            else hi = mid;
+        }
+        if (lo) atomicAdd(&sm.ahead[sm.ord[o + i]], lo);
+    }
+    __syncthreads();
+    for (int g = tid; g < N; g += NT) {
+        const int rd = sm.rank_d[g];
+        if (rd < m) {
+            const int r = rd + sm.ahead[g];
+            if (r < m) {
+                sm.sel[r] = g;
+                sm.rank_of[g] = r;
+            }
+        }
+    }
+    __syncthreads();
+    // connected tree check: every selected node's parent is selected (then,
+    // by induction, every ancestor is).  It holds by construction: c <= 1, so
+    // V never grows along a path, and parents are created before children.
+    for (int r = tid; r < m; r += NT) {
+        const int i = sm.sel[r];
+        const int q = sm.par[i];
+        const int pr = q < 0 ? -1 : sm.rank_of[q];
+        if (q >= 0 && pr < 0) raise_error(a.err, EAGLE_DEVERR_CLOSURE);
         tokens[r] = sm.tok[i];
-        parent[r] = sm.par[i] < 0 ? -1 : sm.rank_of[sm.par[i]];
+        parent[r] = pr;
         depth[r] = sm.dep[i];
         score[r] = sm.V[i];
         src_row[r] = sm.row[i];
@@ -461,7 +447,7 @@ BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
     L.off_M = o;      o = align_up(o + rows * sizeof(float), 256);
     L.off_W = o;      o = align_up(o + rows * sizeof(double), 256);
     L.off_id = o;     o = align_up(o + rows * p->children * sizeof(int32_t), 256);
-    L.off_w = o;      o = align_up(o + rows * p->children * sizeof(double), 256);
+    L.off_c = o;      o = align_up(o + rows * p->children * sizeof(double), 256);
     L.total = o;
     return L;
 }
@@ -506,7 +492,7 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ra.M = reinterpret_cast<float *>(base + L.off_M);
     ra.W = reinterpret_cast<double *>(base + L.off_W);
     ra.top_id = reinterpret_cast<int32_t *>(base + L.off_id);
-    ra.top_w = reinterpret_cast<double *>(base + L.off_w);
+    ra.conf = reinterpret_cast<double *>(base + L.off_c);
     ra.err = reinterpret_cast<uint32_t *>(base);
     const size_t esz = dt == EAGLE_F32 ? 4 : 2;
     ra.vec_ok = ((uintptr_t)logits % 16 == 0) && ((size_t)row_stride * esz % 16 == 0);
@@ -540,9 +526,8 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ta.chain_k = p->chain_k;
     ta.m_max = p->m_max;
     ta.r_max = p->r_max;
-    ta.W = ra.W;
     ta.top_id = ra.top_id;
-    ta.top_w = ra.top_w;
+    ta.conf = ra.conf;
     ta.tokens = tokens;
     ta.parent = parent;
     ta.depth = depth;
@@ -551,7 +536,7 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ta.num_nodes = num_nodes;
     ta.err = ra.err;
     if (batch > 0) {
-        hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(512), 0, st, ta);
+        hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(1024), 0, st, ta);
         return hipGetLastError();
     }
     return hipSuccess;

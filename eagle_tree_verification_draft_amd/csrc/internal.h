@@ -24,7 +24,7 @@ struct RowStatsArgs {
     float *M;
     double *W;
     int32_t *top_id;
-    double *top_w;
+    double *conf;      // c = w / W of every (row, child)
     uint32_t *err;
     bool vec_ok;
 };
@@ -32,9 +32,8 @@ struct RowStatsArgs {
 struct TreeSelectArgs {
     const int32_t *kind;
     int depth_max, topk, children, m, chain_k, m_max, r_max;
-    const double *W;
     const int32_t *top_id;
-    const double *top_w;
+    const double *conf;
     int32_t *tokens, *parent, *depth;
     double *score;
     int32_t *src_row, *num_nodes;
@@ -42,7 +41,7 @@ struct TreeSelectArgs {
 };
 
 struct BuildLayout {
-    size_t off_M, off_W, off_id, off_w, total;
+    size_t off_M, off_W, off_id, off_c, total;
 };
 BuildLayout build_layout(const eagle_tree_params *p, int32_t batch);
 int row_vectors(int vocab, int vec);
