@@ -8,20 +8,26 @@
 namespace eagle {
 
 // ---------------------------------------------------------------------------
-// Kernel 1: one workgroup per draft row.  The row is read once from HBM with
-// 16-byte loads (coalesced across the workgroup) and kept in registers:
-//   M = row max; W = sum of exact integer weights (fp64, exact in any order);
-//   top-C by (logit desc, id asc): every top-C element is >= T, where T is the
-//   largest over waves of the C-th largest lane maximum in that wave (C lanes
-//   of that wave hold an element >= T, so the C-th largest of the row is >= T).
-//   Elements >= T are appended to an LDS list during the weight pass and
-//   ranked there.  If more than kCandCap qualify (heavy ties), C rounds of
-//   block argmax over the row select exactly.
+// Kernel 1: draft-row statistics, one workgroup per draft row r: M = row max;
+// the exact integer weights w = W35(l - M) summed in fp64 (exact in any
+// order); and the top-C by (logit desc, id asc), written in rank order with
+// their logits (the tree kernel forms c = w / W from them).
+//
+// Two forms:
+//   - k_row_stats (few rows, where latency matters): the row is read once with
+//     16-byte coalesced loads and kept in registers across up to 1024 threads;
+//   - k_row_stats_stream (many rows or long rows): a streaming max pass, then a
+//     streaming weight pass over the same lines (second read from L2), with
+//     few registers, so two workgroups share a compute unit and overlap.
+//
+// Candidates: every element >= T, with T such that at least C elements are
+// >= T: with at least C waves, the C-th largest wave maximum (C waves hold
+// such an element); otherwise the largest over waves of the C-th largest lane
+// maximum of the wave.  They are appended to an LDS list during the weight
+// pass and ranked there; if more than kCandCap qualify (heavy ties) or
+// T = -inf, C rounds of block argmax over the row select exactly.
 // ---------------------------------------------------------------------------
 constexpr int kCandCap = 2048;
-
-// threads per row: up to 1024 while a row fits 8 vectors per thread, 512 above
-template <int kNV> struct RowMaxThreads { static constexpr int n = kNV <= 8 ? 1024 : 512; };
 
 template <typename T> struct Vec;
 template <> struct Vec<float> { static constexpr int n = 4; };
@@ -47,35 +53,25 @@ __device__ __forceinline__ float load_scalar(const T *p);
 template <> __device__ __forceinline__ float load_scalar<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
-// Loads this thread's part of a row: vector j holds elements [(j*NT + tid)*VEC, +VEC).
-// Missing elements read as -inf (never a candidate, weight 0).
-template <typename T, int kNV>
-__device__ __forceinline__ void load_row(const T *row, int V, bool vec_ok, uint4 (&x)[kNV])
+// One 16-byte vector of a row starting at element `base`; missing elements
+// read as -inf (never a candidate, weight 0).
+template <typename T>
+__device__ __forceinline__ uint4 load_vec(const T *row, int base, int V, bool vec_ok)
 {
     constexpr int VEC = Vec<T>::n;
-    const int NT = blockDim.x, tid = threadIdx.x;
+    if (vec_ok && base + VEC <= V) return *reinterpret_cast<const uint4 *>(row + base);
+    float f[8];
 #pragma unroll
-    for (int j = 0; j < kNV; ++j) {
-        const int base = (j * NT + tid) * VEC;
-        if (vec_ok && base + VEC <= V) {
-            x[j] = ld16_stream(row + base);
-        } else {
-            float f[8];
+    for (int e = 0; e < VEC; ++e) f[e] = (base + e < V) ? load_scalar<T>(row + base + e) : -__builtin_inff();
+    if constexpr (VEC == 4) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    } else {
+        // re-pack to bf16 pairs (values came from bf16, so truncation is exact)
+        uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                f[e] = (base + e < V) ? load_scalar<T>(row + base + e) : -__builtin_inff();
-            if constexpr (VEC == 4) {
-                x[j] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                                  __float_as_uint(f[3]));
-            } else {
-                // re-pack to bf16 pairs (values came from bf16, so truncation is exact)
-                uint32_t w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = (__float_as_uint(f[2 * e]) >> 16) | (__float_as_uint(f[2 * e + 1]) & 0xffff0000u);
-                x[j] = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        }
+        for (int e = 0; e < 4; ++e)
+            w[e] = (__float_as_uint(f[2 * e]) >> 16) | (__float_as_uint(f[2 * e + 1]) & 0xffff0000u);
+        return make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
@@ -89,58 +85,114 @@ struct RowStatsSmem {
     int count;
 };
 
-template <typename T, int kNV>
-__global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArgs a)
+// Candidate threshold: needs sm.red.f = the wave maxima (left there by
+// block_max) when C <= waves, else the per-lane maxima.
+__device__ __forceinline__ float row_threshold(float lmax, int C, RowStatsSmem &sm)
 {
-    constexpr int VEC = Vec<T>::n;
-    __shared__ RowStatsSmem sm;
-    const int b = blockIdx.x / a.r_max, r = blockIdx.x % a.r_max;
-    const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
-    const int rows_needed = kind == EAGLE_TREE_CHAIN ? a.chain_k : a.rows_dyn;
-    if (r >= rows_needed) return;
-    const int C = kind == EAGLE_TREE_CHAIN ? 1 : a.children;
-    const int V = a.vocab, NT = blockDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const T *row = static_cast<const T *>(a.logits) + ((size_t)b * a.r_max + r) * (size_t)a.row_stride;
-
-    uint4 x[kNV];
-    load_row<T, kNV>(row, V, a.vec_ok, x);
-
-    // row max and per-lane max
-    // (the max pass unpacks opaque copies so that the unpacked values are not
-    // kept live until the weight pass)
-    float lmax = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < kNV; ++j) {
-        float f[VEC];
-        unpack<T>(opaque(x[j]), f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
-        if constexpr (kNV > 16) __builtin_amdgcn_sched_barrier(0);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+    if (C <= nw) {
+        if (tid < nw) {
+            const float fj = sm.red.f[tid];
+            int gt = 0, ge = 0;
+            for (int i = 0; i < nw; ++i) {
+                const float fi = sm.red.f[i];
+                gt += fi > fj ? 1 : 0;
+                ge += fi >= fj ? 1 : 0;
+            }
+            if (gt < C && C <= ge) sm.thr[0] = fj;
+        }
+        if (tid == 0) sm.count = 0;
+        __syncthreads();
+        return sm.thr[0];
     }
-    const float M = block_max(lmax, sm.red);
-
-    // threshold: C-th largest lane max of this wave (bitonic sort, descending)
-    float s = lmax;
+    float sv = lmax;
 #pragma unroll
     for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const float o = __shfl_xor(s, j);
+            const float o = __shfl_xor(sv, j);
             const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-            s = keep_max ? fmaxf(s, o) : fminf(s, o);
+            sv = keep_max ? fmaxf(sv, o) : fminf(sv, o);
         }
     }
-    const float tw = __shfl(s, C - 1);
+    const float tw = __shfl(sv, C - 1);
     if (lane == 0) sm.thr[wv] = tw;
-    __syncthreads();
-    float thr = sm.thr[0];
-    for (int j = 1; j < (NT >> 6); ++j) thr = fmaxf(thr, sm.thr[j]);
-
-    // exact weight sum; elements >= thr are appended to the LDS candidate list
-    // (their order there is irrelevant: ranking is by (value, id)).  With
-    // thr == -inf (fewer than C lanes per wave hold data) the exact fallback runs.
     if (tid == 0) sm.count = 0;
     __syncthreads();
+    float thr = sm.thr[0];
+    for (int j = 1; j < nw; ++j) thr = fmaxf(thr, sm.thr[j]);
+    return thr;
+}
+
+// Ranks the candidate list (complete: called after a barrier) and writes the
+// row's top-C; returns false if the list overflowed (caller falls back).
+__device__ __forceinline__ bool rank_candidates(int C, int total, RowStatsSmem &sm, int32_t *out_id,
+                                                float *out_v)
+{
+    const int tid = threadIdx.x, NT = blockDim.x;
+    if (total > kCandCap) return false;
+    // rank of every candidate: comparisons split into segments of 16, one
+    // (segment, candidate) pair per thread; the lanes of a wave share a
+    // segment, so their LDS reads broadcast; partial counts meet in LDS atomics
+    for (int i = tid; i < total; i += NT) sm.rank[i] = 0;
+    __syncthreads();
+    const int nseg = (total + 15) / 16;
+    for (int t = tid; t < total * nseg; t += NT) {
+        const int g = t / total, i = t % total;
+        const float vi = sm.cand_v[i];
+        const int ii = sm.cand_i[i];
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int j = 16 * g + q;
+            cnt += (j < total && before(sm.cand_v[j], sm.cand_i[j], vi, ii)) ? 1 : 0;
+        }
+        if (cnt) atomicAdd(&sm.rank[i], cnt);
+    }
+    __syncthreads();
+    for (int i = tid; i < total; i += NT)
+        if (sm.rank[i] < C) sm.sel[sm.rank[i]] = i;
+    __syncthreads();
+    if (tid < C) {
+        const int i = sm.sel[tid];   // total >= C: T leaves at least C candidates
+        out_id[tid] = sm.cand_i[i];
+        out_v[tid] = sm.cand_v[i];
+    }
+    return true;
+}
+
+// Rows held in registers: vector j of a thread holds elements
+// [(j * NT + tid) * VEC, + VEC).
+template <typename T, int kNV>
+__global__ __launch_bounds__(1024) void k_row_stats(RowStatsArgs a)
+{
+    constexpr int VEC = Vec<T>::n;
+    __shared__ RowStatsSmem sm;
+    const int r_all = blockIdx.x;
+    const int b = r_all / a.r_max, r = r_all % a.r_max;
+    const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
+    const int rows_needed = kind == EAGLE_TREE_CHAIN ? a.chain_k : a.rows_dyn;
+    if (r >= rows_needed) return;
+    const int C = kind == EAGLE_TREE_CHAIN ? 1 : a.children;
+    const int V = a.vocab, NT = blockDim.x, tid = threadIdx.x;
+    const T *row = static_cast<const T *>(a.logits) + (size_t)r_all * (size_t)a.row_stride;
+
+    uint4 x[kNV];
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) x[j] = load_vec<T>(row, (j * NT + tid) * VEC, V, a.vec_ok);
+
+    float lmax = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) {
+        float f[VEC];
+        unpack<T>(x[j], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
+    }
+    if (tid == 0) sm.thr[0] = -__builtin_inff();   // stays -inf (exact fallback) if no maximum qualifies
+    const float M = block_max(lmax, sm.red);       // wave maxima stay in sm.red.f
+    const float thr = row_threshold(lmax, C, sm);
+
     const bool use_list = thr != -__builtin_inff();
     double wsum = 0.0;
 #pragma unroll
@@ -151,49 +203,113 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             wsum += (double)weight_of(f[e], M);
-            if (f[e] >= thr) {
+            if (f[e] >= thr && base + e < V) {
                 const int o = atomicAdd(&sm.count, 1);
                 if (o < kCandCap) { sm.cand_v[o] = f[e]; sm.cand_i[o] = base + e; }
             }
         }
-        if constexpr (kNV > 16) __builtin_amdgcn_sched_barrier(0);
     }
     const double W = block_sum_d(wsum, sm.red);   // contains barriers: the list is complete
-    const int total = sm.count;
-
-    if (tid < kMaxChildren) sm.sel[tid] = 0;
-    if (use_list && total <= kCandCap) {
-        // rank of every candidate: comparisons split into segments of 16, one
-        // (segment, candidate) pair per thread; the lanes of a wave share a
-        // segment, so their LDS reads broadcast; partial counts meet in LDS atomics
-        for (int i = tid; i < total; i += NT) sm.rank[i] = 0;
-        __syncthreads();
-        const int nseg = (total + 15) / 16;
-        for (int t = tid; t < total * nseg; t += NT) {
-            const int g = t / total, i = t % total;
-            const float vi = sm.cand_v[i];
-            const int ii = sm.cand_i[i];
-            int cnt = 0;
+    int32_t *out_id = a.top_id + (size_t)r_all * a.children;
+    float *out_v = a.top_v + (size_t)r_all * a.children;
+    if (!(use_list && rank_candidates(C, sm.count, sm, out_id, out_v))) {
+        // heavy ties or T = -inf: C rounds of "best element after the previous
+        // pick" over the registers (rare; exact for any input)
+        float pv = __builtin_inff();
+        int pi = -1;
+        for (int c = 0; c < C; ++c) {
+            float bv = -__builtin_inff();
+            int bi = 0x7fffffff;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int j = 16 * g + q;
-                cnt += (j < total && before(sm.cand_v[j], sm.cand_i[j], vi, ii)) ? 1 : 0;
+            for (int j = 0; j < kNV; ++j) {
+                float f[VEC];
+                unpack<T>(x[j], f);
+                const int base = (j * NT + tid) * VEC;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int id = base + e;
+                    if (id < V && before(pv, pi, f[e], id) && before(f[e], id, bv, bi)) { bv = f[e]; bi = id; }
+                }
             }
-            if (cnt) atomicAdd(&sm.rank[i], cnt);
+            block_best(bv, bi, sm.red);
+            if (tid == 0) { out_id[c] = bi; out_v[c] = bv; }
+            pv = bv;
+            pi = bi;
         }
-        __syncthreads();
-        for (int i = tid; i < total; i += NT)
-            if (sm.rank[i] < C) sm.sel[sm.rank[i]] = i;
-        __syncthreads();
-        if (tid < C) {
-            const int i = sm.sel[tid];
-            const size_t o2 = ((size_t)b * a.r_max + r) * a.children + tid;
-            a.top_id[o2] = sm.cand_i[i];
-            a.conf[o2] = (double)weight_of(sm.cand_v[i], M) / W;
+    }
+    if (tid == 0) {
+        a.W[r_all] = W;
+        a.M[r_all] = M;
+    }
+}
+
+// Streaming form: a max pass, then a weight pass over the same lines.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_row_stats_stream(RowStatsArgs a)
+{
+    constexpr int VEC = Vec<T>::n;
+    __shared__ RowStatsSmem sm;
+    const int r_all = blockIdx.x;
+    const int b = r_all / a.r_max, r = r_all % a.r_max;
+    const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
+    const int rows_needed = kind == EAGLE_TREE_CHAIN ? a.chain_k : a.rows_dyn;
+    if (r >= rows_needed) return;
+    const int C = kind == EAGLE_TREE_CHAIN ? 1 : a.children;
+    const int V = a.vocab, NT = blockDim.x, tid = threadIdx.x;
+    const T *row = static_cast<const T *>(a.logits) + (size_t)r_all * (size_t)a.row_stride;
+    const int nvec = (V + VEC - 1) / VEC;
+
+    float lmax = -__builtin_inff();
+    for (int v0 = tid; v0 < nvec; v0 += 4 * NT) {
+        uint4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * NT;
+            x[u] = v < nvec ? load_vec<T>(row, v * VEC, V, a.vec_ok) : make_uint4(0u, 0u, 0u, 0u);   // (skipped below)
         }
-    } else {
-        // heavy ties or thr == -inf: C rounds of "best element after the
-        // previous pick", re-reading the row (rare; exact for any input)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (v0 + u * NT >= nvec) continue;
+            float f[VEC];
+            unpack<T>(x[u], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
+        }
+    }
+    if (tid == 0) sm.thr[0] = -__builtin_inff();
+    const float M = block_max(lmax, sm.red);   // wave maxima stay in sm.red.f
+    const float thr = row_threshold(lmax, C, sm);
+
+    const bool use_list = thr != -__builtin_inff();
+    double wsum = 0.0;
+    for (int v0 = tid; v0 < nvec; v0 += 4 * NT) {
+        uint4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * NT;
+            x[u] = v < nvec ? load_vec<T>(row, v * VEC, V, a.vec_ok) : make_uint4(0u, 0u, 0u, 0u);   // (skipped below)
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * NT;
+            if (v >= nvec) continue;
+            float f[VEC];
+            unpack<T>(x[u], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                wsum += (double)weight_of(f[e], M);
+                const int id = v * VEC + e;
+                if (f[e] >= thr && id < V) {
+                    const int o = atomicAdd(&sm.count, 1);
+                    if (o < kCandCap) { sm.cand_v[o] = f[e]; sm.cand_i[o] = id; }
+                }
+            }
+        }
+    }
+    const double W = block_sum_d(wsum, sm.red);
+    int32_t *out_id = a.top_id + (size_t)r_all * a.children;
+    float *out_v = a.top_v + (size_t)r_all * a.children;
+    if (!(use_list && rank_candidates(C, sm.count, sm, out_id, out_v))) {
         float pv = __builtin_inff();
         int pi = -1;
         for (int c = 0; c < C; ++c) {
@@ -204,20 +320,14 @@ __global__ __launch_bounds__(RowMaxThreads<kNV>::n) void k_row_stats(RowStatsArg
                 if (before(pv, pi, f, id) && before(f, id, bv, bi)) { bv = f; bi = id; }
             }
             block_best(bv, bi, sm.red);
-            if (tid == 0) {
-                const size_t o2 = ((size_t)b * a.r_max + r) * a.children + c;
-                a.top_id[o2] = bi;
-                a.conf[o2] = (double)weight_of(bv, M) / W;
-            }
+            if (tid == 0) { out_id[c] = bi; out_v[c] = bv; }
             pv = bv;
             pi = bi;
         }
     }
     if (tid == 0) {
-        const size_t ro = (size_t)b * a.r_max + r;
-        a.M[ro] = M;
-        a.W[ro] = W;
-        if (!__builtin_isfinite(M) || !__builtin_isfinite(W)) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+        a.W[r_all] = W;
+        a.M[r_all] = M;
     }
 }
 
@@ -269,8 +379,14 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         if (tid == 0) {
             double Vp = 1.0;
             for (int i = 0; i < K; ++i) {
-                Vp = Vp * a.conf[(rb + i) * Cw];
-                tokens[i] = a.top_id[(rb + i) * Cw];
+                // the row's argmax and its confidence
+                const float bv = a.top_v[(rb + i) * Cw];
+                const int bi = a.top_id[(rb + i) * Cw];
+                const double W = a.W[rb + i];
+                const float M = a.M[rb + i];
+                if (!__builtin_isfinite(M) || !__builtin_isfinite(W)) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+                Vp = Vp * ((double)weight_of(bv, M) / W);
+                tokens[i] = bi;
                 parent[i] = i - 1;
                 depth[i] = i + 1;
                 score[i] = Vp;
@@ -286,10 +402,15 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
 
     const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
     const int R = 1 + (D - 1) * k;
+    // the rows' children in rank order, c = W35(l - M) / W
     for (int i = tid; i < R * C; i += NT) {
         const int r = i / C, j = i - r * C;
-        sm.conf[i] = a.conf[(rb + r) * Cw + j];
-        sm.cid[i] = a.top_id[(rb + r) * Cw + j];
+        const size_t o = (rb + r) * Cw + j;
+        const float M = a.M[rb + r];
+        const double W = a.W[rb + r];
+        sm.cid[i] = a.top_id[o];
+        sm.conf[i] = (double)weight_of(a.top_v[o], M) / W;
+        if (j == 0 && (!__builtin_isfinite(M) || !__builtin_isfinite(W))) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
     }
     for (int i = tid; i < kMaxCand; i += NT) {
         sm.rank_d[i] = 0;
@@ -447,30 +568,31 @@ BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
     L.off_M = o;      o = align_up(o + rows * sizeof(float), 256);
     L.off_W = o;      o = align_up(o + rows * sizeof(double), 256);
     L.off_id = o;     o = align_up(o + rows * p->children * sizeof(int32_t), 256);
-    L.off_c = o;      o = align_up(o + rows * p->children * sizeof(double), 256);
+    L.off_v = o;      o = align_up(o + rows * p->children * sizeof(float), 256);
     L.total = o;
     return L;
 }
 
-// vectors per thread (4, 8, 16 or 32) and threads per row so that one row
-// fits the registers of one workgroup; 0 if it does not fit
+// Register path: vectors per thread (1, 2, 4 or 8) for a row of `vocab`
+// elements read by up to 1024 threads; 0: the row needs the streaming kernel.
+constexpr int kRegisterRowsMax = 256;
+
 int row_vectors(int vocab, int vec)
 {
-    if (vocab <= 1024 * 4 * vec) return 4;
-    if (vocab <= 1024 * 8 * vec) return 8;
-    if (vocab <= 512 * 16 * vec) return 16;
-    if (vocab <= 512 * 32 * vec) return 32;
+    const long long per = 1024LL * vec;
+    for (int nv = 1; nv <= 8; nv *= 2)
+        if (vocab <= per * nv) return nv;
     return 0;
 }
 
+// threads of the register path: enough for the row, a multiple of 64
 int row_threads(int vocab, int vec)
 {
     const int nv = row_vectors(vocab, vec);
-    const int per = (nv ? nv : 32) * vec;
-    int nt = (vocab + per - 1) / per;
+    const long long per = (long long)(nv ? nv : 8) * vec;
+    long long nt = (vocab + per - 1) / per;
     nt = (nt + 63) / 64 * 64;
-    if (nt < 64) nt = 64;
-    return nt;
+    return (int)(nt < 64 ? 64 : (nt > 1024 ? 1024 : nt));
 }
 
 hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const void *logits,
@@ -483,6 +605,7 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     RowStatsArgs ra;
     ra.logits = logits;
     ra.row_stride = row_stride;
+    ra.rows = batch * p->r_max;
     ra.r_max = p->r_max;
     ra.vocab = p->vocab;
     ra.children = p->children;
@@ -492,28 +615,37 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ra.M = reinterpret_cast<float *>(base + L.off_M);
     ra.W = reinterpret_cast<double *>(base + L.off_W);
     ra.top_id = reinterpret_cast<int32_t *>(base + L.off_id);
-    ra.conf = reinterpret_cast<double *>(base + L.off_c);
+    ra.top_v = reinterpret_cast<float *>(base + L.off_v);
     ra.err = reinterpret_cast<uint32_t *>(base);
     const size_t esz = dt == EAGLE_F32 ? 4 : 2;
     ra.vec_ok = ((uintptr_t)logits % 16 == 0) && ((size_t)row_stride * esz % 16 == 0);
-    const dim3 g1((unsigned)(batch * p->r_max));
-    if (batch > 0 && p->r_max > 0) {
-        const int vec = dt == EAGLE_F32 ? 4 : 8;
-        const dim3 blk(row_threads(p->vocab, vec));
-        const int nv = row_vectors(p->vocab, vec);
-#define EAGLE_ROWS(T, NV) hipLaunchKernelGGL((k_row_stats<T, NV>), g1, blk, 0, st, ra)
-        if (dt == EAGLE_F32) {
-            if (nv == 4) EAGLE_ROWS(float, 4);
-            else if (nv == 8) EAGLE_ROWS(float, 8);
-            else if (nv == 16) EAGLE_ROWS(float, 16);
-            else EAGLE_ROWS(float, 32);
+    const int vec = dt == EAGLE_F32 ? 4 : 8;
+    const int nv = row_vectors(p->vocab, vec);
+    const int nt = row_threads(p->vocab, vec);
+    if (ra.rows > 0) {
+        // registers for few rows (each row's latency is the step's), streaming
+        // for many rows (workgroups overlap) and for rows too long for registers
+        if (nv == 0 || ra.rows > kRegisterRowsMax) {
+#define EAGLE_STREAM(T) hipLaunchKernelGGL((k_row_stats_stream<T>), dim3((unsigned)ra.rows), dim3(1024), 0, st, ra)
+            if (dt == EAGLE_F32) EAGLE_STREAM(float);
+            else EAGLE_STREAM(uint16_t);
+#undef EAGLE_STREAM
         } else {
-            if (nv == 4) EAGLE_ROWS(uint16_t, 4);
-            else if (nv == 8) EAGLE_ROWS(uint16_t, 8);
-            else if (nv == 16) EAGLE_ROWS(uint16_t, 16);
-            else EAGLE_ROWS(uint16_t, 32);
-        }
+            const dim3 g1((unsigned)ra.rows);
+#define EAGLE_ROWS(T, NV) hipLaunchKernelGGL((k_row_stats<T, NV>), g1, dim3(nt), 0, st, ra)
+            if (dt == EAGLE_F32) {
+                if (nv == 1) EAGLE_ROWS(float, 1);
+                else if (nv == 2) EAGLE_ROWS(float, 2);
+                else if (nv == 4) EAGLE_ROWS(float, 4);
+                else EAGLE_ROWS(float, 8);
+            } else {
+                if (nv == 1) EAGLE_ROWS(uint16_t, 1);
+                else if (nv == 2) EAGLE_ROWS(uint16_t, 2);
+                else if (nv == 4) EAGLE_ROWS(uint16_t, 4);
+                else EAGLE_ROWS(uint16_t, 8);
+            }
 #undef EAGLE_ROWS
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -527,7 +659,9 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ta.m_max = p->m_max;
     ta.r_max = p->r_max;
     ta.top_id = ra.top_id;
-    ta.conf = ra.conf;
+    ta.top_v = ra.top_v;
+    ta.M = ra.M;
+    ta.W = ra.W;
     ta.tokens = tokens;
     ta.parent = parent;
     ta.depth = depth;

@@ -123,8 +123,6 @@ eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const v
     if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes)
         return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
     if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
-    if (row_vectors(p->vocab, dtype == EAGLE_F32 ? 4 : 8) == 0)
-        return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d too large for dtype %d rows", p->vocab, (int)dtype);
     s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
     if (s != EAGLE_OK) return s;
     if (batch == 0) return ok();

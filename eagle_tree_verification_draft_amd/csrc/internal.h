@@ -19,12 +19,12 @@ constexpr int kMaxRows = 128;    // draft rows one dynamic tree uses: 1 + (D-1)k
 struct RowStatsArgs {
     const void *logits;
     int64_t row_stride;
-    int r_max, vocab, children, chain_k, rows_dyn;
+    int rows, r_max, vocab, children, chain_k, rows_dyn;
     const int32_t *kind;
-    float *M;
-    double *W;
-    int32_t *top_id;
-    double *conf;      // c = w / W of every (row, child)
+    float *M;          // row max
+    double *W;         // exact row weight sum
+    int32_t *top_id;   // top-C ids of each row, rank order
+    float *top_v;      // and their logits
     uint32_t *err;
     bool vec_ok;
 };
@@ -32,8 +32,10 @@ struct RowStatsArgs {
 struct TreeSelectArgs {
     const int32_t *kind;
     int depth_max, topk, children, m, chain_k, m_max, r_max;
+    const float *M;
+    const double *W;
     const int32_t *top_id;
-    const double *conf;
+    const float *top_v;
     int32_t *tokens, *parent, *depth;
     double *score;
     int32_t *src_row, *num_nodes;
@@ -41,7 +43,7 @@ struct TreeSelectArgs {
 };
 
 struct BuildLayout {
-    size_t off_M, off_W, off_id, off_c, total;
+    size_t off_M, off_W, off_id, off_v, total;
 };
 BuildLayout build_layout(const eagle_tree_params *p, int32_t batch);
 int row_vectors(int vocab, int vec);

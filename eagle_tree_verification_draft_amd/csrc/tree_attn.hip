@@ -111,9 +111,12 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Work items of one workgroup, in processing order: the draft tile (last key
-// split only, when the sequence has nodes), then the prefix tiles of the
-// split.  Every item reaches LDS by direct global->LDS loads, kAhead items
+// Work items of one workgroup, in processing order: the prefix tiles of the
+// split, then the draft tile (last key split only, when the sequence has
+// nodes).  With a contiguous cache the first prefix tiles are requested
+// before prefix_len is read (every key below the capacity is addressable);
+// requests that turn out to lie past it are drained, never used.  Every item
+// reaches LDS by direct global->LDS loads, kAhead items
 // ahead of the one being computed, so every wave issues the same number of
 // loads per item and a partial wait (vmcnt) separates the items in flight:
 //   - prefix tile: K rows and V^T chunks; keys at or past prefix_len read the
@@ -122,14 +125,21 @@ __device__ __forceinline__ void wait_vmcnt()
 //     that straddles prefix_len may carry anything past it;
 //   - draft tile: K rows of the draft tokens, and their V rows key-major into
 //     sm.dv, transposed to V^T in LDS (zeros for keys >= num_nodes) before use.
-template <int kNW>
+//
+// kKS = 2 (few query rows): the waves form kNW / 2 row waves x 2 key halves;
+// a wave computes its 32 rows against one 32-key half of every tile with its
+// own online-softmax state, and the two halves' states are combined through
+// LDS at the end, so every SIMD works on every tile.
+template <int kNW, int kKS>
 __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
 {
     constexpr int kPer = kTileChunks / 64 / kNW;   // 16-byte slots per wave per operand per tile
     constexpr int kLw = 2 * kPer;                  // loads per wave per item
+    constexpr int kRW = kNW / kKS;                 // row waves
     __shared__ AttnSmem sm;
     const int tid = threadIdx.x, NT = kNW * 64, lane = tid & 63, wv = tid >> 6;
     const int ln = lane & 31, hh = lane >> 5;
+    const int rw = wv % kRW, kh = wv / kRW;        // row wave, key half (kKS = 2)
     // block -> (split, row group, sequence/kv head); all splits and row groups
     // of one (sequence, kv head) share blockIdx mod 8 when units0 % 8 == 0,
     // which keeps them on one XCD and its L2
@@ -140,35 +150,13 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     const int b = u0 / a.Hkv, kvh = u0 % a.Hkv;
     const int G = a.G, m_max = a.m_max;
 
-    int L = a.prefix_len[b];
-    if (L < 0 || L > a.cap) {
-        if (tid == 0 && s == 0 && rg == 0) raise_error(a.err, EAGLE_DEVERR_PREFIX);
-        L = L < 0 ? 0 : a.cap;
-    }
-    int n = a.num_nodes[b];
-    n = n < 0 ? 0 : (n > m_max ? m_max : n);
-    const int nsplit_b = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
-    if (s >= nsplit_b) return;
-    const int key_lo = s * a.chunk, key_hi = min(L, key_lo + a.chunk);
-    const bool last_split = (s == nsplit_b - 1);
     const bool paged = a.block_size != 0;
     const int bs = a.block_size;
-    const int page0 = paged ? key_lo / bs : 0;
-
-    // pages of this split -> LDS
-    if (paged && key_hi > key_lo) {
-        const int np = (key_hi - 1) / bs - page0 + 1;
-        for (int i = tid; i < np; i += NT) sm.bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
-    }
-
-    const int row0 = rg * a.rows_pg + wv * 32;          // first row of this wave
-    const int rows_valid = n * G;                        // rows with a real node
-    const bool wave_active = row0 < rows_valid && wv * 32 < a.rows_pg;
+    const int key_lo = s * a.chunk;
+    const int row0 = rg * a.rows_pg + rw * 32;          // first row of this wave
     const int my_row = row0 + ln;
     const int my_node = my_row / G;
-    const bool row_ok = my_row < rows_valid && wv * 32 + ln < a.rows_pg;
-
-    __syncthreads();   // sm.bt visible
+    const bool row_exists = rw * 32 + ln < a.rows_pg && my_node < m_max;
 
     const uint16_t *kc = static_cast<const uint16_t *>(a.kc);
     const uint16_t *vc = static_cast<const uint16_t *>(a.vc);
@@ -178,9 +166,14 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     const uint16_t *kslab = paged ? kc : kc + kvbase * (size_t)a.cap * kHD;
     const uint16_t *vslab = paged ? vc : vc + kvbase * (size_t)kHD * a.cap;
 
-    const int ndraft = (last_split && n > 0) ? 1 : 0;
-    const int nprefix = (key_hi - key_lo + kTK - 1) / kTK;
-    const int nitems = ndraft + nprefix;
+    // Items of the split: its prefix tiles, then (last split, nodes present)
+    // the draft tile.  Until the prefix length is known, key_hi and nprefix
+    // describe the keys below the cache capacity, which are all addressable
+    // in a contiguous cache: its first tiles are requested before the length
+    // arrives (a paged cache needs the block table first).
+    int key_hi = paged ? key_lo : min(a.cap, key_lo + a.chunk);
+    int nprefix = key_hi > key_lo ? (key_hi - key_lo + kTK - 1) / kTK : 0;
+    int n = 0, page0 = 0;
 
     auto k_src = [&](int key, int J) -> const uint16_t * {
         if (!paged) return kslab + (size_t)key * kHD + J * 8;
@@ -201,7 +194,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     const size_t kvh_off = (size_t)kvh * bs * kHD;
     auto issue = [&](int item) {
         AttnBuf &B = sm.buf[item % kNBuf];
-        if (item < ndraft) {
+        if (item >= nprefix) {
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
                 const int it = wv * kPer + q, slot = it * 64 + lane;
@@ -210,9 +203,9 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
                 load_lds16(kd + ((drow + (t < n ? t : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &B.K[it * 64]);
                 load_lds16(vd + ((drow + (r < n ? r : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &sm.dv[it * 64]);
             }
-        } else if (key_lo + (item - ndraft + 1) * kTK <= key_hi && fast_pages) {
+        } else if (key_lo + (item + 1) * kTK <= key_hi && fast_pages) {
             // full tile: lane offsets from shifts and masks only
-            const int k0 = key_lo + (item - ndraft) * kTK;
+            const int k0 = key_lo + item * kTK;
             if (!paged) {
                 const uint16_t *kt = kslab + (size_t)k0 * kHD, *vt = vslab + k0;
 #pragma unroll
@@ -242,7 +235,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
                 }
             }
         } else {
-            const int k0 = key_lo + (item - ndraft) * kTK, klast = key_hi - 1;
+            const int k0 = key_lo + item * kTK, klast = key_hi - 1;
             const int vlast = k0 + ((klast - k0) & ~7);   // first key of the chunk holding klast
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
@@ -257,6 +250,64 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
         }
     };
 
+    const int nspec = paged ? 0 : min(kAhead, nprefix);
+    for (int i = 0; i < nspec; ++i) issue(i);
+    // Q fragments (B operand of S^T = K Q^T): lane holds q[my_row][16ks + 8hh .. +7]
+    // (rows below m_max are addressable whatever num_nodes says; rows without
+    // a node are zeroed below), the ancestor bits, and the sequence's lengths
+    bf16x8 qf[8];
+    {
+        const u32x4a *qrow = reinterpret_cast<const u32x4a *>(
+            static_cast<const uint16_t *>(a.q) +
+            (((size_t)b * m_max + (my_node < m_max ? my_node : 0)) * a.Hq + kvh * G + (my_row % G)) * kHD);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4a v = {0, 0, 0, 0};
+            if (row_exists) v = qrow[2 * ks + hh];
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+    uint64_t my_anc = row_exists ? a.anc[(size_t)b * m_max + my_node] : 0;
+    int L = a.prefix_len[b];
+    n = a.num_nodes[b];
+    if (L < 0 || L > a.cap) {
+        if (tid == 0 && s == 0 && rg == 0) raise_error(a.err, EAGLE_DEVERR_PREFIX);
+        L = L < 0 ? 0 : a.cap;
+    }
+    n = n < 0 ? 0 : (n > m_max ? m_max : n);
+    const int nsplit_b = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+    if (s >= nsplit_b) {
+        wait_vmcnt<0>();   // no LDS write may land after the workgroup has left
+        return;
+    }
+    key_hi = min(L, key_lo + a.chunk);
+    nprefix = key_hi > key_lo ? (key_hi - key_lo + kTK - 1) / kTK : 0;
+    const bool last_split = (s == nsplit_b - 1);
+    const int ndraft = (last_split && n > 0) ? 1 : 0;
+    const int nitems = nprefix + ndraft;
+    // requested tiles past the prefix are not items: drain them before their
+    // buffers are reused
+    if (nspec > nprefix) wait_vmcnt<0>();
+
+    if (paged) {
+        // pages of this split -> LDS
+        page0 = key_lo / bs;
+        if (key_hi > key_lo) {
+            const int np = (key_hi - 1) / bs - page0 + 1;
+            for (int i = tid; i < np; i += NT) sm.bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
+        }
+        __syncthreads();   // sm.bt visible
+    }
+
+    const int rows_valid = n * G;                        // rows with a real node
+    const bool wave_active = row0 < rows_valid && rw * 32 < a.rows_pg;
+    const bool row_ok = my_row < rows_valid && rw * 32 + ln < a.rows_pg;
+    if (!row_ok) {
+        my_anc = 0;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(u32x4a{0, 0, 0, 0});
+    }
+
     f32x16 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -267,26 +318,11 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     const float c2 = a.scale_log2;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
-    // The first items' loads go out first; the Q fragments and the ancestor
-    // bits follow, and one full wait covers them all (the compiler cannot
-    // count loads across the data-dependent issue loops, so a later wait for
-    // the Q registers would be a full wait inside the pipeline).
-    for (int i = 0; i < kAhead && i < nitems; ++i) issue(i);
-    // Q fragments (B operand of S^T = K Q^T): lane holds q[my_row][16ks + 8hh .. +7]
-    bf16x8 qf[8];
-    {
-        const u32x4a *qrow = reinterpret_cast<const u32x4a *>(
-            static_cast<const uint16_t *>(a.q) +
-            (((size_t)b * m_max + (my_node < m_max ? my_node : 0)) * a.Hq + kvh * G + (my_row % G)) * kHD);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            u32x4a v = {0, 0, 0, 0};
-            if (row_ok) v = qrow[2 * ks + hh];
-            qf[ks] = as_bf16x8(v);
-        }
-    }
-    uint64_t my_anc = 0;
-    if (row_ok) my_anc = a.anc[(size_t)b * m_max + my_node];
+    // the remaining first items; one full wait then covers them, the Q
+    // fragments and the ancestor bits (the compiler cannot count loads across
+    // the data-dependent issue loops, so a later wait for the Q registers
+    // would be a full wait inside the pipeline)
+    for (int i = nspec; i < kAhead && i < nitems; ++i) issue(i);
     wait_vmcnt<0>();
     for (int item = 0; item < nitems; ++item) {
         // this wave's loads of `item` have landed once at most the loads of
@@ -297,8 +333,8 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
         else wait_vmcnt<0>();
         __syncthreads();                      // ... and every wave's; item - 1 is fully consumed
         AttnBuf &B = sm.buf[item % kNBuf];
-        const bool draft = item < ndraft;
-        const int k0 = key_lo + (item - ndraft) * kTK;
+        const bool draft = item >= nprefix;
+        const int k0 = key_lo + item * kTK;
         if (draft) {
             // draft V rows (key-major) -> V^T, zeros for keys >= n; thread =
             // (8 dims, 8 keys): an 8x8 block of bf16 transposed in registers
@@ -350,59 +386,69 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
             // whose registers hold only half), so the products issue back to
             // back behind one LDS round trip per group
             constexpr int kGroup = kNW == 8 ? 4 : 8;
-            f32x16 s0, s1;
+            // key halves this wave covers: sh = 0, 1 (kKS = 1) or sh = kh
+            constexpr int kNH = 2 / kKS;
+            const int sh0 = kKS == 2 ? kh : 0;
+            f32x16 sacc[kNH];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+            for (int u = 0; u < kNH; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[u][r] = 0.0f;
 #pragma unroll
             for (int g0 = 0; g0 < 8; g0 += kGroup) {
-                u32x4a ka[kGroup], kb[kGroup];
+                u32x4a ka[kNH][kGroup];
 #pragma unroll
-                for (int j = 0; j < kGroup; ++j) {
-                    ka[j] = B.K[kpos(ln, 2 * (g0 + j) + hh)];
-                    kb[j] = B.K[kpos(32 + ln, 2 * (g0 + j) + hh)];
-                }
+                for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+                    for (int u = 0; u < kNH; ++u) ka[u][j] = B.K[kpos(32 * (sh0 + u) + ln, 2 * (g0 + j) + hh)];
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < kGroup; ++j) {
-                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[j]), qf[g0 + j], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[g0 + j], s1, 0, 0, 0);
-                }
+                for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+                    for (int u = 0; u < kNH; ++u)
+                        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[u][j]), qf[g0 + j], sacc[u], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the V^T operands of this tile, in flight during the softmax (with
             // 8 waves, two per SIMD, the registers hold them only after it)
-            constexpr int kEarly = kNW == 8 ? 0 : 16;
-            u32x4a va[16];
+            constexpr int kNV = 8 * kNH;                  // V^T operands per tile
+            constexpr int kEarly = kNW == 8 ? 0 : kNV;
+            u32x4a va[kNV];
 #pragma unroll
             for (int j = 0; j < kEarly; ++j) {
-                const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
                 va[j] = B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
             }
             __builtin_amdgcn_sched_barrier(0);
-            // s0/s1[8t + q] is the raw score of tile key 32sh + 16t + 8hh + q for
-            // row my_row.  Rows without a node have zero Q (finite scores, never
+            // sacc[u][8t + q] is the raw score of tile key 32(sh0 + u) + 16t + 8hh + q
+            // for row my_row.  Rows without a node have zero Q (finite scores, never
             // written out), so only keys need masking: past prefix_len in the
             // tail tile, and non-ancestors in the draft tile.
             if (draft) {
-                const uint32_t m0 = (uint32_t)my_anc >> (8 * hh), m1 = (uint32_t)(my_anc >> 32) >> (8 * hh);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int bit = 16 * (r >> 3) + (r & 7);
-                    s0[r] = ((m0 >> bit) & 1u) ? s0[r] : -__builtin_inff();
-                    s1[r] = ((m1 >> bit) & 1u) ? s1[r] : -__builtin_inff();
+                for (int u = 0; u < kNH; ++u) {
+                    const uint32_t mk = (uint32_t)(my_anc >> (32 * (sh0 + u))) >> (8 * hh);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int bit = 16 * (r >> 3) + (r & 7);
+                        sacc[u][r] = ((mk >> bit) & 1u) ? sacc[u][r] : -__builtin_inff();
+                    }
                 }
             } else if (k0 + kTK > key_hi) {
                 const int lim = key_hi - k0 - 8 * hh;    // tile keys below lim + 8hh are valid
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kq = 16 * (r >> 3) + (r & 7);
-                    s0[r] = kq < lim ? s0[r] : -__builtin_inff();
-                    s1[r] = 32 + kq < lim ? s1[r] : -__builtin_inff();
-                }
+                for (int u = 0; u < kNH; ++u)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kq = 32 * (sh0 + u) + 16 * (r >> 3) + (r & 7);
+                        sacc[u][r] = kq < lim ? sacc[u][r] : -__builtin_inff();
+                    }
             }
             float tmax = -__builtin_inff();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
+            for (int u = 0; u < kNH; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[u][r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             // Lazy rescaling: the exponent reference m_run moves (and O, l are
             // rescaled) only when some row's max grew by more than 2^8 in exp2
@@ -421,37 +467,37 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
             }
             const float mc = (m_run == -__builtin_inff() ? 0.0f : m_run) * c2;
             float lsum = 0.0f;
-            bf16x8 pf[2][2];
+            bf16x8 pf[kNH][2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, -mc));
-                lsum += p0 + p1;
-                pf[0][r >> 3][r & 7] = (__bf16)p0;
-                pf[1][r >> 3][r & 7] = (__bf16)p1;
-            }
+            for (int u = 0; u < kNH; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][r], c2, -mc));
+                    lsum += p;
+                    pf[u][r >> 3][r & 7] = (__bf16)p;
+                }
             lsum += __shfl_xor(lsum, 32);
             l_run += lsum;
             // ---- O^T += V^T P^T: four independent accumulators per k-step ----
-            if constexpr (kEarly == 16) {
+            if constexpr (kEarly == kNV) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[sh][t], oacc[dt], 0, 0, 0);
+                for (int j = 0; j < kNV; ++j) {
+                    const int u = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[u][t], oacc[dt], 0, 0, 0);
                 }
             } else {
 #pragma unroll
-                for (int g0 = 0; g0 < 16; g0 += 8) {
+                for (int g0 = 0; g0 < kNV; g0 += 8) {
 #pragma unroll
                     for (int j = g0; j < g0 + 8; ++j) {
-                        const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                        const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
                         va[j] = B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int j = g0; j < g0 + 8; ++j) {
-                        const int sh = j >> 3, t = (j >> 2) & 1, dt = j & 3;
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[sh][t], oacc[dt], 0, 0, 0);
+                        const int u = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[u][t], oacc[dt], 0, 0, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -459,10 +505,38 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
         }
     }
 
+    if constexpr (kKS == 2) {
+        // combine the key halves: the second half's state goes through LDS
+        // (the tile ring is free once every wave has left the loop)
+        __syncthreads();
+        float *xo = reinterpret_cast<float *>(sm.buf) + (size_t)rw * 64 * 64;   // [64 regs][64 lanes]
+        float2 *xml = reinterpret_cast<float2 *>(sm.dv) + rw * 64;
+        if (kh == 1 && wave_active) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xo[(16 * dt + r) * 64 + lane] = oacc[dt][r];
+            xml[lane] = make_float2(m_run, l_run);
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        if (wave_active) {
+            const float2 o = xml[lane];
+            const float mn = fmaxf(m_run, o.x);
+            const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+            const float e0 = __builtin_amdgcn_exp2f((m_run - mu) * c2), e1 = __builtin_amdgcn_exp2f((o.x - mu) * c2);
+            l_run = l_run * e0 + o.y * e1;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * e0 + xo[(16 * dt + r) * 64 + lane] * e1;
+            m_run = mn;
+        }
+    }
+
     // ---- epilogue ----
     // oacc[dt][r] is O^T[d = 32dt + 8(r>>2) + 4hh + (r&3)][my_row]
     const int h_out = kvh * G + (my_row % G);
-    const bool row_exists = wv * 32 + ln < a.rows_pg && my_node < m_max;
     uint16_t *out = static_cast<uint16_t *>(a.out);
     if (nsplit_b == 1) {
         if (row_exists) {
@@ -485,7 +559,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     if (row_ok) {
         const int unit = u0 * a.RG + rg;
         const size_t pbase = ((size_t)unit * a.nsplit + s) * a.rows_pg;
-        const int row_local = wv * 32 + ln;
+        const int row_local = rw * 32 + ln;
         float *po = a.part_o + (pbase + row_local) * kHD;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -530,19 +604,19 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a)
     if (node < n) {
         const size_t base = (size_t)unit * a.nsplit * a.rows_pg + rl;
         float M = -__builtin_inff(), den = 0.0f;
-        // batches of 4 splits: all loads of a batch are issued before use
-        for (int s0 = 0; s0 < nsplit_b; s0 += 4) {
-            float2 ml[4];
-            float4 o0[4], o1[4];
+        // batches of 8 splits: all loads of a batch are issued before use
+        for (int s0 = 0; s0 < nsplit_b; s0 += 8) {
+            float2 ml[8];
+            float4 o0[8], o1[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 8; ++q) {
                 const size_t pr = base + (size_t)min(s0 + q, nsplit_b - 1) * a.rows_pg;
                 ml[q] = a.part_ml[pr];
                 o0[q] = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8);
                 o1[q] = *reinterpret_cast<const float4 *>(a.part_o + pr * kHD + d8 + 4);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 8; ++q) {
                 if (s0 + q >= nsplit_b) break;
                 // online merge in log2 units
                 const float Mn = fmaxf(M, ml[q].x);
@@ -736,10 +810,12 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
         hipLaunchKernelGGL(k_tree_attn_f32, g, dim3(64), 0, st, a);
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
-        if (P.waves == 4)
-            hipLaunchKernelGGL(k_tree_attn_bf16<4>, g, dim3(256), 0, st, a);
+        if (P.waves == 4 && a.rows_pg <= 64)
+            hipLaunchKernelGGL((k_tree_attn_bf16<4, 2>), g, dim3(256), 0, st, a);
+        else if (P.waves == 4)
+            hipLaunchKernelGGL((k_tree_attn_bf16<4, 1>), g, dim3(256), 0, st, a);
         else
-            hipLaunchKernelGGL(k_tree_attn_bf16<8>, g, dim3(512), 0, st, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<8, 1>), g, dim3(512), 0, st, a);
         if (P.nsplit > 1) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

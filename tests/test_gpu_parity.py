@@ -108,6 +108,16 @@ SMALL = {
     "f32-tiny-vocab": lambda: _small(1, vocab=37, children=16, depth=3, topk=4, m=40, prefix=40),
     # chain only, K = depth 64 is not allowed (m_max <= 64), use K = 64 nodes
     "bf16-chain64": lambda: _small(5, batch=2, kinds=[1, 1], chain_k=64, vocab=3000, prefix=(50, 200)),
+    # register-held rows (few rows) with heavy ties (sd 0.02), and at 8 vectors per thread
+    "bf16-v32000-ties": lambda: _small(2, vocab=32000, draft_sigma=0.02, prefix=100),
+    "f32-v32000": lambda: _small(1, vocab=32000, prefix=64),
+    # streaming rows (more rows than the register form takes), mixed trees and chains
+    "bf16-v16001-stream-mixed": lambda: _small(5, batch=6, vocab=16001, prefix=(50, 300), kinds=[0, 1, 1, 0, 0, 1]),
+    # rows too long for registers: streaming kernel (bf16 and fp32, ragged vocab)
+    "bf16-stream": lambda: _small(2, batch=2, vocab=70001, prefix=100),
+    "f32-stream": lambda: _small(1, vocab=40003, prefix=64),
+    # the largest vocabulary, heavy ties
+    "bf16-vmax-ties": lambda: _small(2, vocab=1 << 17, draft_sigma=0.05, prefix=64),
 }
 
 
