@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes as C
 import dataclasses
+import math
 import os
 from typing import Optional
 
@@ -109,6 +110,21 @@ def _ptr(t: Optional[torch.Tensor]):
     return C.c_void_p(t.data_ptr())
 
 
+def _rows(t: torch.Tensor):
+    """(pointer, row stride in elements) of a [..., V] logit tensor whose rows are
+    contiguous and evenly spaced, e.g. the [..., :V] slice of a wider buffer."""
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError("logit rows passed to libeagle must be contiguous")
+    lead = [d for d in range(t.dim() - 1) if t.shape[d] > 1]
+    rs = t.stride(lead[-1]) if lead else t.shape[-1]
+    if rs < t.shape[-1]:
+        raise ValueError("logit row stride is shorter than a row")
+    for d in lead:
+        if t.stride(d) != rs * math.prod(t.shape[d + 1:-1]):
+            raise ValueError("logit rows passed to libeagle must be evenly spaced")
+    return C.c_void_p(t.data_ptr()), rs
+
+
 def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -143,8 +159,9 @@ def build_tree_workspace_size(p: TreeParams, batch: int) -> int:
 
 def build_tree(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind: Optional[torch.Tensor],
                tokens, parent, depth, score, src_row, num_nodes, workspace: torch.Tensor, stream=None):
-    _check(lib().eagle_build_tree(C.byref(p), batch, _ptr(draft_logits), dtype_code(draft_logits.dtype),
-                                  draft_logits.shape[-1], _ptr(kind), _ptr(tokens), _ptr(parent), _ptr(depth),
+    rows, stride = _rows(draft_logits)
+    _check(lib().eagle_build_tree(C.byref(p), batch, rows, dtype_code(draft_logits.dtype),
+                                  stride, _ptr(kind), _ptr(tokens), _ptr(parent), _ptr(depth),
                                   _ptr(score), _ptr(src_row), _ptr(num_nodes), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_build_tree")
@@ -178,8 +195,9 @@ def accept_workspace_size(a: AcceptParams, batch: int) -> int:
 def accept(a: AcceptParams, batch: int, target_logits: torch.Tensor, tokens, parent, num_nodes,
            rand_words: Optional[torch.Tensor], accepted, accept_len, bonus_token, workspace: torch.Tensor,
            stream=None):
-    _check(lib().eagle_accept(C.byref(a), batch, _ptr(target_logits), dtype_code(target_logits.dtype),
-                              target_logits.shape[-1], _ptr(tokens), _ptr(parent), _ptr(num_nodes),
+    rows, stride = _rows(target_logits)
+    _check(lib().eagle_accept(C.byref(a), batch, rows, dtype_code(target_logits.dtype),
+                              stride, _ptr(tokens), _ptr(parent), _ptr(num_nodes),
                               _ptr(rand_words), _ptr(accepted), _ptr(accept_len), _ptr(bonus_token),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_accept")

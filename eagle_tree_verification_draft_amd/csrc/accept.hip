@@ -4,6 +4,7 @@
 // step reads one target row (the current node's) once from HBM into registers.
 #include "common.h"
 #include "internal.h"
+#include "rowvec.h"
 
 namespace eagle {
 
@@ -34,27 +35,6 @@ struct AcceptSmem {
     int bonus;
 };
 
-template <typename T> struct AVec;
-template <> struct AVec<float> { static constexpr int n = 4; };
-template <> struct AVec<uint16_t> { static constexpr int n = 8; };
-
-template <typename T> __device__ __forceinline__ float ld1(const T *p);
-template <> __device__ __forceinline__ float ld1<float>(const float *p) { return *p; }
-template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
-
-template <typename T>
-__device__ __forceinline__ void unpack_a(const uint4 &u, float *o);
-template <> __device__ __forceinline__ void unpack_a<float>(const uint4 &u, float *o)
-{
-    o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
-    o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
-}
-template <> __device__ __forceinline__ void unpack_a<uint16_t>(const uint4 &u, float *o)
-{
-    o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
-    o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
-}
-
 // exclusive scan of exact integer-valued doubles over the block
 __device__ __forceinline__ double block_exclusive_scan_d(double v, double *part)
 {
@@ -80,7 +60,7 @@ __device__ __forceinline__ double block_exclusive_scan_d(double v, double *part)
 template <typename T, typename F>
 __device__ __forceinline__ void for_each_elem(const T *row, int V, bool vec_ok, F &&fn)
 {
-    constexpr int VEC = AVec<T>::n;
+    constexpr int VEC = Vec<T>::n;
     const int NT = blockDim.x, tid = threadIdx.x;
     const int nvec = vec_ok ? V / VEC : 0;
     // batches of 4 independent 16-byte loads per thread
@@ -96,13 +76,13 @@ __device__ __forceinline__ void for_each_elem(const T *row, int V, bool vec_ok, 
             const int j = j0 + q * NT;
             if (j < nvec) {
                 float f[VEC];
-                unpack_a<T>(u[q], f);
+                unpack<T>(u[q], f);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) fn(f[e], j * VEC + e);
             }
         }
     }
-    for (int v = nvec * VEC + tid; v < V; v += NT) fn(ld1<T>(row + v), v);
+    for (int v = nvec * VEC + tid; v < V; v += NT) fn(load_scalar<T>(row + v), v);
 }
 
 template <typename T>
@@ -165,7 +145,7 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptArgs a)
                         raise_error(a.err, EAGLE_DEVERR_TREE);
                         sm.wchild[i] = 0.0;
                     } else {
-                        sm.wchild[i] = (double)weight_of_t(ld1<T>(row + t), M, a.temperature, a.unit_t);
+                        sm.wchild[i] = (double)weight_of_t(load_scalar<T>(row + t), M, a.temperature, a.unit_t);
                     }
                 }
             __syncthreads();
@@ -200,10 +180,10 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptArgs a)
                 const int E = (V + NT - 1) / NT;
                 const int lo = min(V, tid * E), hi = min(V, lo + E);
                 double mine = 0.0;
-                for (int v = lo; v < hi; ++v) mine += (double)weight_of_t(ld1<T>(row + v), M, a.temperature, a.unit_t);
+                for (int v = lo; v < hi; ++v) mine += (double)weight_of_t(load_scalar<T>(row + v), M, a.temperature, a.unit_t);
                 for (int j = 0; j < nrem; ++j) {
                     const int t = sm.removed[j];
-                    if (t >= lo && t < hi) mine -= (double)weight_of_t(ld1<T>(row + t), M, a.temperature, a.unit_t);
+                    if (t >= lo && t < hi) mine -= (double)weight_of_t(load_scalar<T>(row + t), M, a.temperature, a.unit_t);
                 }
                 const double before_me = block_exclusive_scan_d(mine, sm.part);
                 if (tid == 0) sm.bonus = -1;
@@ -215,7 +195,7 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptArgs a)
                         bool gone = false;
                         for (int j = 0; j < nrem; ++j) gone |= sm.removed[j] == v;
                         if (gone) continue;
-                        cum += (double)weight_of_t(ld1<T>(row + v), M, a.temperature, a.unit_t);
+                        cum += (double)weight_of_t(load_scalar<T>(row + v), M, a.temperature, a.unit_t);
                         if (cum > sd) { sm.bonus = v; break; }
                     }
                 }
@@ -232,6 +212,275 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptArgs a)
         ++len;
         cur = next;
         __syncthreads();
+    }
+    for (int j = len + tid; j < a.max_accept; j += NT) acc[j] = -1;
+    if (tid == 0) {
+        a.accept_len[b] = len;
+        a.bonus[b] = bonus;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident walk (the general form): one workgroup per sequence; at
+// each step the current node's target row is read once into registers --
+// thread t holds kNV 16-byte vectors, vector q covering elements
+// (q*NT + t)*VEC .. +VEC-1 -- and the maximum, the exact weight sum and the
+// bonus prefix search all run from there.  Every wave holds node i of the
+// sequence in lane i (m_max <= 64), so each wave finds the current node's
+// children with a ballot and runs the sequential child tests on wave-uniform
+// values itself; the only barriers are those of the row reductions.
+// ---------------------------------------------------------------------------
+constexpr int kRegMaxVectors = 16;
+
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+struct RegSmem {
+    BlockScratch red;
+    double part[kRegMaxVectors * 16];   // bonus search: residual weight of (vector q, wave w)
+    double before;                      // residual weight ahead of the chosen (q, w)
+    int qw;                             // chosen q * waves + w, or -1
+    int bonus;
+};
+
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int k)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, k);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), k);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// exclusive prefix sum over the lanes of one wave (exact integer-valued doubles)
+__device__ __forceinline__ double wave_exclusive_scan_d(double v)
+{
+    const int lane = threadIdx.x & 63;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    return incl - v;
+}
+
+// exclusive prefix sum over the lanes of one wave (64-bit integers)
+__device__ __forceinline__ unsigned long long wave_exclusive_scan_u64(unsigned long long v)
+{
+    const int lane = threadIdx.x & 63;
+    unsigned long long incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    return incl - v;
+}
+
+template <typename T, int kNV, bool kSample>
+__global__ __launch_bounds__(1024) void k_accept_reg(AcceptArgs a)
+{
+    __shared__ RegSmem sm;
+    constexpr int VEC = Vec<T>::n;
+    const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x;
+    const int lane = tid & 63, wv = tid >> 6, nw = NT >> 6;
+    const int m_max = a.m_max, V = a.vocab, nfull = V / VEC;   // rows aligned, V >= VEC (host)
+    const size_t m1 = (size_t)m_max + 1;
+    const float T_ = a.temperature;
+    const bool unit_t = a.unit_t;
+    int n = a.num_nodes[b];
+    if (n < 0 || n > m_max) {
+        if (tid == 0) raise_error(a.err, EAGLE_DEVERR_TREE);
+        n = n < 0 ? 0 : m_max;
+    }
+    // node `lane` of this sequence, in every wave; padding lanes never match a parent
+    const int tok = lane < n ? a.tokens[(size_t)b * m_max + lane] : -1;
+    const int par = lane < n ? a.parent[(size_t)b * m_max + lane] : -2;
+    const uint32_t word = (kSample && lane < n) ? a.words[(size_t)b * m1 + lane] : 0u;
+    const uint32_t word_bonus = kSample ? a.words[(size_t)b * m1 + m_max] : 0u;
+
+    int cur = -1, len = 0, bonus = -1;
+    int32_t *acc = a.accepted + (size_t)b * a.max_accept;
+    for (int step = 0; step <= kMaxMMax; ++step) {
+        const T *row = static_cast<const T *>(a.target) + ((size_t)b * m1 + (size_t)(cur + 1)) * (size_t)a.row_stride;
+        // the thread index passes through an opaque move each step, so the
+        // per-element indices and bounds tests derived from it are recomputed
+        // here rather than hoisted out of the walk and held in registers
+        int t_ = tid;
+        asm volatile("" : "+v"(t_));
+        uint4 x[kNV];
+#pragma unroll
+        for (int j = 0; j < kNV; ++j) x[j] = load_vec_clamped<T>(row, j * NT + t_, nfull);
+#pragma unroll
+        for (int j = 0; j < kNV; ++j) fix_tail<T>(x[j], row, j * NT + t_, nfull, V);
+        const unsigned long long sib = __ballot(par == cur);   // children of the current node
+        int next = -1;
+        if constexpr (!kSample) {
+            // this thread's elements ascend in id with position j*VEC + e, so a
+            // strict '>' keeps the first maximum; the id is formed once at the end
+            float bv = -__builtin_inff();
+            int bp = 0;
+            bool nan = false;
+#pragma unroll
+            for (int j = 0; j < kNV; ++j) {
+                float f[VEC];
+                unpack<T>(x[j], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    nan |= (f[e] != f[e]);
+                    if (f[e] > bv) { bv = f[e]; bp = j * VEC + e; }
+                }
+            }
+            if (__any(nan) && lane == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+            int bi = ((bp / VEC) * NT + t_) * VEC + bp % VEC;
+            block_best(bv, bi, sm.red);
+            const unsigned long long hit = __ballot(par == cur && tok == bi);
+            if (hit) next = __builtin_ctzll(hit);
+            else bonus = bi;
+        } else {
+            // the children's own logits, loaded with the row and weighed once M is known
+            const bool kid = (sib >> lane) & 1ull;
+            const bool kid_ok = kid && (unsigned)tok < (unsigned)V;
+            float lk = 0.0f;
+            if (kid_ok) lk = load_scalar<T>(row + tok);
+            float lmax = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < kNV; ++j) {
+                float f[VEC];
+                unpack<T>(x[j], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
+            }
+            const float M = block_max(lmax, sm.red);
+#pragma unroll
+            for (int j = 0; j < kNV; ++j) x[j] = opaque(x[j]);   // unpack again, not keep the floats
+            // exact weight sums per (vector j, wave), kept for the bonus search;
+            // W is their sum (integers below 2^53: exact in any order).  The
+            // temperature branch is taken once, outside the element loops.
+            auto parts = [&](auto unit) {
+#pragma unroll
+                for (int j = 0; j < kNV; ++j) {
+                    float f[VEC];
+                    unpack<T>(x[j], f);
+                    double sj = 0.0;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        sj += (double)(decltype(unit)::value ? weight_of(f[e], M) : weight_from_x((f[e] - M) / T_));
+                    sj = wave_sum_d(sj);
+                    if (lane == 0) sm.part[j * nw + wv] = sj;
+                }
+            };
+            if (unit_t) parts(Flag<true>{});
+            else parts(Flag<false>{});
+            __syncthreads();
+            const int P = kNV * nw;
+            double wl = 0.0;
+            for (int i = lane; i < P; i += 64) wl += sm.part[i];
+            const double W = wave_sum_d(wl);
+            if (!__builtin_isfinite(M) || !__builtin_isfinite(W)) {
+                if (tid == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+                break;
+            }
+#pragma unroll
+            for (int j = 0; j < kNV; ++j) x[j] = opaque(x[j]);
+            if (kid && !kid_ok && wv == 0) raise_error(a.err, EAGLE_DEVERR_TREE);   // malformed tree: no mass
+            // children in index order: child k is accepted iff r_k * R_k < w_k * 2^32,
+            // where R_k is W less the masses of the children before k (all rejected
+            // if k is the first to pass); a child repeating an earlier child's token
+            // carries no mass.  Every child is tested at once; the first pass wins.
+            bool gone = false;
+            for (unsigned long long left = sib; left; left &= left - 1) {
+                const int k = __builtin_ctzll(left);
+                gone |= lane > k && tok == __builtin_amdgcn_readlane(tok, k);
+            }
+            const unsigned long long wk =
+                (kid_ok && !gone) ? (unsigned long long)weight_of_t(lk, M, T_, unit_t) : 0ull;
+            const unsigned long long ahead = wave_exclusive_scan_u64(wk);
+            const unsigned long long Rk = (unsigned long long)W - ahead;
+            const bool pass = kid && (unsigned __int128)word * Rk < ((unsigned __int128)wk << 32);
+            const unsigned long long passed = __ballot(pass);
+            if (passed) next = __builtin_ctzll(passed);
+            if (next < 0) {
+                // bonus: every child was rejected; R = W less all their masses, and the
+                // bonus is the smallest v whose inclusive cumulative residual weight
+                // exceeds s = floor(r * R / 2^32).  In ascending v the elements run by
+                // vector q, then wave, then lane, then element.
+                const unsigned long long R = (unsigned long long)W - readlane_u64(ahead + wk, 63);
+                const unsigned long long s = (unsigned long long)(((unsigned __int128)word_bonus * R) >> 32);
+                const double sd = (double)s;
+                const unsigned long long removed = __ballot(kid_ok && !gone);
+                if (tid == 0) sm.bonus = -1;
+                if (wv == 0) {
+                    // lane l covers parts [l*c, l*c + c), c <= 4, with the removed
+                    // tokens' masses taken out of the parts that hold them
+                    const int c = (P + 63) / 64;
+                    const int lo = min(P, lane * c), hi = min(P, lo + c);
+                    double pv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) pv[u] = lo + u < hi ? sm.part[lo + u] : 0.0;
+                    for (unsigned long long left = removed; left; left &= left - 1) {
+                        const int k = __builtin_ctzll(left);
+                        const int v = __builtin_amdgcn_readlane(tok, k);
+                        const double wv_k = (double)readlane_u64(wk, k);
+                        const int gi = v / VEC, idx = (gi / NT) * nw + ((gi % NT) >> 6);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (idx == lo + u && lo + u < hi) pv[u] -= wv_k;
+                    }
+                    double mine = 0.0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) mine += pv[u];
+                    const double before = wave_exclusive_scan_d(mine);
+                    const bool here = before <= sd && sd < before + mine;
+                    if (__ballot(here) == 0ull && lane == 0) sm.qw = -1;
+                    if (here) {
+                        double cum = before;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            if (lo + u < hi && sd < cum + pv[u]) { sm.qw = lo + u; sm.before = cum; break; }
+                            cum += pv[u];
+                        }
+                    }
+                }
+                __syncthreads();
+                const int qw = sm.qw;
+                if (qw >= 0 && wv == qw % nw) {
+                    const int qs = qw / nw;
+                    float f[VEC];
+#pragma unroll
+                    for (int j = 0; j < kNV; ++j)
+                        if (j == qs) unpack<T>(x[j], f);
+                    // this lane's removed elements of vector qs
+                    unsigned gone_e = 0u;
+                    for (unsigned long long left = removed; left; left &= left - 1) {
+                        const int k = __builtin_ctzll(left);
+                        const int v = __builtin_amdgcn_readlane(tok, k);
+                        if (v / VEC == qs * NT + t_) gone_e |= 1u << (v % VEC);
+                    }
+                    double mine = 0.0;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (!((gone_e >> e) & 1u)) mine += (double)weight_of_t(f[e], M, T_, unit_t);
+                    const double before = sm.before + wave_exclusive_scan_d(mine);
+                    if (before <= sd && sd < before + mine) {
+                        double cum = before;
+                        for (int e = 0; e < VEC; ++e) {
+                            if ((gone_e >> e) & 1u) continue;
+                            cum += (double)weight_of_t(f[e], M, T_, unit_t);
+                            if (cum > sd) { sm.bonus = (qs * NT + t_) * VEC + e; break; }
+                        }
+                    }
+                }
+                __syncthreads();
+                bonus = sm.bonus;
+            }
+        }
+        if (next < 0) break;
+        if (len >= a.max_accept) {
+            if (tid == 0) raise_error(a.err, EAGLE_DEVERR_PATH);
+            break;
+        }
+        if (tid == 0) acc[len] = next;
+        ++len;
+        cur = next;
     }
     for (int j = len + tid; j < a.max_accept; j += NT) acc[j] = -1;
     if (tid == 0) {
@@ -342,9 +591,9 @@ hipError_t launch_accept(const eagle_accept_params *p, int32_t batch, const void
     a.bonus = bonus;
     a.err = err;
     const int vec = dt == EAGLE_F32 ? 4 : 8;
-    int nt = (p->vocab / vec + 63) / 64 * 64;
-    nt = nt < 64 ? 64 : (nt > kAcceptThreads ? kAcceptThreads : nt);
     if (p->mode == EAGLE_ACCEPT_GREEDY && (size_t)batch * (p->m_max + 1) <= (size_t)kParallelGreedyRows) {
+        int nt = (p->vocab / vec + 63) / 64 * 64;
+        nt = nt < 64 ? 64 : (nt > kAcceptThreads ? kAcceptThreads : nt);
         int32_t *g = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(err) + kWsHeader);
         const dim3 grid((unsigned)(batch * (p->m_max + 1)));
         if (dt == EAGLE_F32)
@@ -356,6 +605,39 @@ hipError_t launch_accept(const eagle_accept_params *p, int32_t batch, const void
         hipLaunchKernelGGL(k_greedy_walk, dim3(batch), dim3(64), 0, st, a, (const int32_t *)g);
         return hipGetLastError();
     }
+    // register-resident walk: kNV vectors per thread, the fewest threads that hold the row
+    const int nvec = (p->vocab + vec - 1) / vec;
+    int knv = 1;
+    while (knv < kRegMaxVectors && knv * kAcceptThreads < nvec) knv *= 2;
+    if (a.vec_ok && p->vocab >= vec && knv * kAcceptThreads >= nvec) {
+        int nt = ((nvec + knv - 1) / knv + 63) / 64 * 64;
+        nt = nt < 64 ? 64 : nt;
+        const dim3 grid((unsigned)batch), block((unsigned)nt);
+        const bool sample = p->mode != EAGLE_ACCEPT_GREEDY;
+#define EAGLE_ACCEPT_REG(KNV)                                                                    \
+    case KNV:                                                                                    \
+        if (dt == EAGLE_F32) {                                                                   \
+            if (sample) hipLaunchKernelGGL((k_accept_reg<float, KNV, true>), grid, block, 0, st, a); \
+            else hipLaunchKernelGGL((k_accept_reg<float, KNV, false>), grid, block, 0, st, a);   \
+        } else {                                                                                 \
+            if (sample) hipLaunchKernelGGL((k_accept_reg<uint16_t, KNV, true>), grid, block, 0, st, a); \
+            else hipLaunchKernelGGL((k_accept_reg<uint16_t, KNV, false>), grid, block, 0, st, a); \
+        }                                                                                        \
+        break;
+        switch (knv) {
+            EAGLE_ACCEPT_REG(1)
+            EAGLE_ACCEPT_REG(2)
+            EAGLE_ACCEPT_REG(4)
+            EAGLE_ACCEPT_REG(8)
+            EAGLE_ACCEPT_REG(16)
+        }
+#undef EAGLE_ACCEPT_REG
+        return hipGetLastError();
+    }
+    // unaligned rows, rows shorter than one vector, and rows longer than 16
+    // vectors per thread (fp32 beyond 65536 entries): looping walk
+    int nt = (p->vocab / vec + 63) / 64 * 64;
+    nt = nt < 64 ? 64 : (nt > kAcceptThreads ? kAcceptThreads : nt);
     if (dt == EAGLE_F32)
         hipLaunchKernelGGL(k_accept<float>, dim3(batch), dim3(nt), 0, st, a);
     else

@@ -35,7 +35,7 @@ constexpr int kRoundMagicBits = 0x4B400000;
 // Weight of an already-formed x (NaN in -> NaN out; no undefined conversions).
 __device__ __forceinline__ float weight_from_x(float x)
 {
-    x = (x < -32.0f) ? -32.0f : x;
+    x = __builtin_elementwise_maximum(x, -32.0f);   // clamp below at -32; NaN stays NaN
     const float y = x * kL2E;
     const float t = y + kRoundMagic;
     const float n = t - kRoundMagic;

@@ -135,3 +135,16 @@ def test_zero_batch_launches_nothing():
     out = C.c_void_p(1 << 24)
     assert L.eagle_build_tree(C.byref(p), 0, out, 1, 32000, None, out, out, out, out, out, out,
                               C.c_void_p(1 << 21), 1 << 20, None) == E.EAGLE_OK
+
+
+def test_logit_rows_marshalling():
+    """Rows inside a wider buffer pass their stride; anything else is refused."""
+    import torch
+    assert E._rows(torch.zeros(2, 3, 10))[1] == 10
+    assert E._rows(torch.zeros(2, 3, 16)[..., :10])[1] == 16
+    assert E._rows(torch.zeros(4, 1, 16)[..., :10])[1] == 16
+    assert E._rows(torch.zeros(1, 1, 10))[1] == 10
+    with pytest.raises(ValueError):
+        E._rows(torch.zeros(2, 3, 16)[:, :2, :10])      # rows not evenly spaced
+    with pytest.raises(ValueError):
+        E._rows(torch.zeros(3, 10).t())                 # elements not contiguous
