@@ -95,11 +95,15 @@ __device__ __forceinline__ int vpos(int e, int J) { return e * 8 + (J ^ ((e >> 1
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4a v) { return __builtin_bit_cast(bf16x8, v); }
 
 // 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
-// (dst must be the same for the whole wave)
+// (dst must be the same for the whole wave).  The loads carry the non-temporal
+// cache policy (bit 1 of the policy operand): K/V lines are streamed once, and
+// streaming reads marked so run measurably closer to the HBM peak.
+constexpr int kCachePolicyNT = 2;
+
 __device__ __forceinline__ void load_lds16(const void *src, void *dst_wave)
 {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)dst_wave, 16, 0, 0);
+                                     (__attribute__((address_space(3))) void *)dst_wave, 16, 0, kCachePolicyNT);
 }
 
 // s_waitcnt with vmcnt = n and the other counters left free (gfx9 encoding:
