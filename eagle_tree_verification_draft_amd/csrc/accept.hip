@@ -262,6 +262,33 @@ __device__ __forceinline__ double wave_exclusive_scan_d(double v)
     return incl - v;
 }
 
+// block maximum that propagates NaN (any NaN input makes the result NaN)
+__device__ __forceinline__ float block_maximum(float v, BlockScratch &s)
+{
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = __builtin_elementwise_maximum(v, __shfl_xor(v, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s.f[w] = v;
+    __syncthreads();
+    float r = s.f[0];
+    for (int j = 1; j < nw; ++j) r = __builtin_elementwise_maximum(r, s.f[j]);
+    return r;
+}
+
+__device__ __forceinline__ int block_min_i(int v, BlockScratch &s)
+{
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s.i[w] = v;
+    __syncthreads();
+    int r = s.i[0];
+    for (int j = 1; j < nw; ++j) r = min(r, s.i[j]);
+    return r;
+}
+
 // exclusive prefix sum over the lanes of one wave (64-bit integers)
 __device__ __forceinline__ unsigned long long wave_exclusive_scan_u64(unsigned long long v)
 {
@@ -314,24 +341,39 @@ __global__ __launch_bounds__(1024) void k_accept_reg(AcceptArgs a)
         const unsigned long long sib = __ballot(par == cur);   // children of the current node
         int next = -1;
         if constexpr (!kSample) {
-            // this thread's elements ascend in id with position j*VEC + e, so a
-            // strict '>' keeps the first maximum; the id is formed once at the end
-            float bv = -__builtin_inff();
-            int bp = 0;
-            bool nan = false;
+            // pass A: the row maximum, NaN-propagating (a NaN anywhere makes it NaN)
+            float mt = -__builtin_inff();
 #pragma unroll
             for (int j = 0; j < kNV; ++j) {
                 float f[VEC];
                 unpack<T>(x[j], f);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    nan |= (f[e] != f[e]);
-                    if (f[e] > bv) { bv = f[e]; bp = j * VEC + e; }
-                }
+                for (int e = 0; e < VEC; ++e) mt = __builtin_elementwise_maximum(mt, f[e]);
             }
-            if (__any(nan) && lane == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
-            int bi = ((bp / VEC) * NT + t_) * VEC + bp % VEC;
-            block_best(bv, bi, sm.red);
+            const float M = block_maximum(mt, sm.red);
+#pragma unroll
+            for (int j = 0; j < kNV; ++j) x[j] = opaque(x[j]);   // unpack again, not keep the floats
+            if (M != M) {
+                if (tid == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+                break;
+            }
+            // pass B, only in threads that hold the maximum (usually one wave):
+            // their first element equal to it, scanning positions j*VEC + e
+            // downwards; the block minimum of the ids is the first maximum
+            int bi = 0x7fffffff;
+            if (mt == M) {
+                int bp = 0;
+#pragma unroll
+                for (int j = kNV - 1; j >= 0; --j) {
+                    float f[VEC];
+                    unpack<T>(x[j], f);
+#pragma unroll
+                    for (int e = VEC - 1; e >= 0; --e)
+                        if (f[e] == M) bp = j * VEC + e;
+                }
+                bi = ((bp / VEC) * NT + t_) * VEC + bp % VEC;
+            }
+            bi = block_min_i(bi, sm.red);
             const unsigned long long hit = __ballot(par == cur && tok == bi);
             if (hit) next = __builtin_ctzll(hit);
             else bonus = bi;

@@ -30,7 +30,9 @@ template <> __device__ __forceinline__ float load_scalar<float>(const float *p) 
 template <> __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
 // One 16-byte vector of a row starting at element `base`; missing elements
-// read as -inf (never a candidate, weight 0).
+// read as -inf (never a candidate, weight 0).  Logit rows are read with the
+// default cache policy: they are usually written just before, and a
+// non-temporal read does not benefit from lines still held in the caches.
 template <typename T>
 __device__ __forceinline__ uint4 load_vec(const T *row, int base, int V, bool vec_ok)
 {

@@ -221,7 +221,13 @@ eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const vo
  * Outputs: accepted [batch][max_accept] node ids root-first, -1 padded;
  *   accept_len [batch]; bonus_token [batch].
  * Errors: EAGLE_ERR_INVALID for null pointers, T <= 0 in SAMPLE mode;
- * EAGLE_ERR_UNSUPPORTED past the v1 limits.
+ * EAGLE_ERR_UNSUPPORTED past the v1 limits.  Device errors (workspace error
+ * word): EAGLE_DEVERR_NONFINITE_ROW when a target row that is read holds a NaN
+ * (GREEDY) or gives a non-finite maximum or weight sum (SAMPLE), after which
+ * that sequence's outputs are unspecified (rows read: those on the walk, and in
+ * GREEDY for small batches every row of the tree); EAGLE_DEVERR_TREE for a
+ * num_nodes outside [0, m_max] or a child token outside [0, vocab);
+ * EAGLE_DEVERR_PATH when a path is longer than max_accept.
  */
 typedef struct {
     eagle_accept_mode mode;

@@ -73,9 +73,7 @@ ROUTES = [
 ]
 
 
-@pytest.mark.parametrize("name,dtype,V,mode,B,m_max,pad,T", ROUTES, ids=[r[0] for r in ROUTES])
-def test_accept_route(name, dtype, V, mode, B, m_max, pad, T):
-    say(f"[accept {name}] B={B} m_max={m_max} V={V} pad={pad}")
+def _inputs(name, dtype, V, mode, B, m_max, pad, T):
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     tokens, parent, nn = _random_tree(rng, B, m_max, V, n_lo=1)
     # greedy: a large boost walks the planted path; sampling: one that gives the
@@ -83,10 +81,11 @@ def test_accept_route(name, dtype, V, mode, B, m_max, pad, T):
     boost = 30.0 if mode == 0 else math.log(V) + 3.0
     target = _target(rng, B, m_max, V, tokens, parent, nn, dtype, boost=boost)
     words = rng.integers(0, 1 << 32, size=(B, m_max + 1), dtype=np.uint64).astype(np.uint32)
-    max_accept = m_max
-    o_acc, o_len, o_bon = oracle.accept(mode, to_np(target), tokens, parent, nn, max_accept,
-                                        rand_words=words if mode == 1 else None, T=T)
+    return tokens, parent, nn, target, words
 
+
+def _run_gpu(dtype, V, mode, B, m_max, pad, T, tokens, parent, nn, target, words):
+    """(accepted, accept_len, bonus, device error bits) from the C ABI."""
     dev = "cuda"
     if pad:
         # rows inside a wider buffer whose padding holds large values: any read
@@ -96,20 +95,54 @@ def test_accept_route(name, dtype, V, mode, B, m_max, pad, T):
         tg = buf.to(dev)[..., :V]
     else:
         tg = target.to(dev)
-    a = E.AcceptParams(mode, T, m_max, V, max_accept)
+    a = E.AcceptParams(mode, T, m_max, V, m_max)
     ws = torch.empty(max(256, E.accept_workspace_size(a, B)), dtype=torch.uint8, device=dev)
     E.workspace_init(ws)
-    acc = torch.empty((B, max_accept), dtype=torch.int32, device=dev)
+    acc = torch.empty((B, m_max), dtype=torch.int32, device=dev)
     alen = torch.empty(B, dtype=torch.int32, device=dev)
     bon = torch.empty(B, dtype=torch.int32, device=dev)
     w_dev = torch.from_numpy(words.view(np.int32)).to(dev) if mode == 1 else None
     E.accept(a, B, tg, torch.from_numpy(tokens).to(dev), torch.from_numpy(parent).to(dev),
              torch.from_numpy(nn).to(dev), w_dev, acc, alen, bon, ws)
     torch.cuda.synchronize()
-    assert E.read_errors(ws) == 0
-    assert np.array_equal(alen.cpu().numpy(), o_len), (alen.cpu().numpy(), o_len)
-    assert np.array_equal(acc.cpu().numpy(), o_acc)
-    assert np.array_equal(bon.cpu().numpy(), o_bon)
+    return acc.cpu().numpy(), alen.cpu().numpy(), bon.cpu().numpy(), E.read_errors(ws)
+
+
+@pytest.mark.parametrize("name,dtype,V,mode,B,m_max,pad,T", ROUTES, ids=[r[0] for r in ROUTES])
+def test_accept_route(name, dtype, V, mode, B, m_max, pad, T):
+    say(f"[accept {name}] B={B} m_max={m_max} V={V} pad={pad}")
+    tokens, parent, nn, target, words = _inputs(name, dtype, V, mode, B, m_max, pad, T)
+    o_acc, o_len, o_bon = oracle.accept(mode, to_np(target), tokens, parent, nn, m_max,
+                                        rand_words=words if mode == 1 else None, T=T)
+    acc, alen, bon, errs = _run_gpu(dtype, V, mode, B, m_max, pad, T, tokens, parent, nn, target, words)
+    assert errs == 0
+    assert np.array_equal(alen, o_len), (alen, o_len)
+    assert np.array_equal(acc, o_acc)
+    assert np.array_equal(bon, o_bon)
     say(f"[accept {name}] mean accepted length {o_len.mean():.2f}, max {o_len.max()}")
     # the walks must go beyond the root for the case to mean anything
     assert o_len.max() >= 2
+
+
+NAN_ROUTES = ["greedy-parallel-bf16", "greedy-reg-bf16-2vec", "greedy-reg-bf16-vmax", "sample-reg-bf16-1vec",
+              "greedy-loop-bf16-unaligned", "sample-loop-bf16-unaligned"]
+
+
+@pytest.mark.parametrize("name", NAN_ROUTES)
+def test_accept_nan_row_reported(name):
+    """A NaN in the root row of sequence 1 raises NONFINITE_ROW; the other
+    sequences' results are those of the clean rows."""
+    route = {r[0]: r for r in ROUTES}[name]
+    _, dtype, V, mode, B, m_max, pad, T = route
+    say(f"[accept nan {name}]")
+    tokens, parent, nn, target, words = _inputs(*route)
+    o_acc, o_len, o_bon = oracle.accept(mode, to_np(target), tokens, parent, nn, m_max,
+                                        rand_words=words if mode == 1 else None, T=T)
+    bad = target.clone()
+    bad[1, 0, V // 3] = float("nan")
+    acc, alen, bon, errs = _run_gpu(dtype, V, mode, B, m_max, pad, T, tokens, parent, nn, bad, words)
+    assert errs & E.DEVERR_NONFINITE_ROW
+    keep = np.arange(B) != 1
+    assert np.array_equal(alen[keep], o_len[keep])
+    assert np.array_equal(acc[keep], o_acc[keep])
+    assert np.array_equal(bon[keep], o_bon[keep])
