@@ -134,14 +134,20 @@ __device__ __forceinline__ void wait_vmcnt()
 // a wave computes its 32 rows against one 32-key half of every tile with its
 // own online-softmax state, and the two halves' states are combined through
 // LDS at the end, so every SIMD works on every tile.
-template <int kNW, int kKS>
-__global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
+template <int kNW, int kKS, bool kProd>
+__global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(AttnArgs a)
 {
     constexpr int kPer = kTileChunks / 64 / kNW;   // 16-byte slots per wave per operand per tile
     constexpr int kLw = 2 * kPer;                  // loads per wave per item
     constexpr int kRW = kNW / kKS;                 // row waves
     __shared__ AttnSmem sm;
     const int tid = threadIdx.x, NT = kNW * 64, lane = tid & 63, wv = tid >> 6;
+    constexpr int kThreads = kNW * 64 * (kProd ? 2 : 1);
+    // kProd: waves kNW.. only issue the tile loads (producers), so their issue
+    // stalls never hold up the compute waves that share their SIMDs
+    const bool producer = kProd && wv >= kNW;
+    const bool loader = !kProd || producer;
+    const int lw = kProd ? wv - kNW : wv;               // loader wave index
     const int ln = lane & 31, hh = lane >> 5;
     const int rw = wv % kRW, kh = wv / kRW;        // row wave, key half (kKS = 2)
     // block -> (split, row group, sequence/kv head); all splits and row groups
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
         if (item >= nprefix) {
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
-                const int it = wv * kPer + q, slot = it * 64 + lane;
+                const int it = lw * kPer + q, slot = it * 64 + lane;
                 const int r = slot >> 4, P = slot & 15;
                 const int t = swap23(r);
                 load_lds16(kd + ((drow + (t < n ? t : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &B.K[it * 64]);
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
                 const uint16_t *kt = kslab + (size_t)k0 * kHD, *vt = vslab + k0;
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    const int it = wv * kPer + q, slot = it * 64 + lane;
+                    const int it = lw * kPer + q, slot = it * 64 + lane;
                     const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
                     load_lds16(kt + (swap23(r) * kHD + ((P ^ (r & 15)) << 3)), &B.K[it * 64]);
                     load_lds16(vt + (e * a.cap + ((Q ^ ((e >> 1) & 7)) << 3)), &B.Vt[it * 64]);
@@ -224,13 +230,13 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
                 int pk[kPer], pv[kPer];
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    const int it = wv * kPer + q, slot = it * 64 + lane;
+                    const int it = lw * kPer + q, slot = it * 64 + lane;
                     pk[q] = sm.bt[tp + (swap23(slot >> 4) >> bshift)];
                     pv[q] = sm.bt[tp + ((((slot & 7) ^ ((slot >> 4) & 7)) << 3) >> bshift)];
                 }
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    const int it = wv * kPer + q, slot = it * 64 + lane;
+                    const int it = lw * kPer + q, slot = it * 64 + lane;
                     const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
                     const int ko = swap23(r), vj = (Q ^ ((e >> 1) & 7)) << 3;
                     load_lds16(kc + (size_t)pk[q] * pstride + kvh_off + (((ko & (bs - 1)) * kHD) + ((P ^ (r & 15)) << 3)),
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
             const int vlast = k0 + ((klast - k0) & ~7);   // first key of the chunk holding klast
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
-                const int it = wv * kPer + q, slot = it * 64 + lane;
+                const int it = lw * kPer + q, slot = it * 64 + lane;
                 const int r = slot >> 4, P = slot & 15;
                 const int key = min(k0 + swap23(r), klast);
                 load_lds16(k_src(key, P ^ (r & 15)), &B.K[it * 64]);
@@ -255,7 +261,8 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     };
 
     const int nspec = paged ? 0 : min(kAhead, nprefix);
-    for (int i = 0; i < nspec; ++i) issue(i);
+    if (loader)
+        for (int i = 0; i < nspec; ++i) issue(i);
     // Q fragments (B operand of S^T = K Q^T): lane holds q[my_row][16ks + 8hh .. +7]
     // (rows below m_max are addressable whatever num_nodes says; rows without
     // a node are zeroed below), the ancestor bits, and the sequence's lengths
@@ -298,14 +305,14 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
         page0 = key_lo / bs;
         if (key_hi > key_lo) {
             const int np = (key_hi - 1) / bs - page0 + 1;
-            for (int i = tid; i < np; i += NT) sm.bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
+            for (int i = tid; i < np; i += kThreads) sm.bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
         }
         __syncthreads();   // sm.bt visible
     }
 
     const int rows_valid = n * G;                        // rows with a real node
-    const bool wave_active = row0 < rows_valid && rw * 32 < a.rows_pg;
-    const bool row_ok = my_row < rows_valid && rw * 32 + ln < a.rows_pg;
+    const bool wave_active = !producer && row0 < rows_valid && rw * 32 < a.rows_pg;
+    const bool row_ok = !producer && my_row < rows_valid && rw * 32 + ln < a.rows_pg;
     if (!row_ok) {
         my_anc = 0;
 #pragma unroll
@@ -326,8 +333,30 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
     // fragments and the ancestor bits (the compiler cannot count loads across
     // the data-dependent issue loops, so a later wait for the Q registers
     // would be a full wait inside the pipeline)
-    for (int i = nspec; i < kAhead && i < nitems; ++i) issue(i);
+    if (loader)
+        for (int i = nspec; i < kAhead && i < nitems; ++i) issue(i);
     wait_vmcnt<0>();
+    if (producer) {
+        // the same barriers as the compute waves: one per item, one more for
+        // items the compute waves fix up in LDS (draft tile, tail tile), and
+        // the two of the key-half combine
+        for (int item = 0; item < nitems; ++item) {
+            const int later = min(kAhead - 1, nitems - 1 - item);
+            if (later >= 2) wait_vmcnt<2 * kLw>();
+            else if (later == 1) wait_vmcnt<kLw>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            const int k0 = key_lo + item * kTK;
+            if (item >= nprefix || k0 + kTK > key_hi) __syncthreads();
+            if (item + kAhead < nitems) issue(item + kAhead);
+        }
+        wait_vmcnt<0>();
+        if constexpr (kKS == 2) {
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
     for (int item = 0; item < nitems; ++item) {
         // this wave's loads of `item` have landed once at most the loads of
         // the (up to kAhead - 1) later items issued so far are outstanding
@@ -381,7 +410,7 @@ __global__ __launch_bounds__(kNW * 64) void k_tree_attn_bf16(AttnArgs a)
             }
             __syncthreads();
         }
-        if (item + kAhead < nitems) issue(item + kAhead);
+        if (!kProd && item + kAhead < nitems) issue(item + kAhead);
 
         if (wave_active) {
             // ---- S^T = K Q^T: two independent 32-key accumulators ----
@@ -815,11 +844,11 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
         if (P.waves == 4 && a.rows_pg <= 64)
-            hipLaunchKernelGGL((k_tree_attn_bf16<4, 2>), g, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<4, 2, true>), g, dim3(512), 0, st, a);
         else if (P.waves == 4)
-            hipLaunchKernelGGL((k_tree_attn_bf16<4, 1>), g, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<4, 1, false>), g, dim3(256), 0, st, a);
         else
-            hipLaunchKernelGGL((k_tree_attn_bf16<8, 1>), g, dim3(512), 0, st, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<8, 1, false>), g, dim3(512), 0, st, a);
         if (P.nsplit > 1) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

@@ -102,6 +102,11 @@ SMALL = {
     # paged, mixed trees and chains, ragged lengths, poisoned tails
     "bf16-paged-mixed": lambda: _small(5, batch=6, vocab=7001, prefix=(1, 5000),
                                        kinds=[0, 1, 0, 1, 1, 0]),
+    # paged MHA (query rows <= 64: the 4-wave key-half kernel), ragged lengths, poisoned tails
+    "bf16-mha-paged16": lambda: _small(2, batch=3, num_q_heads=8, num_kv_heads=8, prefix=(1, 2500),
+                                       block_size=16, poison_tail=True, kinds=[0, 0, 0], vocab=3000),
+    "bf16-mha-paged32": lambda: _small(2, batch=2, num_q_heads=4, num_kv_heads=4, prefix=(40, 5000),
+                                       block_size=32, poison_tail=True, kinds=[0, 0], vocab=3000),
     # sampling at temperature 0.7
     "bf16-rs-T0.7": lambda: dataclasses.replace(_small(3, batch=3, prefix=300, vocab=2000), temperature=0.7),
     # tiny vocabulary: fewer elements than one thread block, exact fallback top-C
