@@ -94,6 +94,19 @@ __device__ __forceinline__ int vpos(int e, int J) { return e * 8 + (J ^ ((e >> 1
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4a v) { return __builtin_bit_cast(bf16x8, v); }
 
+// v combined with the value of lane ^ 32 through one lane-half swap (a VALU
+// instruction, no LDS round trip); the result is the same in both lanes
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
 // (dst must be the same for the whole wave).  The loads carry the non-temporal
 // cache policy (bit 1 of the policy operand): K/V lines are streamed once, and
@@ -482,7 +495,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
             for (int u = 0; u < kNH; ++u)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[u][r]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_xor32(tmax);
             // Lazy rescaling: the exponent reference m_run moves (and O, l are
             // rescaled) only when some row's max grew by more than 2^8 in exp2
             // units; otherwise p = exp2((s - m_run) c) <= 2^8, which fp32 sums
@@ -509,7 +522,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
                     lsum += p;
                     pf[u][r >> 3][r & 7] = (__bf16)p;
                 }
-            lsum += __shfl_xor(lsum, 32);
+            lsum = sum_xor32(lsum);
             l_run += lsum;
             // ---- O^T += V^T P^T: four independent accumulators per k-step ----
             if constexpr (kEarly == kNV) {
