@@ -287,11 +287,11 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             u32x4a v = {0, 0, 0, 0};
-            if (row_exists) v = qrow[2 * ks + hh];
+            if (row_exists && !producer) v = qrow[2 * ks + hh];
             qf[ks] = as_bf16x8(v);
         }
     }
-    uint64_t my_anc = row_exists ? a.anc[(size_t)b * m_max + my_node] : 0;
+    uint64_t my_anc = (row_exists && !producer) ? a.anc[(size_t)b * m_max + my_node] : 0;
     int L = a.prefix_len[b];
     n = a.num_nodes[b];
     if (L < 0 || L > a.cap) {
@@ -342,12 +342,16 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
     const float c2 = a.scale_log2;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
-    // the remaining first items; one full wait then covers them, the Q
-    // fragments and the ancestor bits (the compiler cannot count loads across
-    // the data-dependent issue loops, so a later wait for the Q registers
-    // would be a full wait inside the pipeline)
+    // the remaining first items (from the first one not requested as a
+    // prefix tile: a sequence shorter than the capacity has its draft tile
+    // among the speculative requests, which were drained above); one full
+    // wait then covers them, the Q fragments and the ancestor bits (the
+    // compiler cannot count loads across the data-dependent issue loops, so a
+    // later wait for the Q registers would be a full wait inside the pipeline)
     if (loader)
-        for (int i = nspec; i < kAhead && i < nitems; ++i) issue(i);
+        for (int i = min(nspec, nprefix); i < kAhead && i < nitems; ++i) issue(i);
+    // (producers wait for their first tiles here too: letting them run ahead
+    // of the first barrier measured slower)
     wait_vmcnt<0>();
     if (producer) {
         // the same barriers as the compute waves: one per item, one more for

@@ -107,6 +107,11 @@ SMALL = {
                                        block_size=16, poison_tail=True, kinds=[0, 0, 0], vocab=3000),
     "bf16-mha-paged32": lambda: _small(2, batch=2, num_q_heads=4, num_kv_heads=4, prefix=(40, 5000),
                                        block_size=32, poison_tail=True, kinds=[0, 0], vocab=3000),
+    # contiguous cache with ragged prefixes: short sequences' first tiles are
+    # requested past their prefix before its length is known (draft tile among them)
+    "bf16-contig-ragged": lambda: _small(2, batch=4, num_q_heads=8, num_kv_heads=8, prefix=(5, 3000),
+                                         kinds=[0, 0, 0, 0], vocab=3000),
+    "bf16-gqa-contig-ragged": lambda: _small(4, batch=3, prefix=(5, 2000), vocab=3000),
     # sampling at temperature 0.7
     "bf16-rs-T0.7": lambda: dataclasses.replace(_small(3, batch=3, prefix=300, vocab=2000), temperature=0.7),
     # tiny vocabulary: fewer elements than one thread block, exact fallback top-C
