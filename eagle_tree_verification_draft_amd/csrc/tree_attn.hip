@@ -66,8 +66,6 @@ __device__ __forceinline__ const T *v_elem(const AttnArgs &a, int b, int kvh, in
 
 constexpr int kTileChunks = kTK * kHD * 2 / 16;   // 16-byte chunks per K (or V^T) tile: 1024
 constexpr int kMaxPages = 4096 / 8 + 2;             // pages of one split (chunk <= 4096, page >= 8)
-constexpr int kNBuf = 4;                            // LDS ring of K / V^T tiles
-constexpr int kAhead = kNBuf - 1;                   // tiles in flight ahead of the one in use
 
 typedef unsigned int u32x4a __attribute__((ext_vector_type(4)));
 
@@ -83,11 +81,28 @@ struct AttnBuf {
     u32x4a Vt[kHD * 8];
 };
 
-struct AttnSmem {
-    AttnBuf buf[kNBuf];
+// LDS of one workgroup: a ring of kRing tile buffers (kRing - 1 tiles in flight
+// ahead of the one in use).  A paged cache needs the split's page list and a
+// staging area for the draft V rows, so its ring has 4 buffers; a contiguous
+// cache stages the draft V rows in the draft buffer's own V^T area, and its
+// ring of 5 buffers fills the 160 KB of LDS.
+template <int kRing> struct AttnSmem;
+template <> struct AttnSmem<4> {
+    AttnBuf buf[4];
     u32x4a dv[kTK * 16];   // draft V rows as they arrive (key-major, swizzled like K)
     int bt[kMaxPages];
 };
+template <> struct AttnSmem<5> {
+    AttnBuf buf[5];
+};
+static_assert(sizeof(AttnSmem<5>) <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ int *page_list(AttnSmem<4> &sm) { return sm.bt; }
+__device__ __forceinline__ int *page_list(AttnSmem<5> &) { return nullptr; }   // contiguous only
+// where the draft V rows land (key-major) before the transpose into V^T
+__device__ __forceinline__ u32x4a *draft_rows(AttnSmem<4> &sm, AttnBuf &) { return sm.dv; }
+__device__ __forceinline__ u32x4a *draft_rows(AttnSmem<5> &, AttnBuf &B) { return B.Vt; }
+
 
 __device__ __forceinline__ int kpos(int r, int J) { return r * 16 + (J ^ (r & 15)); }
 __device__ __forceinline__ int vpos(int e, int J) { return e * 8 + (J ^ ((e >> 1) & 7)); }
@@ -128,6 +143,17 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// waits until this wave's loads of the current item have landed, the loads of
+// `later` later items (at most kMaxLater) still outstanding
+template <int kLw, int kMaxLater>
+__device__ __forceinline__ void wait_item(int later)
+{
+    if (kMaxLater >= 3 && later >= 3) wait_vmcnt<(kMaxLater >= 3 ? 3 : 0) * kLw>();
+    else if (kMaxLater >= 2 && later >= 2) wait_vmcnt<(kMaxLater >= 2 ? 2 : 0) * kLw>();
+    else if (later >= 1) wait_vmcnt<kLw>();
+    else wait_vmcnt<0>();
+}
+
 // Work items of one workgroup, in processing order: the prefix tiles of the
 // split, then the draft tile (last key split only, when the sequence has
 // nodes).  With a contiguous cache the first prefix tiles are requested
@@ -140,24 +166,32 @@ __device__ __forceinline__ void wait_vmcnt()
 //     last valid key (finite data; the scores of those keys are masked), and
 //     V^T entries of those keys are zeroed in LDS before use, since the chunk
 //     that straddles prefix_len may carry anything past it;
-//   - draft tile: K rows of the draft tokens, and their V rows key-major into
-//     sm.dv, transposed to V^T in LDS (zeros for keys >= num_nodes) before use.
+//   - draft tile: K rows of the draft tokens, and their V rows key-major into a
+//     staging area (the 4-buffer ring's own, or the draft buffer's V^T area),
+//     transposed to V^T in LDS (zeros for keys >= num_nodes) before use.
 //
 // kKS = 2 (few query rows): the waves form kNW / 2 row waves x 2 key halves;
 // a wave computes its 32 rows against one 32-key half of every tile with its
 // own online-softmax state, and the two halves' states are combined through
 // LDS at the end, so every SIMD works on every tile.
-template <int kNW, int kKS, bool kProd>
-__global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(AttnArgs a)
+// which waves issue the tile loads (see the kernel)
+constexpr int kLoadAll = 0, kLoadProducers = 1;
+
+template <int kNW, int kKS, int kLoad, int kRing>
+__global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void k_tree_attn_bf16(AttnArgs a)
 {
-    constexpr int kPer = kTileChunks / 64 / kNW;   // 16-byte slots per wave per operand per tile
-    constexpr int kLw = 2 * kPer;                  // loads per wave per item
+    constexpr int kAhead = kRing - 1;                   // tiles in flight ahead of the one in use
+    constexpr bool kProd = kLoad == kLoadProducers;
+    constexpr int kPer = kTileChunks / 64 / kNW;        // 16-byte slots per loading wave per operand per tile
+    constexpr int kLw = 2 * kPer;                       // loads per loading wave per item
     constexpr int kRW = kNW / kKS;                 // row waves
-    __shared__ AttnSmem sm;
+    __shared__ AttnSmem<kRing> sm;
+    int *const bt = page_list(sm);
     const int tid = threadIdx.x, NT = kNW * 64, lane = tid & 63, wv = tid >> 6;
     constexpr int kThreads = kNW * 64 * (kProd ? 2 : 1);
-    // kProd: waves kNW.. only issue the tile loads (producers), so their issue
-    // stalls never hold up the compute waves that share their SIMDs
+    // kLoadProducers: waves kNW.. only issue the tile loads (producers), so
+    // their issue stalls never hold up the compute waves that share their
+    // SIMDs (kLoadAll: every wave issues its share and computes)
     const bool producer = kProd && wv >= kNW;
     const bool loader = !kProd || producer;
     const int lw = kProd ? wv - kNW : wv;               // loader wave index
@@ -173,7 +207,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
     const int b = u0 / a.Hkv, kvh = u0 % a.Hkv;
     const int G = a.G, m_max = a.m_max;
 
-    const bool paged = a.block_size != 0;
+    const bool paged = kRing == 4 && a.block_size != 0;   // the 5-buffer ring serves contiguous caches
     const int bs = a.block_size;
     const int key_lo = s * a.chunk;
     const int row0 = rg * a.rows_pg + rw * 32;          // first row of this wave
@@ -200,12 +234,12 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
 
     auto k_src = [&](int key, int J) -> const uint16_t * {
         if (!paged) return kslab + (size_t)key * kHD + J * 8;
-        const int blk = sm.bt[key / bs - page0];
+        const int blk = bt[key / bs - page0];
         return kc + (((size_t)blk * a.Hkv + kvh) * bs + key % bs) * kHD + J * 8;
     };
     auto v_src = [&](int e, int key) -> const uint16_t * {
         if (!paged) return vslab + (size_t)e * a.cap + key;
-        const int blk = sm.bt[key / bs - page0];
+        const int blk = bt[key / bs - page0];
         return vc + (((size_t)blk * a.Hkv + kvh) * kHD + e) * bs + key % bs;
     };
     const size_t drow = (size_t)b * m_max;               // draft rows of this sequence
@@ -216,7 +250,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
     const size_t pstride = (size_t)a.Hkv * bs * kHD;     // elements per page (K and V^T alike)
     const size_t kvh_off = (size_t)kvh * bs * kHD;
     auto issue = [&](int item) {
-        AttnBuf &B = sm.buf[item % kNBuf];
+        AttnBuf &B = sm.buf[item % kRing];
         if (item >= nprefix) {
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
@@ -224,7 +258,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
                 const int r = slot >> 4, P = slot & 15;
                 const int t = swap23(r);
                 load_lds16(kd + ((drow + (t < n ? t : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &B.K[it * 64]);
-                load_lds16(vd + ((drow + (r < n ? r : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &sm.dv[it * 64]);
+                load_lds16(vd + ((drow + (r < n ? r : 0)) * a.Hkv + kvh) * kHD + (P ^ (r & 15)) * 8, &draft_rows(sm, B)[it * 64]);
             }
         } else if (key_lo + (item + 1) * kTK <= key_hi && fast_pages) {
             // full tile: lane offsets from shifts and masks only
@@ -244,8 +278,8 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
                     const int it = lw * kPer + q, slot = it * 64 + lane;
-                    pk[q] = sm.bt[tp + (swap23(slot >> 4) >> bshift)];
-                    pv[q] = sm.bt[tp + ((((slot & 7) ^ ((slot >> 4) & 7)) << 3) >> bshift)];
+                    pk[q] = bt[tp + (swap23(slot >> 4) >> bshift)];
+                    pv[q] = bt[tp + ((((slot & 7) ^ ((slot >> 4) & 7)) << 3) >> bshift)];
                 }
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
@@ -318,9 +352,9 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
         page0 = key_lo / bs;
         if (key_hi > key_lo) {
             const int np = (key_hi - 1) / bs - page0 + 1;
-            for (int i = tid; i < np; i += kThreads) sm.bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
+            for (int i = tid; i < np; i += kThreads) bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
         }
-        __syncthreads();   // sm.bt visible
+        __syncthreads();   // page list visible
     }
 
     const int rows_valid = n * G;                        // rows with a real node
@@ -358,10 +392,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
         // items the compute waves fix up in LDS (draft tile, tail tile), and
         // the two of the key-half combine
         for (int item = 0; item < nitems; ++item) {
-            const int later = min(kAhead - 1, nitems - 1 - item);
-            if (later >= 2) wait_vmcnt<2 * kLw>();
-            else if (later == 1) wait_vmcnt<kLw>();
-            else wait_vmcnt<0>();
+            wait_item<kLw, kAhead - 1>(min(kAhead - 1, nitems - 1 - item));
             __syncthreads();
             const int k0 = key_lo + item * kTK;
             if (item >= nprefix || k0 + kTK > key_hi) __syncthreads();
@@ -377,24 +408,27 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
     for (int item = 0; item < nitems; ++item) {
         // this wave's loads of `item` have landed once at most the loads of
         // the (up to kAhead - 1) later items issued so far are outstanding
-        const int later = min(kAhead - 1, nitems - 1 - item);
-        if (later >= 2) wait_vmcnt<2 * kLw>();
-        else if (later == 1) wait_vmcnt<kLw>();
-        else wait_vmcnt<0>();
+        wait_item<kLw, kAhead - 1>(min(kAhead - 1, nitems - 1 - item));
         __syncthreads();                      // ... and every wave's; item - 1 is fully consumed
-        AttnBuf &B = sm.buf[item % kNBuf];
+        AttnBuf &B = sm.buf[item % kRing];
         const bool draft = item >= nprefix;
+        // V^T of this item: with the 5-buffer ring the draft's V rows are staged
+        // in its own buffer's V^T area and transposed into the previous item's
+        // buffer (fully consumed, and the draft is the last item, so nothing is
+        // requested into it again)
+        u32x4a *const Vt = (kRing == 5 && draft) ? sm.buf[(item + kRing - 1) % kRing].Vt : B.Vt;
         const int k0 = key_lo + item * kTK;
         if (draft) {
             // draft V rows (key-major) -> V^T, zeros for keys >= n; thread =
             // (8 dims, 8 keys): an 8x8 block of bf16 transposed in registers
+            const u32x4a *dv = draft_rows(sm, B);
             if (tid < 128) {
                 const int e8 = tid & 15, kg = tid >> 4;
                 u32x4a rows[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int t = 8 * kg + u;
-                    rows[u] = t < n ? sm.dv[t * 16 + (e8 ^ (t & 15))] : u32x4a{0, 0, 0, 0};
+                    rows[u] = t < n ? dv[t * 16 + (e8 ^ (t & 15))] : u32x4a{0, 0, 0, 0};
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -406,7 +440,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
                         const uint32_t hi = (rows[2 * p + 1][w] >> sh) & 0xffffu;
                         o[p] = lo | (hi << 16);
                     }
-                    B.Vt[vpos(8 * e8 + q, kg)] = o;
+                    Vt[vpos(8 * e8 + q, kg)] = o;
                 }
             }
             __syncthreads();
@@ -467,7 +501,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
 #pragma unroll
             for (int j = 0; j < kEarly; ++j) {
                 const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
-                va[j] = B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
+                va[j] = Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
             }
             __builtin_amdgcn_sched_barrier(0);
             // sacc[u][8t + q] is the raw score of tile key 32(sh0 + u) + 16t + 8hh + q
@@ -541,7 +575,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
 #pragma unroll
                     for (int j = g0; j < g0 + 8; ++j) {
                         const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
-                        va[j] = B.Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
+                        va[j] = Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -560,7 +594,7 @@ __global__ __launch_bounds__(kNW * 64 * (kProd ? 2 : 1)) void k_tree_attn_bf16(A
         // (the tile ring is free once every wave has left the loop)
         __syncthreads();
         float *xo = reinterpret_cast<float *>(sm.buf) + (size_t)rw * 64 * 64;   // [64 regs][64 lanes]
-        float2 *xml = reinterpret_cast<float2 *>(sm.dv) + rw * 64;
+        float2 *xml = reinterpret_cast<float2 *>(reinterpret_cast<float *>(sm.buf) + (size_t)kRW * 64 * 64) + rw * 64;
         if (kh == 1 && wave_active) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
@@ -860,12 +894,17 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
         hipLaunchKernelGGL(k_tree_attn_f32, g, dim3(64), 0, st, a);
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
-        if (P.waves == 4 && a.rows_pg <= 64)
-            hipLaunchKernelGGL((k_tree_attn_bf16<4, 2, true>), g, dim3(512), 0, st, a);
-        else if (P.waves == 4)
-            hipLaunchKernelGGL((k_tree_attn_bf16<4, 1, false>), g, dim3(256), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_tree_attn_bf16<8, 1, false>), g, dim3(512), 0, st, a);
+        const bool contiguous = p->block_size == 0;
+        if (P.waves == 4 && a.rows_pg <= 64) {
+            if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16<4, 2, kLoadProducers, 5>), g, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_tree_attn_bf16<4, 2, kLoadProducers, 4>), g, dim3(512), 0, st, a);
+        } else if (P.waves == 4) {
+            if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16<4, 1, kLoadAll, 5>), g, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((k_tree_attn_bf16<4, 1, kLoadAll, 4>), g, dim3(256), 0, st, a);
+        } else {
+            if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16<8, 1, kLoadAll, 5>), g, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_tree_attn_bf16<8, 1, kLoadAll, 4>), g, dim3(512), 0, st, a);
+        }
         if (P.nsplit > 1) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

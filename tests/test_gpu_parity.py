@@ -112,6 +112,11 @@ SMALL = {
     "bf16-contig-ragged": lambda: _small(2, batch=4, num_q_heads=8, num_kv_heads=8, prefix=(5, 3000),
                                          kinds=[0, 0, 0, 0], vocab=3000),
     "bf16-gqa-contig-ragged": lambda: _small(4, batch=3, prefix=(5, 2000), vocab=3000),
+    # 65..128 query rows (G = 2): the 4-wave kernel over whole tiles, contiguous and paged
+    "bf16-g2-rows120": lambda: _small(2, batch=2, num_q_heads=8, num_kv_heads=4, prefix=(200, 1500),
+                                      kinds=[0, 0], vocab=3000),
+    "bf16-g2-rows120-paged": lambda: _small(2, batch=2, num_q_heads=8, num_kv_heads=4, prefix=(200, 1500),
+                                            block_size=16, poison_tail=True, kinds=[0, 0], vocab=3000),
     # sampling at temperature 0.7
     "bf16-rs-T0.7": lambda: dataclasses.replace(_small(3, batch=3, prefix=300, vocab=2000), temperature=0.7),
     # tiny vocabulary: fewer elements than one thread block, exact fallback top-C
