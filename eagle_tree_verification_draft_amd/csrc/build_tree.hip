@@ -158,7 +158,9 @@ __global__ __launch_bounds__(1024) void k_row_stats(RowStatsArgs a)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             wsum += (double)weight_of(f[e], M);
-            if (f[e] >= thr && base + e < V) {
+            // padding reads -inf, below any finite T; with T = -inf the list
+            // is not used (exact selection instead), so nothing is appended
+            if (use_list && f[e] >= thr) {
                 const int o = atomicAdd(&sm.count, 1);
                 if (o < kCandCap) { sm.cand_v[o] = f[e]; sm.cand_i[o] = base + e; }
             }
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(1024) void k_row_stats_stream(RowStatsArgs a)
             for (int e = 0; e < VEC; ++e) {
                 wsum += (double)weight_of(f[e], M);
                 const int id = v * VEC + e;
-                if (f[e] >= thr && id < V) {
+                if (use_list && f[e] >= thr) {   // as in the register form
                     const int o = atomicAdd(&sm.count, 1);
                     if (o < kCandCap) { sm.cand_v[o] = f[e]; sm.cand_i[o] = id; }
                 }
