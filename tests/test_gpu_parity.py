@@ -117,6 +117,14 @@ SMALL = {
                                       kinds=[0, 0], vocab=3000),
     "bf16-g2-rows120-paged": lambda: _small(2, batch=2, num_q_heads=8, num_kv_heads=4, prefix=(200, 1500),
                                             block_size=16, poison_tail=True, kinds=[0, 0], vocab=3000),
+    # page sizes 8 and 64 (page-major V^T with 1 and 8 chunks per page) and 24
+    # (pages that do not tile a 64-key tile: per-key page lookups, swizzled V^T)
+    "bf16-paged8": lambda: _small(5, batch=2, vocab=3000, prefix=(30, 1200), block_size=8, poison_tail=True,
+                                  kinds=[0, 1]),
+    "bf16-paged64": lambda: _small(5, batch=2, vocab=3000, prefix=(30, 1200), block_size=64, poison_tail=True,
+                                   kinds=[0, 1]),
+    "bf16-paged24": lambda: _small(2, batch=2, num_q_heads=8, num_kv_heads=8, vocab=3000, prefix=(30, 1200),
+                                   block_size=24, poison_tail=True, kinds=[0, 0]),
     # sampling at temperature 0.7
     "bf16-rs-T0.7": lambda: dataclasses.replace(_small(3, batch=3, prefix=300, vocab=2000), temperature=0.7),
     # tiny vocabulary: fewer elements than one thread block, exact fallback top-C
