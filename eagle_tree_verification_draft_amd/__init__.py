@@ -34,6 +34,7 @@ EXPORTS = (
     "eagle_build_tree_workspace_size", "eagle_build_tree",
     "eagle_tree_mask",
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
+    "eagle_kv_commit",
     "eagle_accept_workspace_size", "eagle_accept",
     "eagle_status_string", "eagle_last_error",
 )
@@ -82,6 +83,8 @@ def lib() -> C.CDLL:
         L.eagle_tree_attn_workspace_size.argtypes = [C.POINTER(AttnParams), i32]
         L.eagle_tree_attn_workspace_size.restype = sz
         L.eagle_tree_attn.argtypes = [C.POINTER(AttnParams), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.eagle_kv_commit.argtypes = [C.POINTER(AttnParams), i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
         L.eagle_accept_workspace_size.argtypes = [C.POINTER(AcceptParams), i32]
         L.eagle_accept_workspace_size.restype = sz
         L.eagle_accept.argtypes = [C.POINTER(AcceptParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -91,7 +94,7 @@ def lib() -> C.CDLL:
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
         for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_tree_mask",
-                  "eagle_tree_attn", "eagle_accept"):
+                  "eagle_tree_attn", "eagle_kv_commit", "eagle_accept"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -188,6 +191,16 @@ def tree_attn(a: AttnParams, batch: int, q, k_draft, v_draft, k_cache, v_cache, 
            "eagle_tree_attn")
 
 
+def kv_commit(a: AttnParams, batch: int, k_draft, v_draft, accepted, accept_len, prefix_len, k_cache, v_cache,
+              block_table, slot_mapping, prefix_len_out, workspace: torch.Tensor, stream=None):
+    """accepted is [batch][max_accept]; prefix_len_out may be prefix_len itself."""
+    _check(lib().eagle_kv_commit(C.byref(a), batch, _ptr(k_draft), _ptr(v_draft), _ptr(accepted),
+                                 _ptr(accept_len), accepted.shape[-1], _ptr(prefix_len), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(block_table), _ptr(slot_mapping), _ptr(prefix_len_out),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_kv_commit")
+
+
 def accept_workspace_size(a: AcceptParams, batch: int) -> int:
     return lib().eagle_accept_workspace_size(C.byref(a), batch)
 
@@ -260,10 +273,12 @@ class VerifyStep:
         self.accepted = torch.empty((B, s.max_accept), **i32)
         self.accept_len = torch.empty((B,), **i32)
         self.bonus = torch.empty((B,), **i32)
+        self.slot_mapping = torch.empty((B, M), **i32)
         self.ws_tree = _workspace(build_tree_workspace_size(self.tree, B), dev)
         self.ws_mask = _workspace(256, dev)
         self.ws_attn = _workspace(tree_attn_workspace_size(self.attn, B), dev)
         self.ws_acc = _workspace(accept_workspace_size(self.acc, B), dev)
+        self.ws_commit = _workspace(256, dev)
 
     def build(self, draft_logits, kind=None, stream=None):
         build_tree(self.tree, self.s.batch, draft_logits, kind, self.tokens, self.parent, self.depth, self.score,
@@ -281,6 +296,14 @@ class VerifyStep:
         accept(self.acc, self.s.batch, target_logits, self.tokens, self.parent, self.num_nodes, rand_words,
                self.accepted, self.accept_len, self.bonus, self.ws_acc, stream)
 
+    def commit(self, k_draft, v_draft, prefix_len, k_cache, v_cache, block_table, prefix_len_out=None,
+               stream=None):
+        """Writes the accepted path's draft K/V into the cache; prefix_len_out
+        defaults to prefix_len itself (advanced in place)."""
+        kv_commit(self.attn, self.s.batch, k_draft, v_draft, self.accepted, self.accept_len, prefix_len, k_cache,
+                  v_cache, block_table, self.slot_mapping,
+                  prefix_len if prefix_len_out is None else prefix_len_out, self.ws_commit, stream)
+
     def run(self, draft_logits, kind, prefix_len, q, k_draft, v_draft, k_cache, v_cache, block_table,
             target_logits, rand_words=None, stream=None):
         self.build(draft_logits, kind, stream)
@@ -290,6 +313,6 @@ class VerifyStep:
 
     def errors(self) -> int:
         bits = 0
-        for ws in (self.ws_tree, self.ws_mask, self.ws_attn, self.ws_acc):
+        for ws in (self.ws_tree, self.ws_mask, self.ws_attn, self.ws_acc, self.ws_commit):
             bits |= read_errors(ws)
         return bits

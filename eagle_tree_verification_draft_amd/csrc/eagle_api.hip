@@ -215,6 +215,31 @@ eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const vo
                       "tree_attn launch");
 }
 
+eagle_status eagle_kv_commit(const eagle_attn_params *a, int32_t batch, const void *k_draft,
+                             const void *v_draft, const int32_t *accepted, const int32_t *accept_len,
+                             int32_t max_accept, const int32_t *prefix_len, void *k_cache, void *v_cache,
+                             const int32_t *block_table, int32_t *slot_mapping, int32_t *prefix_len_out,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    eagle_status s = check_attn_params(a, batch);
+    if (s != EAGLE_OK) return s;
+    if (max_accept < 1) return fail(EAGLE_ERR_INVALID, "max_accept %d < 1", max_accept);
+    const bool no_cache = a->block_size == 0 && a->max_prefix == 0;
+    if (!k_draft || !v_draft || !accepted || !accept_len || !prefix_len || (!no_cache && (!k_cache || !v_cache)) ||
+        !slot_mapping || !prefix_len_out)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (a->block_size > 0 && !block_table) return fail(EAGLE_ERR_INVALID, "paged cache needs a block table");
+    if (!(aligned16(k_draft) && aligned16(v_draft) && aligned16(k_cache)))
+        return fail(EAGLE_ERR_UNSUPPORTED, "k_draft, v_draft and k_cache must be 16-byte aligned");
+    s = check_workspace(workspace, workspace_bytes, kWsHeader);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_kv_commit(a, batch, k_draft, v_draft, accepted, accept_len, max_accept, prefix_len,
+                                       k_cache, v_cache, block_table, slot_mapping, prefix_len_out,
+                                       static_cast<uint32_t *>(workspace), (hipStream_t)stream),
+                      "kv_commit launch");
+}
+
 size_t eagle_accept_workspace_size(const eagle_accept_params *a, int32_t batch)
 {
     if (!a || batch < 0 || a->m_max < 1 || a->m_max > kMaxMMax) return kWsHeader;

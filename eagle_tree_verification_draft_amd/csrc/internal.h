@@ -78,6 +78,16 @@ hipError_t launch_tree_attn(const eagle_attn_params *a, const AttnPlan &P, int32
                             const int32_t *prefix_len, const uint64_t *anc, const int32_t *num_nodes,
                             void *out, void *ws, hipStream_t st);
 
+// ---- KV commit -----------------------------------------------------------
+// positions a sequence's cache may hold: contiguous max_prefix; paged
+// max_prefix when it is in (0, max_blocks * block_size), else the pages' total
+int commit_capacity(const eagle_attn_params *p);
+
+hipError_t launch_kv_commit(const eagle_attn_params *p, int32_t batch, const void *k_draft, const void *v_draft,
+                            const int32_t *accepted, const int32_t *accept_len, int32_t max_accept,
+                            const int32_t *prefix_len, void *k_cache, void *v_cache, const int32_t *block_table,
+                            int32_t *slot_mapping, int32_t *prefix_len_out, uint32_t *err, hipStream_t st);
+
 // ---- accept --------------------------------------------------------------
 hipError_t launch_accept(const eagle_accept_params *a, int32_t batch, const void *target,
                          eagle_dtype dt, int64_t row_stride, const int32_t *tokens,

@@ -198,6 +198,49 @@ eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const vo
                              size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
+/* KV commit                                                           */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (EAGLE-1 explainer, "Verification": the accepted tokens extend the
+ * sequence; P-EAGLE page, "KV cache and CUDA graphs": tokens that are not
+ * kept map to the padding slot -1, so nothing is written for them).  For
+ * sequence b with L = prefix_len[b] and A = accept_len[b]: the j-th accepted
+ * node (node id accepted[b][j], j < A, root-first as eagle_accept writes
+ * them) is the token at position L + j.  Its draft K/V rows
+ * (k_draft / v_draft [b][node][kvh][:], every kv head) are written into the
+ * cache at that position, in the layouts of eagle_tree_attn (same params):
+ *   contiguous: k_cache[b][kvh][L + j][:] and v_cache[b][kvh][:][L + j]
+ *   paged:      page p = block_table[b][(L + j) / block_size], slot
+ *               t = (L + j) % block_size: k_cache[p][kvh][t][:], v_cache[p][kvh][:][t]
+ * slot_mapping[b][i] (i < m_max) = the cache slot of node i if it was
+ * committed (contiguous: L + j; paged: p * block_size + t), else -1.
+ * prefix_len_out[b] = L + (tokens committed); it may alias prefix_len.
+ * Nothing else in the cache is written; if a node id repeats, slot_mapping
+ * holds its later position.  accepted is [batch][max_accept]; a sequence's
+ * capacity is the bound eagle_tree_attn clamps prefix_len to (contiguous:
+ * max_prefix; paged: max_prefix when it is in (0, max_blocks * block_size),
+ * else max_blocks * block_size), so prefix_len_out is valid for the next
+ * eagle_tree_attn call with the same params.  Page ids in block_table must
+ * name pages of the cache (not checked).
+ * The commit of a sequence stops at the first token that cannot be written: a
+ * node id outside [0, m_max) (EAGLE_DEVERR_TREE), or a position at or past
+ * the capacity or on an unassigned page (EAGLE_DEVERR_PREFIX).  L outside
+ * [0, capacity] commits nothing and leaves prefix_len_out[b] = L
+ * (EAGLE_DEVERR_PREFIX); accept_len outside [0, min(max_accept, m_max)] is
+ * clamped to that range (EAGLE_DEVERR_TREE).
+ * Workspace: only the error word (eagle_workspace_init'ed, >= 256 bytes).
+ * Errors: EAGLE_ERR_INVALID for null pointers or max_accept < 1; the
+ * parameter checks of eagle_tree_attn; EAGLE_ERR_UNSUPPORTED unless k_draft,
+ * v_draft and k_cache are 16-byte aligned.  A commit must not run
+ * concurrently (on another stream) with a call that reads the same cache.
+ */
+eagle_status eagle_kv_commit(const eagle_attn_params *a, int32_t batch, const void *k_draft,
+                             const void *v_draft, const int32_t *accepted, const int32_t *accept_len,
+                             int32_t max_accept, const int32_t *prefix_len, void *k_cache, void *v_cache,
+                             const int32_t *block_table, int32_t *slot_mapping, int32_t *prefix_len_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* Acceptance                                                          */
 /* ------------------------------------------------------------------ */
 /*

@@ -52,9 +52,10 @@ def lib():
         L.orc_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp]
         L.orc_tree_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_tree_attn_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+        L.orc_kv_commit.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.orc_accept.argtypes = [i32, f32, i32, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp]
         for f in ("orc_row_stats", "orc_build_tree", "orc_tree_mask", "orc_tree_attn",
-                  "orc_tree_attn_rows", "orc_accept", "orc_num_threads"):
+                  "orc_tree_attn_rows", "orc_kv_commit", "orc_accept", "orc_num_threads"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -207,6 +208,41 @@ def tree_attn_rows(q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_le
                                     _p(pl), _p(an), len(sel), _p(sb), _p(si), _p(sh), _p(out)),
            "tree_attn_rows")
     return out
+
+
+def kv_commit(k_draft, v_draft, accepted, accept_len, prefix_len, k_cache, v_cache, block_table=None,
+              max_prefix=0):
+    """The accepted path's draft K/V written into copies of the caches.
+
+    Layouts as in tree_attn (contiguous [B][Hkv][P][d] / [B][Hkv][d][P]; paged
+    [pages][Hkv][bs][d] / [pages][Hkv][d][bs] with block_table [B][max_blocks]).
+    Capacity: contiguous P; paged max_prefix if it is in (0, max_blocks * bs),
+    else max_blocks * bs.  Returns (k_cache, v_cache, slot_mapping [B][m_max],
+    prefix_len_out [B], (tree_flags, prefix_flags))."""
+    kd, vd = np.ascontiguousarray(k_draft), np.ascontiguousarray(v_draft)
+    kc, vc = np.array(k_cache, copy=True, order="C"), np.array(v_cache, copy=True, order="C")
+    dt = 0 if kd.dtype == np.float32 else 1
+    for x in (kd, vd, kc, vc):
+        if (x.dtype == np.float32) != (dt == 0) or x.dtype not in (np.float32, np.uint16):
+            raise TypeError("K/V inputs must all be float32 or all uint16 (bf16 bits)")
+    B, M, Hkv, d = kd.shape
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    alen = np.ascontiguousarray(accept_len, dtype=np.int32)
+    pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
+    if block_table is None:
+        bt, bs, maxb, rows = None, 0, 0, kc.shape[2]
+        cap = rows
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bs, maxb, rows = kc.shape[2], bt.shape[1], 0
+        cap = max_prefix if 0 < max_prefix < maxb * bs else maxb * bs
+    p = _AttnParams(Hkv, Hkv, d, M, bs, maxb, rows, dt, 1.0)
+    slot = np.zeros((B, M), np.int32)
+    plo = np.zeros(B, np.int32)
+    flags = np.zeros(2, np.int32)
+    _check(lib().orc_kv_commit(C.byref(p), cap, B, _p(kd), _p(vd), _p(acc), _p(alen), acc.shape[1], _p(pl),
+                               _p(kc), _p(vc), _p(bt), _p(slot), _p(plo), _p(flags)), "kv_commit")
+    return kc, vc, slot, plo, (int(flags[0]), int(flags[1]))
 
 
 def accept(mode, target_logits, tokens, parent, num_nodes, max_accept, rand_words=None, T=1.0):

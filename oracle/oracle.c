@@ -16,6 +16,10 @@
  *   - attention mask: each token sees only its own ancestors (section
  *     "Attention mask adjustment"); tree attention processes the branches in
  *     one pass (EAGLE-1 explainer, "Role of Tree Attention");
+ *   - KV commit: the accepted tokens extend the sequence (EAGLE-1 explainer,
+ *     "Verification"), so the accepted path's draft K/V are written at the
+ *     next cache positions; tokens not kept map to slot -1 (P-EAGLE page, "KV
+ *     cache and CUDA graphs");
  *   - acceptance: draft tokens are accepted by comparing draft and target
  *     distributions, the rest discarded after a rejection and a token
  *     resampled, leaving the target distribution unchanged (EAGLE-1 explainer,
@@ -428,32 +432,34 @@ typedef struct {
     double scale;     /* softmax scale (1/sqrt(d)) */
 } orc_attn_params;
 
+/* element index of key position t, kv head kvh, dimension e in the K cache
+   ([..][t][e]) and in the V cache (stored transposed, [..][e][t]) */
+static int64_t k_idx(const orc_attn_params *a, const int *block_table, int b, int kvh, int t, int e)
+{
+    int d = a->head_dim, Hkv = a->num_kv_heads;
+    if (a->block_size == 0) return (((int64_t)b * Hkv + kvh) * a->max_prefix + t) * d + e;
+    int blk = block_table[(size_t)b * a->max_blocks + t / a->block_size];
+    return (((int64_t)blk * Hkv + kvh) * a->block_size + t % a->block_size) * d + e;
+}
+
+static int64_t v_idx(const orc_attn_params *a, const int *block_table, int b, int kvh, int t, int e)
+{
+    int d = a->head_dim, Hkv = a->num_kv_heads;
+    if (a->block_size == 0) return (((int64_t)b * Hkv + kvh) * d + e) * a->max_prefix + t;
+    int blk = block_table[(size_t)b * a->max_blocks + t / a->block_size];
+    return (((int64_t)blk * Hkv + kvh) * d + e) * a->block_size + t % a->block_size;
+}
+
 static double kelem(const orc_attn_params *a, const void *k_cache, const int *block_table,
                     int b, int kvh, int t, int e)
 {
-    int d = a->head_dim, Hkv = a->num_kv_heads;
-    int64_t idx;
-    if (a->block_size == 0) {
-        idx = (((int64_t)b * Hkv + kvh) * a->max_prefix + t) * d + e;
-    } else {
-        int blk = block_table[(size_t)b * a->max_blocks + t / a->block_size];
-        idx = (((int64_t)blk * Hkv + kvh) * a->block_size + t % a->block_size) * d + e;
-    }
-    return (double)elem_f32(k_cache, a->dtype, idx);
+    return (double)elem_f32(k_cache, a->dtype, k_idx(a, block_table, b, kvh, t, e));
 }
 
 static double velem(const orc_attn_params *a, const void *v_cache, const int *block_table,
                     int b, int kvh, int t, int e)
 {
-    int d = a->head_dim, Hkv = a->num_kv_heads;
-    int64_t idx;
-    if (a->block_size == 0) {
-        idx = (((int64_t)b * Hkv + kvh) * d + e) * a->max_prefix + t;
-    } else {
-        int blk = block_table[(size_t)b * a->max_blocks + t / a->block_size];
-        idx = (((int64_t)blk * Hkv + kvh) * d + e) * a->block_size + t % a->block_size;
-    }
-    return (double)elem_f32(v_cache, a->dtype, idx);
+    return (double)elem_f32(v_cache, a->dtype, v_idx(a, block_table, b, kvh, t, e));
 }
 
 /* Output row for (b, i, h): softmax over prefix keys and ancestor-or-self draft keys. */
@@ -531,6 +537,74 @@ int orc_tree_attn(const orc_attn_params *a, int batch, const void *q, const void
             continue;
         }
         attn_row(a, q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, anc, b, i, h, o);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* KV commit                                                            */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The accepted tokens extend the sequence (EAGLE-1 explainer, "Verification"),
+ * so the j-th accepted node of sequence b is the token at position
+ * L + j (L = prefix_len[b]) and its draft K/V rows, every kv head, are stored
+ * in the cache at that position; nodes that are not kept map to slot -1 and
+ * nothing is written for them (P-EAGLE page, "KV cache and CUDA graphs").
+ * cap = positions a sequence may hold.  A sequence stops at the first node id
+ * outside [0, m_max) (flags[0]) or the first position >= cap or on a page id
+ * < 0 (flags[1]); L outside [0, cap] commits nothing and keeps L (flags[1]);
+ * accept_len outside [0, min(max_accept, m_max)] is clamped (flags[0]).
+ * flags count these events.  slot_mapping [B][m_max]: the slot (contiguous:
+ * position; paged: page * block_size + offset) of each committed node, else -1.
+ */
+int orc_kv_commit(const orc_attn_params *a, int cap, int batch, const void *k_draft, const void *v_draft,
+                  const int *accepted, const int *accept_len, int max_accept, const int *prefix_len,
+                  void *k_cache, void *v_cache, const int *block_table, int *slot_mapping,
+                  int *prefix_len_out, int *flags)
+{
+    if (!a || batch < 0 || max_accept < 1 || a->m_max < 1 || a->m_max > 64) return ORC_ERR_ARG;
+    const size_t esz = a->dtype == 0 ? 4 : 2;
+    const int M = a->m_max, H = a->num_kv_heads, d = a->head_dim, bs = a->block_size;
+    const int amax = max_accept < M ? max_accept : M;
+    flags[0] = flags[1] = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int L = prefix_len[b];
+        int A = accept_len[b];
+        if (A < 0 || A > amax) {
+            A = A < 0 ? 0 : amax;
+            flags[0]++;
+        }
+        for (int i = 0; i < M; ++i) slot_mapping[(size_t)b * M + i] = -1;
+        if (L < 0 || L > cap) {
+            flags[1]++;
+            prefix_len_out[b] = L;
+            continue;
+        }
+        int n = 0;
+        for (int j = 0; j < A; ++j) {
+            const int node = accepted[(size_t)b * max_accept + j];
+            if (node < 0 || node >= M) { flags[0]++; break; }
+            const int pos = L + j;
+            if (pos >= cap) { flags[1]++; break; }
+            int slot = pos;
+            if (bs > 0) {
+                const int page = block_table[(size_t)b * a->max_blocks + pos / bs];
+                if (page < 0) { flags[1]++; break; }
+                slot = page * bs + pos % bs;
+            }
+            for (int h = 0; h < H; ++h)
+                for (int e = 0; e < d; ++e) {
+                    const int64_t src = (((int64_t)b * M + node) * H + h) * d + e;
+                    memcpy((char *)k_cache + k_idx(a, block_table, b, h, pos, e) * esz,
+                           (const char *)k_draft + src * esz, esz);
+                    memcpy((char *)v_cache + v_idx(a, block_table, b, h, pos, e) * esz,
+                           (const char *)v_draft + src * esz, esz);
+                }
+            slot_mapping[(size_t)b * M + node] = slot;
+            ++n;
+        }
+        prefix_len_out[b] = L + n;
     }
     return ORC_OK;
 }

@@ -110,6 +110,26 @@ def test_tree_attn_rejects_missing_table_misalignment_and_workspace():
     assert E.lib().eagle_tree_attn_workspace_size(C.byref(_attn()), 2) >= 256
 
 
+def _call_commit(a, max_accept=6, bt=True, align=0, null_slot=False, ws=1 << 21, wsb=256):
+    L = E.lib()
+    p = C.c_void_p(1 << 24)
+    kd = C.c_void_p((1 << 24) + align)
+    return L.eagle_kv_commit(C.byref(a), 2, kd, p, p, p, max_accept, p, p, p,
+                             C.c_void_p(1 << 22) if bt else None, None if null_slot else p, p,
+                             C.c_void_p(ws), wsb, None)
+
+
+def test_kv_commit_rejects_bad_params():
+    assert _call_commit(_attn(num_q_heads=30)) == E.EAGLE_ERR_INVALID
+    assert _call_commit(_attn(head_dim=64)) == E.EAGLE_ERR_UNSUPPORTED
+    assert _call_commit(_attn(), max_accept=0) == E.EAGLE_ERR_INVALID
+    assert _call_commit(_attn(), bt=False) == E.EAGLE_ERR_INVALID
+    assert _call_commit(_attn(), null_slot=True) == E.EAGLE_ERR_INVALID
+    assert _call_commit(_attn(), align=4) == E.EAGLE_ERR_UNSUPPORTED
+    assert _call_commit(_attn(), wsb=8) == E.EAGLE_ERR_WORKSPACE
+    assert _call_commit(_attn(), ws=(1 << 21) + 16) == E.EAGLE_ERR_WORKSPACE
+
+
 def test_accept_and_mask_reject_bad_params():
     L = E.lib()
     p = C.c_void_p(1 << 24)
@@ -135,6 +155,8 @@ def test_zero_batch_launches_nothing():
     out = C.c_void_p(1 << 24)
     assert L.eagle_build_tree(C.byref(p), 0, out, 1, 32000, None, out, out, out, out, out, out,
                               C.c_void_p(1 << 21), 1 << 20, None) == E.EAGLE_OK
+    assert L.eagle_kv_commit(C.byref(_attn()), 0, out, out, out, out, 6, out, out, out, out, out, out,
+                             C.c_void_p(1 << 21), 256, None) == E.EAGLE_OK
 
 
 def test_logit_rows_marshalling():
