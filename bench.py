@@ -276,6 +276,9 @@ def main():
     torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - tw0) * 1e3 / K
 
+    commit = measure_commit(E, step, w, sets[0], kinds, K)
+    log(f"[bench] kv commit {commit['avg_us']:.2f} us/call for {commit['tokens']} tokens")
+
     errs = step.errors()
     if errs:
         log(f"[bench] WARNING: device error bits {errs:#x}")
@@ -332,6 +335,7 @@ def main():
                      "tflops": round(tflops, 2), "mfma_frac": round(mfma_frac, 4)},
         "cpu_baseline": cpu,
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "kv_commit": commit,
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
         "launch": "hipGraph replay per step" if graphs is not None else "eager",
         "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
@@ -340,6 +344,52 @@ def main():
         "device_errors": errs,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_commit(E, step, w, S, kinds, reps):
+    """eagle_kv_commit of input set 0's accepted paths, outside the step: one
+    call per replay of a graph of 20 calls, HIP events around the replays.
+    The paths are written into a scratch cache of the same layout at
+    positions max(prefix_len - max_accept, 0), which lie on assigned pages."""
+    import torch
+    a = S["attn"]
+    step.run(S["draft"], kinds, a.prefix_len, a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table,
+             S["target"], S["words"])
+    kc, vc = torch.empty_like(a.k_cache), torch.empty_like(a.v_cache)
+    plen = (a.prefix_len - w.max_accept).clamp(min=0).to(torch.int32)
+    plo = torch.empty_like(plen)
+
+    def call():
+        E.kv_commit(step.attn, w.batch, a.k_draft, a.v_draft, step.accepted, step.accept_len, plen, kc, vc,
+                    a.block_table, step.slot_mapping, plo, step.ws_commit)
+
+    per_graph = 20
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            call()
+    g.replay()
+    n = max(1, reps // per_graph)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ea.record()
+    for _ in range(n):
+        g.replay()
+    eb.record()
+    torch.cuda.synchronize()
+    us = ea.elapsed_time(eb) * 1e3 / (n * per_graph)
+    tokens = int(step.accept_len.sum().item())
+    esz = 4 if w.dtype == torch.float32 else 2
+    nbytes = tokens * w.num_kv_heads * w.head_dim * esz * 4   # K and V rows read, then written
+    assert torch.equal(plo, plen + step.accept_len), "kv commit did not write every accepted token"
+    return {"call": "eagle_kv_commit (k_kv_commit)", "avg_us": round(us, 2), "timed_calls": n * per_graph,
+            "tokens": tokens, "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(w, S, seed, tokens_per_step, budget_s):
