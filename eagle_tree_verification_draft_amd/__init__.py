@@ -32,6 +32,7 @@ DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 
 EXPORTS = (
     "eagle_workspace_init", "eagle_read_errors",
     "eagle_build_tree_workspace_size", "eagle_build_tree",
+    "eagle_tree_expand", "eagle_tree_finish",
     "eagle_tree_mask",
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
     "eagle_kv_commit",
@@ -79,6 +80,8 @@ def lib() -> C.CDLL:
         L.eagle_build_tree_workspace_size.restype = sz
         L.eagle_build_tree.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp,
                                        vp, sz, vp]
+        L.eagle_tree_expand.argtypes = [C.POINTER(TreeParams), i32, i32, vp, C.c_int, i64, vp, vp, vp, vp, sz, vp]
+        L.eagle_tree_finish.argtypes = [C.POINTER(TreeParams), i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_attn_workspace_size.argtypes = [C.POINTER(AttnParams), i32]
         L.eagle_tree_attn_workspace_size.restype = sz
@@ -93,8 +96,8 @@ def lib() -> C.CDLL:
         L.eagle_status_string.restype = C.c_char_p
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
-        for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_tree_mask",
-                  "eagle_tree_attn", "eagle_kv_commit", "eagle_accept"):
+        for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_tree_expand",
+                  "eagle_tree_finish", "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit", "eagle_accept"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -168,6 +171,24 @@ def build_tree(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind: Opti
                                   _ptr(score), _ptr(src_row), _ptr(num_nodes), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_build_tree")
+
+
+def tree_expand(p: TreeParams, batch: int, level: int, level_logits: torch.Tensor, frontier_tokens,
+                frontier_parent, frontier_score, workspace: torch.Tensor, stream=None):
+    """One level of draft rows ([batch][1 or topk][V]); writes the next frontier."""
+    rows, stride = _rows(level_logits)
+    _check(lib().eagle_tree_expand(C.byref(p), batch, level, rows, dtype_code(level_logits.dtype), stride,
+                                   _ptr(frontier_tokens), _ptr(frontier_parent), _ptr(frontier_score),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_tree_expand")
+
+
+def tree_finish(p: TreeParams, batch: int, tokens, parent, depth, score, src_row, num_nodes,
+                workspace: torch.Tensor, stream=None):
+    _check(lib().eagle_tree_finish(C.byref(p), batch, _ptr(tokens), _ptr(parent), _ptr(depth), _ptr(score),
+                                   _ptr(src_row), _ptr(num_nodes), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_tree_finish")
 
 
 def tree_mask(batch: int, m_max: int, parent, num_nodes, prefix_len, anc_mask, pos,

@@ -123,14 +123,15 @@ __global__ __launch_bounds__(1024) void k_row_stats(RowStatsArgs a)
 {
     constexpr int VEC = Vec<T>::n;
     __shared__ RowStatsSmem sm;
-    const int r_all = blockIdx.x;
-    const int b = r_all / a.r_max, r = r_all % a.r_max;
+    const int g = blockIdx.x;   // input row; its statistics go to slot r_all
+    const int b = g / a.rows_in, r = a.row_base + g % a.rows_in;
+    const size_t r_all = (size_t)b * a.r_max + r;
     const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
     const int rows_needed = kind == EAGLE_TREE_CHAIN ? a.chain_k : a.rows_dyn;
     if (r >= rows_needed) return;
     const int C = kind == EAGLE_TREE_CHAIN ? 1 : a.children;
     const int V = a.vocab, NT = blockDim.x, tid = threadIdx.x;
-    const T *row = static_cast<const T *>(a.logits) + (size_t)r_all * (size_t)a.row_stride;
+    const T *row = static_cast<const T *>(a.logits) + (size_t)g * (size_t)a.row_stride;
 
     uint4 x[kNV];
 #pragma unroll
@@ -206,14 +207,15 @@ __global__ __launch_bounds__(1024) void k_row_stats_stream(RowStatsArgs a)
 {
     constexpr int VEC = Vec<T>::n;
     __shared__ RowStatsSmem sm;
-    const int r_all = blockIdx.x;
-    const int b = r_all / a.r_max, r = r_all % a.r_max;
+    const int g = blockIdx.x;   // input row; its statistics go to slot r_all
+    const int b = g / a.rows_in, r = a.row_base + g % a.rows_in;
+    const size_t r_all = (size_t)b * a.r_max + r;
     const int kind = a.kind ? a.kind[b] : EAGLE_TREE_DYNAMIC;
     const int rows_needed = kind == EAGLE_TREE_CHAIN ? a.chain_k : a.rows_dyn;
     if (r >= rows_needed) return;
     const int C = kind == EAGLE_TREE_CHAIN ? 1 : a.children;
     const int V = a.vocab, NT = blockDim.x, tid = threadIdx.x;
-    const T *row = static_cast<const T *>(a.logits) + (size_t)r_all * (size_t)a.row_stride;
+    const T *row = static_cast<const T *>(a.logits) + (size_t)g * (size_t)a.row_stride;
     const int nvec = (V + VEC - 1) / VEC;
 
     float lmax = -__builtin_inff();
@@ -330,6 +332,18 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
     int32_t *tokens = a.tokens + (size_t)b * m_max, *parent = a.parent + (size_t)b * m_max;
     int32_t *depth = a.depth + (size_t)b * m_max, *src_row = a.src_row + (size_t)b * m_max;
     double *score = a.score + (size_t)b * m_max;
+
+    if (a.levels && a.levels[b] != a.depth_max) {
+        // incremental build with levels missing: an empty tree
+        if (tid == 0) {
+            raise_error(a.err, EAGLE_DEVERR_TREE);
+            a.num_nodes[b] = 0;
+        }
+        for (int i = tid; i < m_max; i += NT) {
+            tokens[i] = -1; parent[i] = -1; depth[i] = -1; score[i] = 0.0; src_row[i] = -1;
+        }
+        return;
+    }
 
     if (kind == EAGLE_TREE_CHAIN) {
         const int K = a.chain_k;
@@ -515,6 +529,69 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Incremental build (the draft runs one forward per depth): level 0 brings
+// the root's row, level l >= 1 the rows of the k nodes expanded at depth l, in
+// expansion order (rows 1 + (l - 1) k + p).  After the level's row
+// statistics, k_tree_frontier forms the V of the level's children (depth
+// l + 1) exactly as k_tree_select does, ranks them by (V desc, creation asc)
+// and writes the first k: the nodes whose rows the next level brings.  Once
+// every level is in, k_tree_select builds the tree from the statistics of all
+// levels, so the tree equals the one-shot build's over the same rows.
+// ---------------------------------------------------------------------------
+constexpr int kFrontierThreads = 256;
+
+__global__ __launch_bounds__(kFrontierThreads) void k_tree_frontier(FrontierArgs a)
+{
+    __shared__ double V[kMaxTopk * kMaxChildren];
+    __shared__ int in_order;
+    const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x;
+    const int C = a.children, k = a.topk, lv = a.level;
+    const size_t rb = (size_t)b * a.r_max;
+    int32_t *f_tok = a.f_tok + (size_t)b * k, *f_par = a.f_par + (size_t)b * k;
+    double *f_score = a.f_score + (size_t)b * k;
+    double *fV = a.fV + (size_t)b * kMaxTopk;
+    if (tid == 0) {
+        in_order = lv == 0 || a.levels[b] == lv;
+        if (!in_order) raise_error(a.err, EAGLE_DEVERR_TREE);
+    }
+    for (int i = tid; i < k; i += NT) {
+        f_tok[i] = -1; f_par[i] = -1; f_score[i] = 0.0;
+    }
+    __syncthreads();
+    if (!in_order) return;
+    // the level's children in creation order: (parent p, child j)
+    const int n = (lv == 0 ? 1 : a.fn[b]) * C;
+    for (int x = tid; x < n; x += NT) {
+        const int p = x / C, j = x - p * C;
+        const size_t r = rb + (lv == 0 ? 0 : 1 + (size_t)(lv - 1) * k + p);
+        const float M = a.M[r];
+        const double W = a.W[r];
+        const double c = (double)weight_of(a.top_v[r * C + j], M) / W;
+        V[x] = lv == 0 ? c : fV[p] * c;
+        if (j == 0 && (!__builtin_isfinite(M) || !__builtin_isfinite(W))) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+    }
+    __syncthreads();   // fV is read: it may now be overwritten
+    const int ne = lv + 1 < a.depth_max ? min(k, n) : 0;   // depth D is not expanded
+    for (int x = tid; x < n; x += NT) {
+        const double vx = V[x];
+        int rk = 0;
+        for (int y = 0; y < n; ++y) rk += (V[y] > vx || (V[y] == vx && y < x)) ? 1 : 0;
+        if (rk < ne) {
+            const int p = x / C, j = x - p * C;
+            const size_t r = rb + (lv == 0 ? 0 : 1 + (size_t)(lv - 1) * k + p);
+            f_tok[rk] = a.top_id[r * C + j];
+            f_par[rk] = lv == 0 ? -1 : p;
+            f_score[rk] = vx;
+            fV[rk] = vx;
+        }
+    }
+    if (tid == 0) {
+        a.fn[b] = ne;
+        a.levels[b] = lv + 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
@@ -526,6 +603,9 @@ BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
     L.off_W = o;      o = align_up(o + rows * sizeof(double), 256);
     L.off_id = o;     o = align_up(o + rows * p->children * sizeof(int32_t), 256);
     L.off_v = o;      o = align_up(o + rows * p->children * sizeof(float), 256);
+    L.off_fV = o;     o = align_up(o + (size_t)batch * kMaxTopk * sizeof(double), 256);
+    L.off_fn = o;     o = align_up(o + (size_t)batch * sizeof(int32_t), 256);
+    L.off_lv = o;     o = align_up(o + (size_t)batch * sizeof(int32_t), 256);
     L.total = o;
     return L;
 }
@@ -552,22 +632,55 @@ int row_threads(int vocab, int vec)
     return (int)(nt < 64 ? 64 : (nt > 1024 ? 1024 : nt));
 }
 
-hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const void *logits,
-                             eagle_dtype dt, int64_t row_stride, const int32_t *kind,
-                             int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
-                             int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st)
+// row statistics of ra.rows input rows (register or streaming form)
+static hipError_t launch_row_stats(const RowStatsArgs &ra, eagle_dtype dt, hipStream_t st)
 {
-    const BuildLayout L = build_layout(p, batch);
+    if (ra.rows <= 0) return hipSuccess;
+    const int vec = dt == EAGLE_F32 ? 4 : 8;
+    const int nv = row_vectors(ra.vocab, vec);
+    const int nt = row_threads(ra.vocab, vec);
+    // registers for few rows (each row's latency is the step's), streaming
+    // for many rows (workgroups overlap) and for rows too long for registers
+    if (nv == 0 || ra.rows > kRegisterRowsMax) {
+#define EAGLE_STREAM(T) hipLaunchKernelGGL((k_row_stats_stream<T>), dim3((unsigned)ra.rows), dim3(1024), 0, st, ra)
+        if (dt == EAGLE_F32) EAGLE_STREAM(float);
+        else EAGLE_STREAM(uint16_t);
+#undef EAGLE_STREAM
+    } else {
+        const dim3 g1((unsigned)ra.rows);
+#define EAGLE_ROWS(T, NV) hipLaunchKernelGGL((k_row_stats<T, NV>), g1, dim3(nt), 0, st, ra)
+        if (dt == EAGLE_F32) {
+            if (nv == 1) EAGLE_ROWS(float, 1);
+            else if (nv == 2) EAGLE_ROWS(float, 2);
+            else if (nv == 4) EAGLE_ROWS(float, 4);
+            else EAGLE_ROWS(float, 8);
+        } else {
+            if (nv == 1) EAGLE_ROWS(uint16_t, 1);
+            else if (nv == 2) EAGLE_ROWS(uint16_t, 2);
+            else if (nv == 4) EAGLE_ROWS(uint16_t, 4);
+            else EAGLE_ROWS(uint16_t, 8);
+        }
+#undef EAGLE_ROWS
+    }
+    return hipGetLastError();
+}
+
+static RowStatsArgs row_stats_args(const eagle_tree_params *p, int32_t batch, const BuildLayout &L, void *ws,
+                                   const void *logits, eagle_dtype dt, int64_t row_stride, const int32_t *kind,
+                                   int rows_in, int row_base)
+{
     char *base = static_cast<char *>(ws);
     RowStatsArgs ra;
     ra.logits = logits;
     ra.row_stride = row_stride;
-    ra.rows = batch * p->r_max;
+    ra.rows = batch * rows_in;
     ra.r_max = p->r_max;
     ra.vocab = p->vocab;
     ra.children = p->children;
     ra.chain_k = p->chain_k;
     ra.rows_dyn = 1 + (p->depth - 1) * p->topk;
+    ra.rows_in = rows_in;
+    ra.row_base = row_base;
     ra.kind = kind;
     ra.M = reinterpret_cast<float *>(base + L.off_M);
     ra.W = reinterpret_cast<double *>(base + L.off_W);
@@ -576,36 +689,14 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ra.err = reinterpret_cast<uint32_t *>(base);
     const size_t esz = dt == EAGLE_F32 ? 4 : 2;
     ra.vec_ok = ((uintptr_t)logits % 16 == 0) && ((size_t)row_stride * esz % 16 == 0);
-    const int vec = dt == EAGLE_F32 ? 4 : 8;
-    const int nv = row_vectors(p->vocab, vec);
-    const int nt = row_threads(p->vocab, vec);
-    if (ra.rows > 0) {
-        // registers for few rows (each row's latency is the step's), streaming
-        // for many rows (workgroups overlap) and for rows too long for registers
-        if (nv == 0 || ra.rows > kRegisterRowsMax) {
-#define EAGLE_STREAM(T) hipLaunchKernelGGL((k_row_stats_stream<T>), dim3((unsigned)ra.rows), dim3(1024), 0, st, ra)
-            if (dt == EAGLE_F32) EAGLE_STREAM(float);
-            else EAGLE_STREAM(uint16_t);
-#undef EAGLE_STREAM
-        } else {
-            const dim3 g1((unsigned)ra.rows);
-#define EAGLE_ROWS(T, NV) hipLaunchKernelGGL((k_row_stats<T, NV>), g1, dim3(nt), 0, st, ra)
-            if (dt == EAGLE_F32) {
-                if (nv == 1) EAGLE_ROWS(float, 1);
-                else if (nv == 2) EAGLE_ROWS(float, 2);
-                else if (nv == 4) EAGLE_ROWS(float, 4);
-                else EAGLE_ROWS(float, 8);
-            } else {
-                if (nv == 1) EAGLE_ROWS(uint16_t, 1);
-                else if (nv == 2) EAGLE_ROWS(uint16_t, 2);
-                else if (nv == 4) EAGLE_ROWS(uint16_t, 4);
-                else EAGLE_ROWS(uint16_t, 8);
-            }
-#undef EAGLE_ROWS
-        }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    return ra;
+}
+
+static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const RowStatsArgs &ra,
+                                const int32_t *kind, const int32_t *levels, int32_t *tokens, int32_t *parent,
+                                int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                                hipStream_t st)
+{
     TreeSelectArgs ta;
     ta.kind = kind;
     ta.depth_max = p->depth;
@@ -625,12 +716,65 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     ta.score = score;
     ta.src_row = src_row;
     ta.num_nodes = num_nodes;
+    ta.levels = levels;
     ta.err = ra.err;
-    if (batch > 0) {
-        hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(1024), 0, st, ta);
-        return hipGetLastError();
-    }
-    return hipSuccess;
+    if (batch <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(1024), 0, st, ta);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const void *logits,
+                             eagle_dtype dt, int64_t row_stride, const int32_t *kind,
+                             int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                             int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    const RowStatsArgs ra = row_stats_args(p, batch, L, ws, logits, dt, row_stride, kind, p->r_max, 0);
+    hipError_t e = launch_row_stats(ra, dt, st);
+    if (e != hipSuccess) return e;
+    return launch_select(p, batch, ra, kind, nullptr, tokens, parent, depth, score, src_row, num_nodes, st);
+}
+
+hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level, const void *logits,
+                              eagle_dtype dt, int64_t row_stride, int32_t *f_tok, int32_t *f_par,
+                              double *f_score, void *ws, hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    const int rows_in = level == 0 ? 1 : p->topk;
+    const int row_base = level == 0 ? 0 : 1 + (level - 1) * p->topk;
+    const RowStatsArgs ra = row_stats_args(p, batch, L, ws, logits, dt, row_stride, nullptr, rows_in, row_base);
+    hipError_t e = launch_row_stats(ra, dt, st);
+    if (e != hipSuccess) return e;
+    char *base = static_cast<char *>(ws);
+    FrontierArgs fa;
+    fa.level = level;
+    fa.depth_max = p->depth;
+    fa.topk = p->topk;
+    fa.children = p->children;
+    fa.r_max = p->r_max;
+    fa.M = ra.M;
+    fa.W = ra.W;
+    fa.top_id = ra.top_id;
+    fa.top_v = ra.top_v;
+    fa.fV = reinterpret_cast<double *>(base + L.off_fV);
+    fa.fn = reinterpret_cast<int32_t *>(base + L.off_fn);
+    fa.levels = reinterpret_cast<int32_t *>(base + L.off_lv);
+    fa.f_tok = f_tok;
+    fa.f_par = f_par;
+    fa.f_score = f_score;
+    fa.err = ra.err;
+    hipLaunchKernelGGL(k_tree_frontier, dim3((unsigned)batch), dim3(kFrontierThreads), 0, st, fa);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_finish(const eagle_tree_params *p, int32_t batch, int32_t *tokens, int32_t *parent,
+                              int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes, void *ws,
+                              hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    const RowStatsArgs ra = row_stats_args(p, batch, L, ws, nullptr, EAGLE_BF16, p->vocab, nullptr, 0, 0);
+    const int32_t *levels = reinterpret_cast<const int32_t *>(static_cast<char *>(ws) + L.off_lv);
+    return launch_select(p, batch, ra, nullptr, levels, tokens, parent, depth, score, src_row, num_nodes, st);
 }
 
 }  // namespace eagle

@@ -131,6 +131,42 @@ eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const v
                       "build_tree launch");
 }
 
+eagle_status eagle_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level,
+                               const void *level_logits, eagle_dtype dtype, int64_t row_stride,
+                               int32_t *frontier_tokens, int32_t *frontier_parent, double *frontier_score,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    eagle_status s = check_tree_params(p, batch);
+    if (s != EAGLE_OK) return s;
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (level < 0 || level >= p->depth) return fail(EAGLE_ERR_INVALID, "level %d not in [0, depth %d)", level, p->depth);
+    if (!level_logits || !frontier_tokens || !frontier_parent || !frontier_score)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
+    s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_tree_expand(p, batch, level, level_logits, dtype, row_stride, frontier_tokens,
+                                         frontier_parent, frontier_score, workspace, (hipStream_t)stream),
+                      "tree_expand launch");
+}
+
+eagle_status eagle_tree_finish(const eagle_tree_params *p, int32_t batch, int32_t *tokens, int32_t *parent,
+                               int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    eagle_status s = check_tree_params(p, batch);
+    if (s != EAGLE_OK) return s;
+    if (!tokens || !parent || !depth || !score || !src_row || !num_nodes)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_tree_finish(p, batch, tokens, parent, depth, score, src_row, num_nodes, workspace,
+                                         (hipStream_t)stream),
+                      "tree_finish launch");
+}
+
 eagle_status eagle_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent,
                              const int32_t *num_nodes, const int32_t *prefix_len,
                              uint64_t *anc_mask, int32_t *pos, void *workspace,

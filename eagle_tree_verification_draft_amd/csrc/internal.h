@@ -20,6 +20,7 @@ struct RowStatsArgs {
     const void *logits;
     int64_t row_stride;
     int rows, r_max, vocab, children, chain_k, rows_dyn;
+    int rows_in, row_base;   // input rows per sequence; slot of the first (r_max, 0: all rows)
     const int32_t *kind;
     float *M;          // row max
     double *W;         // exact row weight sum
@@ -39,11 +40,29 @@ struct TreeSelectArgs {
     int32_t *tokens, *parent, *depth;
     double *score;
     int32_t *src_row, *num_nodes;
+    const int32_t *levels;   // incremental build: levels given per sequence (NULL: one-shot)
+    uint32_t *err;
+};
+
+// incremental build: one level of draft rows at a time
+struct FrontierArgs {
+    int level, depth_max, topk, children, r_max;
+    const float *M;
+    const double *W;
+    const int32_t *top_id;
+    const float *top_v;
+    double *fV;        // [batch][kMaxTopk] V of the current frontier
+    int32_t *fn;       // [batch] its size
+    int32_t *levels;   // [batch] levels given so far
+    int32_t *f_tok, *f_par;
+    double *f_score;   // outputs [batch][topk]
     uint32_t *err;
 };
 
 struct BuildLayout {
-    size_t off_M, off_W, off_id, off_v, total;
+    size_t off_M, off_W, off_id, off_v;
+    size_t off_fV, off_fn, off_lv;   // incremental-build state
+    size_t total;
 };
 BuildLayout build_layout(const eagle_tree_params *p, int32_t batch);
 int row_vectors(int vocab, int vec);
@@ -53,6 +72,13 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
                              eagle_dtype dt, int64_t row_stride, const int32_t *kind,
                              int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
                              int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st);
+
+hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level, const void *logits,
+                              eagle_dtype dt, int64_t row_stride, int32_t *f_tok, int32_t *f_par,
+                              double *f_score, void *ws, hipStream_t st);
+hipError_t launch_tree_finish(const eagle_tree_params *p, int32_t batch, int32_t *tokens, int32_t *parent,
+                              int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes, void *ws,
+                              hipStream_t st);
 
 // ---- mask ----------------------------------------------------------------
 hipError_t launch_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent,

@@ -1,6 +1,6 @@
 // kv_commit.hip -- the accepted path's draft K/V written into the KV cache
 // (EAGLE-1 explainer, "Verification": the accepted tokens extend the sequence;
-// P-EAGLE page, "KV cache and CUDA graphs": tokens not kept map to the padding
+// P-EAGLE in vLLM, "KV cache and CUDA graphs": tokens not kept map to the padding
 // slot -1).  One workgroup per sequence: the j-th accepted node goes to
 // position prefix_len + j in every kv head.  Wave 0 resolves the node ids and
 // cache slots of all accepted tokens at once (one lane each) and finds the

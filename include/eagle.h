@@ -128,6 +128,50 @@ eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const v
                               size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
+/* Incremental tree build                                              */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (EAGLE-2 explainer, "Dynamic draft tree construction": per depth,
+ * the top-k nodes by V are expanded and the draft runs on them; EAGLE-1
+ * explainer, "Draft generation flow": one draft forward per step).  The same tree
+ * as eagle_build_tree, with the draft rows given one level at a time, so a
+ * draft forward can run between the calls on the nodes chosen so far:
+ *   level 0:      level_logits [batch][1][row_stride], the root's row (row 0);
+ *   level l >= 1: level_logits [batch][topk][row_stride], the rows of the
+ *                 frontier that level l - 1 returned, in frontier order
+ *                 (row 1 + (l - 1) * topk + p of the one-shot layout);
+ *                 rows past the frontier's size (when a depth has fewer
+ *                 than topk nodes) do not change the tree, but they are
+ *                 read and checked as eagle_build_tree checks every row, so
+ *                 they must be finite (zeros will do).
+ * Each call returns the next frontier: the top-k nodes of depth l + 1 by
+ * (V desc, creation index asc) -- the nodes whose draft rows level l + 1
+ * brings -- as frontier_tokens / frontier_parent / frontier_score
+ * [batch][topk]: the token, the index of its parent in the previous
+ * frontier (-1 at level 0: the root), and its V.  Entries past the frontier's
+ * size, and the whole frontier at the last level (depth - 1), are -1 / -1 / 0.
+ * eagle_tree_finish then writes the tree exactly as eagle_build_tree over the
+ * same rows would (dynamic trees; chains are drafted in one pass and use
+ * eagle_build_tree).  One workspace (eagle_build_tree_workspace_size, zeroed
+ * by eagle_workspace_init before first use) carries the state across the
+ * calls of a tree; level 0 starts a new tree.
+ * Device errors: EAGLE_DEVERR_TREE when a level comes out of order (that
+ * call writes an empty frontier) or eagle_tree_finish runs before every level
+ * is in (that sequence gets an empty tree, num_nodes 0); NONFINITE_ROW as in
+ * eagle_build_tree.
+ * Errors: those of eagle_build_tree; EAGLE_ERR_INVALID for a level outside
+ * [0, depth).
+ */
+eagle_status eagle_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level,
+                               const void *level_logits, eagle_dtype dtype, int64_t row_stride,
+                               int32_t *frontier_tokens, int32_t *frontier_parent, double *frontier_score,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+eagle_status eagle_tree_finish(const eagle_tree_params *p, int32_t batch, int32_t *tokens, int32_t *parent,
+                               int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* Ancestor mask                                                       */
 /* ------------------------------------------------------------------ */
 /*
@@ -202,7 +246,7 @@ eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const vo
 /* ------------------------------------------------------------------ */
 /*
  * Defines (EAGLE-1 explainer, "Verification": the accepted tokens extend the
- * sequence; P-EAGLE page, "KV cache and CUDA graphs": tokens that are not
+ * sequence; P-EAGLE in vLLM, "KV cache and CUDA graphs": tokens that are not
  * kept map to the padding slot -1, so nothing is written for them).  For
  * sequence b with L = prefix_len[b] and A = accept_len[b]: the j-th accepted
  * node (node id accepted[b][j], j < A, root-first as eagle_accept writes

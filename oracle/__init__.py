@@ -145,6 +145,33 @@ def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_
     return out
 
 
+def tree_frontiers(draft_logits, depth, topk, children, m, m_max=None):
+    """The nodes expanded at each depth of the dynamic trees, as an incremental
+    build returns them level by level: level l's frontier is the expanded
+    nodes of depth l + 1 in expansion order (they own rows 1 + l * topk + p).
+    Returns tokens, parent (index in the previous frontier, -1 at level 0) and
+    score (V), each [depth][B][topk], padded with -1 / -1 / 0; the last level
+    is empty (depth `depth` is not expanded)."""
+    t = build_tree(draft_logits, depth, topk, children, m, m_max=m_max, debug=True)
+    cd = t["cand"]
+    B = cd["n"].shape[0]
+    tok = np.full((depth, B, topk), -1, np.int32)
+    par = np.full((depth, B, topk), -1, np.int32)
+    score = np.zeros((depth, B, topk), np.float64)
+    for b in range(B):
+        for g in range(int(cd["n"][b])):
+            r = int(cd["row"][b, g])
+            if r < 0:
+                continue
+            lv = int(cd["depth"][b, g]) - 1          # level whose call returns this node
+            p = r - 1 - lv * topk
+            tok[lv, b, p] = cd["token"][b, g]
+            score[lv, b, p] = cd["V"][b, g]
+            q = int(cd["parent"][b, g])
+            par[lv, b, p] = -1 if q < 0 else int(cd["row"][b, q]) - 1 - (lv - 1) * topk
+    return tok, par, score
+
+
 def tree_mask(parent, num_nodes, prefix_len):
     parent = np.ascontiguousarray(parent, dtype=np.int32)
     num_nodes = np.ascontiguousarray(num_nodes, dtype=np.int32)

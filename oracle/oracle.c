@@ -18,7 +18,7 @@
  *     one pass (EAGLE-1 explainer, "Role of Tree Attention");
  *   - KV commit: the accepted tokens extend the sequence (EAGLE-1 explainer,
  *     "Verification"), so the accepted path's draft K/V are written at the
- *     next cache positions; tokens not kept map to slot -1 (P-EAGLE page, "KV
+ *     next cache positions; tokens not kept map to slot -1 (P-EAGLE in vLLM, "KV
  *     cache and CUDA graphs");
  *   - acceptance: draft tokens are accepted by comparing draft and target
  *     distributions, the rest discarded after a rejection and a token
@@ -550,7 +550,7 @@ int orc_tree_attn(const orc_attn_params *a, int batch, const void *q, const void
  * so the j-th accepted node of sequence b is the token at position
  * L + j (L = prefix_len[b]) and its draft K/V rows, every kv head, are stored
  * in the cache at that position; nodes that are not kept map to slot -1 and
- * nothing is written for them (P-EAGLE page, "KV cache and CUDA graphs").
+ * nothing is written for them (P-EAGLE in vLLM, "KV cache and CUDA graphs").
  * cap = positions a sequence may hold.  A sequence stops at the first node id
  * outside [0, m_max) (flags[0]) or the first position >= cap or on a page id
  * < 0 (flags[1]); L outside [0, cap] commits nothing and keeps L (flags[1]);

@@ -130,6 +130,29 @@ def test_kv_commit_rejects_bad_params():
     assert _call_commit(_attn(), ws=(1 << 21) + 16) == E.EAGLE_ERR_WORKSPACE
 
 
+def test_tree_expand_and_finish_reject_bad_params():
+    L = E.lib()
+    p = _tree()
+    x = C.c_void_p(1 << 24)
+    ws = C.c_void_p(1 << 21)
+    need = L.eagle_build_tree_workspace_size(C.byref(p), 2)
+
+    def expand(level, params=p, ptr=x, stride=32000, wsb=need, dtype=E.EAGLE_BF16):
+        return L.eagle_tree_expand(C.byref(params), 2, level, x, dtype, stride, ptr, x, x, ws, wsb, None)
+
+    assert expand(-1) == E.EAGLE_ERR_INVALID
+    assert expand(6) == E.EAGLE_ERR_INVALID          # levels are 0 .. depth - 1
+    assert expand(0, ptr=None) == E.EAGLE_ERR_INVALID
+    assert expand(0, stride=100) == E.EAGLE_ERR_INVALID
+    assert expand(0, wsb=need - 256) == E.EAGLE_ERR_WORKSPACE
+    assert expand(0, dtype=7) == E.EAGLE_ERR_UNSUPPORTED
+    assert expand(0, params=_tree(children=17)) == E.EAGLE_ERR_UNSUPPORTED
+    assert L.eagle_tree_finish(C.byref(p), 2, x, x, x, None, x, x, ws, need, None) == E.EAGLE_ERR_INVALID
+    assert L.eagle_tree_finish(C.byref(p), 2, x, x, x, x, x, x, ws, 256, None) == E.EAGLE_ERR_WORKSPACE
+    assert L.eagle_tree_expand(C.byref(p), 0, 3, x, E.EAGLE_BF16, 32000, x, x, x, ws, need, None) == E.EAGLE_OK
+    assert L.eagle_tree_finish(C.byref(p), 0, x, x, x, x, x, x, ws, need, None) == E.EAGLE_OK
+
+
 def test_accept_and_mask_reject_bad_params():
     L = E.lib()
     p = C.c_void_p(1 << 24)

@@ -1,5 +1,5 @@
 """Pins for the oracle's KV commit (EAGLE-1 explainer, "Verification": the
-accepted tokens extend the sequence; P-EAGLE page, "KV cache and CUDA
+accepted tokens extend the sequence; P-EAGLE in vLLM, "KV cache and CUDA
 graphs": tokens that are not kept map to slot -1 and are not written).
 
 Pins:

@@ -267,3 +267,31 @@ def test_mask_is_ancestor_closure(orc):
                 assert pos[b, i] == -1
         if kinds[b] == 1:                                    # chain -> lower triangular
             assert [int(anc[b, i]) for i in range(7)] == [(1 << (i + 1)) - 1 for i in range(7)]
+
+
+@pytest.mark.parametrize("base,seed,B,k", [(1, 21, 2, 10), (2, 22, 1, 4), (3, 23, 2, 1)])
+def test_frontiers_follow_level_by_level_expansion(orc, base, seed, B, k):
+    """The oracle's per-depth expanded nodes (what an incremental build returns
+    after each level) equal a level-by-level restatement that sees only the
+    rows of the nodes chosen so far: level 0 ranks the root row's top-C by V
+    = w / W; level l ranks the children of level l - 1's frontier, in frontier
+    order, by V = V_parent * w / W and (V desc, creation asc)."""
+    w = synth.small_workload(base, batch=B, topk=k)
+    logits = _rows_np(w, seed)
+    D, C = w.depth, w.children
+    tok, par, score = orc.tree_frontiers(logits, D, k, C, w.m)
+    assert (tok[D - 1] == -1).all() and (par[D - 1] == -1).all()
+    for b in range(B):
+        front = [(1.0, None)]          # (V, row) of the nodes whose rows the next level brings
+        for lv in range(D - 1):
+            cands = []
+            for p, (vp, r) in enumerate(front):
+                M, W, ids, ws = spec_emul.row_stats(logits[b, 0 if lv == 0 else r], C)
+                for j in range(C):
+                    cands.append((vp * (ws[j] / W), len(cands), ids[j], -1 if lv == 0 else p))
+            top = sorted(cands, key=lambda c: (-c[0], c[1]))[:k]
+            assert [int(x) for x in tok[lv, b, :len(top)]] == [c[2] for c in top]
+            assert [int(x) for x in par[lv, b, :len(top)]] == [c[3] for c in top]
+            assert [float(x) for x in score[lv, b, :len(top)]] == [c[0] for c in top]
+            assert (tok[lv, b, len(top):] == -1).all()
+            front = [(c[0], 1 + lv * k + p) for p, c in enumerate(top)]
