@@ -278,6 +278,9 @@ def main():
 
     commit = measure_commit(E, step, w, sets[0], kinds, K)
     log(f"[bench] kv commit {commit['avg_us']:.2f} us/call for {commit['tokens']} tokens")
+    expand = measure_expand(E, step, w, sets[0], kinds, K)
+    if expand:
+        log(f"[bench] incremental build {expand['total_us']:.1f} us for {expand['levels']} levels + finish")
 
     errs = step.errors()
     if errs:
@@ -336,6 +339,7 @@ def main():
         "cpu_baseline": cpu,
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "kv_commit": commit,
+        "tree_expand": expand,
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
         "launch": "hipGraph replay per step" if graphs is not None else "eager",
         "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
@@ -390,6 +394,75 @@ def measure_commit(E, step, w, S, kinds, reps):
     assert torch.equal(plo, plen + step.accept_len), "kv commit did not write every accepted token"
     return {"call": "eagle_kv_commit (k_kv_commit)", "avg_us": round(us, 2), "timed_calls": n * per_graph,
             "tokens": tokens, "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def measure_expand(E, step, w, S, kinds, reps):
+    """The incremental build (eagle_tree_expand per level, then
+    eagle_tree_finish) over input set 0's draft rows, outside the step: HIP
+    events around replays of a graph of one whole build; per-level figures
+    from event-timed eager calls.  Dynamic trees only (None otherwise)."""
+    import numpy as np
+    import torch
+
+    import synth
+    if any(kd != synth.TREE_DYNAMIC for kd in w.kinds):
+        return None
+    B, k, D = w.batch, w.topk, w.depth
+    p = E.TreeParams(D, k, w.children, w.m, 0, w.vocab, w.m_max, w.r_max)
+    ws = torch.empty(max(256, E.build_tree_workspace_size(p, B)), dtype=torch.uint8, device="cuda")
+    E.workspace_init(ws)
+    d = S["draft"]
+    levels = [d[:, 0:1].contiguous()] + [d[:, 1 + (l - 1) * k:1 + l * k].contiguous() for l in range(1, D)]
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ft, fp = torch.empty((B, k), **i32), torch.empty((B, k), **i32)
+    fs = torch.empty((B, k), dtype=torch.float64, device="cuda")
+    t = {n: torch.empty((B, w.m_max), **i32) for n in ("tokens", "parent", "depth", "src_row")}
+    t["score"] = torch.empty((B, w.m_max), dtype=torch.float64, device="cuda")
+    t["num_nodes"] = torch.empty((B,), **i32)
+
+    def run(ev=None):
+        for lv in range(D):
+            E.tree_expand(p, B, lv, levels[lv], ft, fp, fs, ws)
+            if ev is not None:
+                ev[lv + 1].record()
+        E.tree_finish(p, B, t["tokens"], t["parent"], t["depth"], t["score"], t["src_row"], t["num_nodes"], ws)
+        if ev is not None:
+            ev[D + 1].record()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    n = max(1, reps)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ea.record()
+    for _ in range(n):
+        g.replay()
+    eb.record()
+    torch.cuda.synchronize()
+    total_us = ea.elapsed_time(eb) * 1e3 / n
+    n_ev = min(n, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(D + 2)] for _ in range(n_ev)]
+    for e in evs:
+        e[0].record()
+        run(e)
+    torch.cuda.synchronize()
+    per = [float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j in range(D + 1)]
+    # the finished tree is the one-shot build's over the same rows
+    step.build(S["draft"], kinds)
+    torch.cuda.synchronize()
+    for name in ("tokens", "parent", "score", "num_nodes"):
+        assert torch.equal(t[name], getattr(step, name)), f"incremental build differs in {name}"
+    return {"calls": "eagle_tree_expand x depth + eagle_tree_finish", "levels": D,
+            "total_us": round(total_us, 2), "per_level_us": [round(x, 2) for x in per[:D]],
+            "finish_us": round(per[D], 2), "timed_builds": n}
 
 
 def cpu_baseline(w, S, seed, tokens_per_step, budget_s):
