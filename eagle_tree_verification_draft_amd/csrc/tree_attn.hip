@@ -669,11 +669,15 @@ constexpr int kMergeRows = 16;
 __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a)
 {
     const int tid = threadIdx.x;
-    const int blocks_per_unit = (a.rows_pg + kMergeRows - 1) / kMergeRows;
-    const int unit = blockIdx.x / blocks_per_unit;
-    const int rl = (blockIdx.x % blocks_per_unit) * kMergeRows + (tid >> 4);
+    // block -> (sequence/kv head, row group, row block) in the main kernel's
+    // order, so each unit's partials are merged on the XCD whose L2 holds them
+    const int x = blockIdx.x;
+    const int u0 = x % a.units0;
+    const int rest = x / a.units0;
+    const int rg = rest % a.RG, j = rest / a.RG;
+    const int unit = u0 * a.RG + rg;
+    const int rl = j * kMergeRows + (tid >> 4);
     const int d8 = (tid & 15) * 8;
-    const int rg = unit % a.RG, u0 = unit / a.RG;
     const int b = u0 / a.Hkv, kvh = u0 % a.Hkv;
     const int G = a.G, m_max = a.m_max;
     int L = a.prefix_len[b];

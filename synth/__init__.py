@@ -10,7 +10,7 @@ The pages measure with trained draft/target models on text benchmarks
 None of those models or datasets is used: random logits stand in for the
 draft and target models, and the five workload shapes below stand in for the
 model shapes (EAGLE-2 explainer, section "Implementation", tree depth 6,
-expansion 10, m = 60/50/48 for 7B-8B/13B/70B; P-EAGLE page, section
+expansion 10, m = 60/50/48 for 7B-8B/13B/70B; P-EAGLE in vLLM, section
 "Speculative depth efficiency", K = 7 parallel-draft chains).
 
 Layouts (all row-major):
