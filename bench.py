@@ -158,8 +158,7 @@ def main():
     def run_step(S, ev=None):
         a = S["attn"]
         if not args.attn_only:
-            step.build(S["draft"], kinds)
-            step.mask(a.prefix_len)
+            step.build_mask(S["draft"], kinds, a.prefix_len)
         if ev is not None:
             ev[0].record()
         step.attention(a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table, a.prefix_len)
@@ -246,22 +245,20 @@ def main():
         f"(eager with events {attn_eager_ms * 1e3:.2f})")
 
     # ---- per-stage breakdown (separate loop, events between the calls) ---
-    stage_names = ["build_tree", "tree_mask", "tree_attn", "accept"]
+    stage_names = ["build_tree+mask", "tree_attn", "accept"]
     n_stage = min(K, 100)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_stage)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_stage)]
     for k in range(n_stage):
         S = sets[k % nsets]
         a = S["attn"]
         e = sev[k]
         e[0].record()
-        step.build(S["draft"], kinds)
+        step.build_mask(S["draft"], kinds, a.prefix_len)
         e[1].record()
-        step.mask(a.prefix_len)
-        e[2].record()
         step.attention(a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table, a.prefix_len)
-        e[3].record()
+        e[2].record()
         step.accept(S["target"], S["words"])
-        e[4].record()
+        e[3].record()
     torch.cuda.synchronize()
     stage_us = {n: float(np.median([sev[k][j].elapsed_time(sev[k][j + 1]) for k in range(n_stage)])) * 1e3
                 for j, n in enumerate(stage_names)}

@@ -32,7 +32,7 @@ DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 
 EXPORTS = (
     "eagle_workspace_init", "eagle_read_errors",
     "eagle_build_tree_workspace_size", "eagle_build_tree",
-    "eagle_tree_expand", "eagle_tree_finish",
+    "eagle_build_tree_mask", "eagle_tree_expand", "eagle_tree_finish",
     "eagle_tree_mask",
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
     "eagle_kv_commit",
@@ -80,6 +80,8 @@ def lib() -> C.CDLL:
         L.eagle_build_tree_workspace_size.restype = sz
         L.eagle_build_tree.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp,
                                        vp, sz, vp]
+        L.eagle_build_tree_mask.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_expand.argtypes = [C.POINTER(TreeParams), i32, i32, vp, C.c_int, i64, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_finish.argtypes = [C.POINTER(TreeParams), i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -96,8 +98,9 @@ def lib() -> C.CDLL:
         L.eagle_status_string.restype = C.c_char_p
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
-        for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_tree_expand",
-                  "eagle_tree_finish", "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit", "eagle_accept"):
+        for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_build_tree_mask",
+                  "eagle_tree_expand", "eagle_tree_finish", "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit",
+                  "eagle_accept"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -171,6 +174,17 @@ def build_tree(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind: Opti
                                   _ptr(score), _ptr(src_row), _ptr(num_nodes), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_build_tree")
+
+
+def build_tree_mask(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind: Optional[torch.Tensor], prefix_len,
+                    tokens, parent, depth, score, src_row, num_nodes, anc_mask, pos, workspace: torch.Tensor,
+                    stream=None):
+    rows, stride = _rows(draft_logits)
+    _check(lib().eagle_build_tree_mask(C.byref(p), batch, rows, dtype_code(draft_logits.dtype), stride, _ptr(kind),
+                                       _ptr(prefix_len), _ptr(tokens), _ptr(parent), _ptr(depth), _ptr(score),
+                                       _ptr(src_row), _ptr(num_nodes), _ptr(anc_mask), _ptr(pos), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_build_tree_mask")
 
 
 def tree_expand(p: TreeParams, batch: int, level: int, level_logits: torch.Tensor, frontier_tokens,
@@ -305,6 +319,11 @@ class VerifyStep:
         build_tree(self.tree, self.s.batch, draft_logits, kind, self.tokens, self.parent, self.depth, self.score,
                    self.src_row, self.num_nodes, self.ws_tree, stream)
 
+    def build_mask(self, draft_logits, kind, prefix_len, stream=None):
+        """build() and mask() in one call (one launch fewer)."""
+        build_tree_mask(self.tree, self.s.batch, draft_logits, kind, prefix_len, self.tokens, self.parent, self.depth,
+                        self.score, self.src_row, self.num_nodes, self.anc, self.pos, self.ws_tree, stream)
+
     def mask(self, prefix_len, stream=None):
         tree_mask(self.s.batch, self.s.m_max, self.parent, self.num_nodes, prefix_len, self.anc, self.pos,
                   self.ws_mask, stream)
@@ -327,8 +346,7 @@ class VerifyStep:
 
     def run(self, draft_logits, kind, prefix_len, q, k_draft, v_draft, k_cache, v_cache, block_table,
             target_logits, rand_words=None, stream=None):
-        self.build(draft_logits, kind, stream)
-        self.mask(prefix_len, stream)
+        self.build_mask(draft_logits, kind, prefix_len, stream)
         self.attention(q, k_draft, v_draft, k_cache, v_cache, block_table, prefix_len, stream)
         self.accept(target_logits, rand_words, stream)
 

@@ -319,6 +319,7 @@ struct TreeSmem {
     int ahead[kMaxCand];                    // entries of other depths that come first
     int rank_of[kMaxCand];                  // overall rank, -1 if not selected
     int sel[kMaxMMax];                      // creation index by overall rank
+    int prank[kMaxMMax];                    // parent's rank by rank (ancestor masks)
     int lvl_off[kMaxDepth + 1];             // first creation index of each depth, then N
 };
 
@@ -367,6 +368,14 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         }
         for (int i = K + tid; i < m_max; i += NT) {
             tokens[i] = -1; parent[i] = -1; depth[i] = -1; score[i] = 0.0; src_row[i] = -1;
+        }
+        if (a.anc) {
+            // a chain's node i sees nodes 0..i and sits at depth i + 1
+            const int L = a.prefix_len[b];
+            for (int i = tid; i < m_max; i += NT) {
+                a.anc[(size_t)b * m_max + i] = i < K ? (i == 63 ? ~0ull : (2ull << i) - 1) : 0ull;
+                a.pos[(size_t)b * m_max + i] = i < K ? L + i : -1;
+            }
         }
         return;
     }
@@ -521,11 +530,33 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         depth[r] = sm.dep[i];
         score[r] = sm.V[i];
         src_row[r] = sm.row[i];
+        sm.prank[r] = pr;
     }
     for (int r = m + tid; r < m_max; r += NT) {
         tokens[r] = -1; parent[r] = -1; depth[r] = -1; score[r] = 0.0; src_row[r] = -1;
     }
     if (tid == 0) a.num_nodes[b] = m;
+    if (a.anc) {
+        // ancestor masks: node r and the nodes on its path to the root (rank
+        // order is topological, so parents have smaller ranks); position =
+        // prefix_len + depth - 1
+        const int L = a.prefix_len[b];
+        __syncthreads();
+        for (int r = tid; r < m_max; r += NT) {
+            uint64_t acc = 0;
+            int pos = -1;
+            if (r < m) {
+                acc = 1ull << r;
+                // (bounded: a tree with non-finite scores, already reported,
+                // may leave ranks unassigned)
+                int q = sm.prank[r];
+                for (int it = 0; it < kMaxMMax && q >= 0 && q < m; ++it, q = sm.prank[q]) acc |= 1ull << q;
+                pos = L + __popcll(acc) - 1;
+            }
+            a.anc[(size_t)b * m_max + r] = acc;
+            a.pos[(size_t)b * m_max + r] = pos;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -695,7 +726,8 @@ static RowStatsArgs row_stats_args(const eagle_tree_params *p, int32_t batch, co
 static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const RowStatsArgs &ra,
                                 const int32_t *kind, const int32_t *levels, int32_t *tokens, int32_t *parent,
                                 int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
-                                hipStream_t st)
+                                hipStream_t st, const int32_t *prefix_len = nullptr, uint64_t *anc = nullptr,
+                                int32_t *pos = nullptr)
 {
     TreeSelectArgs ta;
     ta.kind = kind;
@@ -717,6 +749,9 @@ static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const
     ta.src_row = src_row;
     ta.num_nodes = num_nodes;
     ta.levels = levels;
+    ta.prefix_len = prefix_len;
+    ta.anc = anc;
+    ta.pos = pos;
     ta.err = ra.err;
     if (batch <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(1024), 0, st, ta);
@@ -733,6 +768,20 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
     hipError_t e = launch_row_stats(ra, dt, st);
     if (e != hipSuccess) return e;
     return launch_select(p, batch, ra, kind, nullptr, tokens, parent, depth, score, src_row, num_nodes, st);
+}
+
+hipError_t launch_build_tree_mask(const eagle_tree_params *p, int32_t batch, const void *logits,
+                                  eagle_dtype dt, int64_t row_stride, const int32_t *kind,
+                                  const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
+                                  double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc,
+                                  int32_t *pos, void *ws, hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    const RowStatsArgs ra = row_stats_args(p, batch, L, ws, logits, dt, row_stride, kind, p->r_max, 0);
+    hipError_t e = launch_row_stats(ra, dt, st);
+    if (e != hipSuccess) return e;
+    return launch_select(p, batch, ra, kind, nullptr, tokens, parent, depth, score, src_row, num_nodes, st,
+                         prefix_len, anc, pos);
 }
 
 hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level, const void *logits,

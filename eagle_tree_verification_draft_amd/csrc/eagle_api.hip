@@ -131,6 +131,28 @@ eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const v
                       "build_tree launch");
 }
 
+eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                   eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
+                                   const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
+                                   double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc_mask,
+                                   int32_t *pos, void *workspace, size_t workspace_bytes, void *stream)
+{
+    eagle_status s = check_tree_params(p, batch);
+    if (s != EAGLE_OK) return s;
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes || !prefix_len ||
+        !anc_mask || !pos)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
+    s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_build_tree_mask(p, batch, draft_logits, dtype, row_stride, kind, prefix_len, tokens,
+                                             parent, depth, score, src_row, num_nodes, anc_mask, pos, workspace,
+                                             (hipStream_t)stream),
+                      "build_tree_mask launch");
+}
+
 eagle_status eagle_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level,
                                const void *level_logits, eagle_dtype dtype, int64_t row_stride,
                                int32_t *frontier_tokens, int32_t *frontier_parent, double *frontier_score,

@@ -41,6 +41,9 @@ struct TreeSelectArgs {
     double *score;
     int32_t *src_row, *num_nodes;
     const int32_t *levels;   // incremental build: levels given per sequence (NULL: one-shot)
+    const int32_t *prefix_len;   // with anc / pos: the ancestor masks and positions too
+    uint64_t *anc;
+    int32_t *pos;
     uint32_t *err;
 };
 
@@ -73,6 +76,11 @@ hipError_t launch_build_tree(const eagle_tree_params *p, int32_t batch, const vo
                              int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
                              int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st);
 
+hipError_t launch_build_tree_mask(const eagle_tree_params *p, int32_t batch, const void *logits,
+                                  eagle_dtype dt, int64_t row_stride, const int32_t *kind,
+                                  const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
+                                  double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc,
+                                  int32_t *pos, void *ws, hipStream_t st);
 hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level, const void *logits,
                               eagle_dtype dt, int64_t row_stride, int32_t *f_tok, int32_t *f_par,
                               double *f_score, void *ws, hipStream_t st);

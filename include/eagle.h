@@ -127,6 +127,19 @@ eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const v
                               int32_t *src_row, int32_t *num_nodes, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/*
+ * eagle_build_tree followed by eagle_tree_mask on its own outputs, in one
+ * call with one launch fewer: the same tree outputs, plus anc_mask and pos
+ * [batch][m_max] as eagle_tree_mask defines them for prefix_len [batch].
+ * Errors: those of eagle_build_tree, and EAGLE_ERR_INVALID for a NULL
+ * prefix_len, anc_mask or pos.
+ */
+eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                   eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
+                                   const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
+                                   double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc_mask,
+                                   int32_t *pos, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Incremental tree build                                              */
 /* ------------------------------------------------------------------ */

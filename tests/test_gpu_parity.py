@@ -153,6 +153,20 @@ def small_case(request):
     return c
 
 
+def test_separate_build_and_mask_equal_the_fused_call(small_case):
+    """The step runs eagle_build_tree_mask; eagle_build_tree followed by
+    eagle_tree_mask must give the same outputs bit for bit."""
+    c = small_case
+    s = c.step
+    fused = {k: getattr(s, k).clone() for k in ("tokens", "parent", "depth", "score", "src_row", "num_nodes",
+                                                  "anc", "pos")}
+    s.build(c.draft, c.kinds)
+    s.mask(c.attn.prefix_len)
+    torch.cuda.synchronize()
+    for k, v in fused.items():
+        assert torch.equal(getattr(s, k), v), k
+
+
 def test_small_all_outputs(small_case):
     c = small_case
     assert_tree_equal(c)
