@@ -37,6 +37,7 @@ EXPORTS = (
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
     "eagle_kv_commit",
     "eagle_accept_workspace_size", "eagle_accept",
+    "eagle_pdraft_prepare",
     "eagle_status_string", "eagle_last_error",
 )
 
@@ -55,6 +56,11 @@ class AttnParams(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("m_max", C.c_int32), ("block_size", C.c_int32), ("max_blocks", C.c_int32),
                 ("max_prefix", C.c_int32), ("scale", C.c_float), ("dtype", C.c_int)]
+
+
+class PdraftParams(C.Structure):
+    _fields_ = [("m_max", C.c_int32), ("max_accept", C.c_int32), ("k_draft", C.c_int32), ("hidden", C.c_int32),
+                ("mask_token_id", C.c_int32), ("dtype", C.c_int)]
 
 
 class AcceptParams(C.Structure):
@@ -94,13 +100,14 @@ def lib() -> C.CDLL:
         L.eagle_accept_workspace_size.restype = sz
         L.eagle_accept.argtypes = [C.POINTER(AcceptParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]
+        L.eagle_pdraft_prepare.argtypes = [C.POINTER(PdraftParams), i32] + [vp] * 16 + [sz, vp]
         L.eagle_status_string.argtypes = [C.c_int]
         L.eagle_status_string.restype = C.c_char_p
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
         for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_build_tree_mask",
                   "eagle_tree_expand", "eagle_tree_finish", "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit",
-                  "eagle_accept"):
+                  "eagle_accept", "eagle_pdraft_prepare"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -249,6 +256,18 @@ def accept(a: AcceptParams, batch: int, target_logits: torch.Tensor, tokens, par
                               _ptr(rand_words), _ptr(accepted), _ptr(accept_len), _ptr(bonus_token),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_accept")
+
+
+def pdraft_prepare(p: PdraftParams, batch: int, tokens, num_nodes, accepted, accept_len, bonus_token, prefix_len,
+                   target_hidden, h_shared, input_ids, positions, hidden_src, is_mask, rejected, num_slots,
+                   draft_hidden, workspace: torch.Tensor, stream=None):
+    _check(lib().eagle_pdraft_prepare(C.byref(p), batch, _ptr(tokens), _ptr(num_nodes), _ptr(accepted),
+                                      _ptr(accept_len), _ptr(bonus_token), _ptr(prefix_len), _ptr(target_hidden),
+                                      _ptr(h_shared), _ptr(input_ids), _ptr(positions), _ptr(hidden_src),
+                                      _ptr(is_mask), _ptr(rejected), _ptr(num_slots), _ptr(draft_hidden),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)),
+           "eagle_pdraft_prepare")
 
 
 # ---------------------------------------------------------------------------

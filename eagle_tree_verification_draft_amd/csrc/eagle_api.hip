@@ -335,4 +335,42 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
                       "accept launch");
 }
 
+eagle_status eagle_pdraft_prepare(const eagle_pdraft_params *p, int32_t batch, const int32_t *tokens,
+                                  const int32_t *num_nodes, const int32_t *accepted,
+                                  const int32_t *accept_len, const int32_t *bonus_token,
+                                  const int32_t *prefix_len, const void *target_hidden,
+                                  const void *h_shared, int32_t *input_ids, int32_t *positions,
+                                  int32_t *hidden_src, uint8_t *is_mask, uint8_t *rejected,
+                                  int32_t *num_slots, void *draft_hidden, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    if (!p) return fail(EAGLE_ERR_INVALID, "parallel-draft params are NULL");
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (p->dtype != EAGLE_F32 && p->dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)p->dtype);
+    if (p->m_max < 1 || p->m_max > kMaxMMax) return fail(EAGLE_ERR_INVALID, "m_max %d not in [1, %d]", p->m_max, kMaxMMax);
+    if (p->max_accept < 1 || p->k_draft < 1 || p->hidden < 1)
+        return fail(EAGLE_ERR_INVALID, "max_accept %d, k_draft %d and hidden %d must be >= 1", p->max_accept,
+                    p->k_draft, p->hidden);
+    if ((long long)p->max_accept + p->k_draft > (1 << 20))
+        return fail(EAGLE_ERR_UNSUPPORTED, "max_accept + k_draft above 2^20");
+    const size_t esz = p->dtype == EAGLE_F32 ? 4 : 2;
+    if ((size_t)p->hidden * esz % 16 != 0)
+        return fail(EAGLE_ERR_UNSUPPORTED, "hidden %d x %zu bytes is not a multiple of 16", p->hidden, esz);
+    if (!tokens || !num_nodes || !accepted || !accept_len || !bonus_token || !prefix_len || !target_hidden ||
+        !h_shared || !input_ids || !positions || !hidden_src || !is_mask || !rejected || !num_slots || !draft_hidden)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (!(aligned16(target_hidden) && aligned16(h_shared) && aligned16(draft_hidden)))
+        return fail(EAGLE_ERR_UNSUPPORTED, "hidden-state buffers must be 16-byte aligned");
+    eagle_status s = check_workspace(workspace, workspace_bytes, kWsHeader);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    if ((long long)batch * (p->max_accept + p->k_draft) > 0x7fffffffLL)
+        return fail(EAGLE_ERR_UNSUPPORTED, "batch x slots above 2^31");
+    return hip_status(launch_pdraft_prepare(p, batch, tokens, num_nodes, accepted, accept_len, bonus_token, prefix_len,
+                                            target_hidden, h_shared, input_ids, positions, hidden_src, is_mask,
+                                            rejected, num_slots, draft_hidden, static_cast<uint32_t *>(workspace),
+                                            (hipStream_t)stream),
+                      "pdraft_prepare launch");
+}
+
 }  // extern "C"

@@ -122,6 +122,14 @@ hipError_t launch_kv_commit(const eagle_attn_params *p, int32_t batch, const voi
                             const int32_t *prefix_len, void *k_cache, void *v_cache, const int32_t *block_table,
                             int32_t *slot_mapping, int32_t *prefix_len_out, uint32_t *err, hipStream_t st);
 
+// ---- parallel-draft inputs ------------------------------------------------
+hipError_t launch_pdraft_prepare(const eagle_pdraft_params *p, int32_t batch, const int32_t *tokens,
+                                 const int32_t *num_nodes, const int32_t *accepted, const int32_t *accept_len,
+                                 const int32_t *bonus, const int32_t *prefix_len, const void *target_hidden,
+                                 const void *h_shared, int32_t *input_ids, int32_t *positions, int32_t *hidden_src,
+                                 uint8_t *is_mask, uint8_t *rejected, int32_t *num_slots, void *draft_hidden,
+                                 uint32_t *err, hipStream_t st);
+
 // ---- accept --------------------------------------------------------------
 hipError_t launch_accept(const eagle_accept_params *a, int32_t batch, const void *target,
                          eagle_dtype dt, int64_t row_stride, const int32_t *tokens,

@@ -347,6 +347,66 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
                           void *stream);
 
 /* ------------------------------------------------------------------ */
+/* Parallel-draft inputs (P-EAGLE)                                     */
+/* ------------------------------------------------------------------ */
+/*
+ * Defines (P-EAGLE in vLLM, "Step 2: parallel drafting": the prompt positions
+ * pair each token with the target hidden state one position earlier, the
+ * first drafting position pairs the newly generated token with the last
+ * hidden state, and positions 2..K carry the shared MASK embedding and the
+ * shared learned hidden state; "Unified Triton kernel" and "Hidden-state
+ * management": one pass that writes the ids, positions, MASK ids, the
+ * rejected-token and mask-token masks and the hidden-state mapping, and the
+ * broadcast copy of the hidden states).  After eagle_accept, for sequence b
+ * with L = prefix_len[b], the usable accepted path a_0..a_{A-1}
+ * (accepted[b][j], A = accept_len[b]) and the bonus token, with
+ * S = max_accept + k_draft slots per sequence:
+ *   slot s <= A:        position L - 1 + s (slot 0 is the root, the last
+ *                       prefix token; slot j + 1 is node a_j); input_ids =
+ *                       tokens[b][a_s] for s < A and bonus_token[b] for
+ *                       s = A; hidden_src = 0 for s = 0, a_{s-1} + 1
+ *                       otherwise (a row of target_hidden); is_mask 0;
+ *   slot A < s < A + K: position L - 1 + s, input_ids = mask_token_id,
+ *                       hidden_src = -1, is_mask 1 (hidden state h_shared);
+ *   slot s >= A + K:    padding: ids, positions and hidden_src -1, is_mask 0,
+ *                       a zero hidden state;
+ *   draft_hidden[b][s][:] = target_hidden[b][hidden_src][:], h_shared, or 0;
+ *   num_slots[b] = A + K; rejected[b][i] = 1 for nodes i < num_nodes[b] not
+ *   on the accepted path (their KV is not kept), else 0.
+ * Layouts: tokens [batch][m_max] and num_nodes [batch] (eagle_build_tree);
+ *   accepted [batch][max_accept], accept_len and bonus_token [batch]
+ *   (eagle_accept); target_hidden [batch][m_max + 1][hidden] (row 0 the
+ *   root, row i + 1 node i); h_shared [hidden]; input_ids, positions and
+ *   hidden_src [batch][S] int32; is_mask [batch][S] and rejected
+ *   [batch][m_max] uint8; num_slots [batch]; draft_hidden [batch][S][hidden].
+ * Device errors: EAGLE_DEVERR_TREE for accept_len outside
+ *   [0, min(max_accept, m_max)] (clamped) or an accepted node id outside
+ *   [0, m_max) (the path is cut before it); EAGLE_DEVERR_PREFIX for L < 1.
+ * Errors: EAGLE_ERR_INVALID for null pointers, k_draft < 1, max_accept < 1,
+ *   m_max outside [1, 64] or hidden < 1; EAGLE_ERR_UNSUPPORTED unless
+ *   hidden * sizeof(dtype) is a multiple of 16 and the three hidden-state
+ *   buffers are 16-byte aligned; EAGLE_ERR_WORKSPACE for a short workspace
+ *   (only the error word: >= 256 bytes, eagle_workspace_init'ed).
+ */
+typedef struct {
+    int32_t m_max;
+    int32_t max_accept;
+    int32_t k_draft;        /* K: tokens one parallel drafting pass predicts */
+    int32_t hidden;         /* hidden size */
+    int32_t mask_token_id;
+    eagle_dtype dtype;      /* of target_hidden, h_shared and draft_hidden */
+} eagle_pdraft_params;
+
+eagle_status eagle_pdraft_prepare(const eagle_pdraft_params *p, int32_t batch, const int32_t *tokens,
+                                  const int32_t *num_nodes, const int32_t *accepted,
+                                  const int32_t *accept_len, const int32_t *bonus_token,
+                                  const int32_t *prefix_len, const void *target_hidden,
+                                  const void *h_shared, int32_t *input_ids, int32_t *positions,
+                                  int32_t *hidden_src, uint8_t *is_mask, uint8_t *rejected,
+                                  int32_t *num_slots, void *draft_hidden, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
 const char *eagle_status_string(eagle_status s);
 const char *eagle_last_error(void); /* thread-local; never NULL */
 

@@ -53,9 +53,10 @@ def lib():
         L.orc_tree_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_tree_attn_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
         L.orc_kv_commit.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_pdraft_prepare.argtypes = [i32] * 7 + [vp] * 16
         L.orc_accept.argtypes = [i32, f32, i32, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp]
         for f in ("orc_row_stats", "orc_build_tree", "orc_tree_mask", "orc_tree_attn",
-                  "orc_tree_attn_rows", "orc_kv_commit", "orc_accept", "orc_num_threads"):
+                  "orc_tree_attn_rows", "orc_kv_commit", "orc_pdraft_prepare", "orc_accept", "orc_num_threads"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -270,6 +271,37 @@ def kv_commit(k_draft, v_draft, accepted, accept_len, prefix_len, k_cache, v_cac
     _check(lib().orc_kv_commit(C.byref(p), cap, B, _p(kd), _p(vd), _p(acc), _p(alen), acc.shape[1], _p(pl),
                                _p(kc), _p(vc), _p(bt), _p(slot), _p(plo), _p(flags)), "kv_commit")
     return kc, vc, slot, plo, (int(flags[0]), int(flags[1]))
+
+
+def pdraft_prepare(tokens, num_nodes, accepted, accept_len, bonus, prefix_len, target_hidden, h_shared, K,
+                   mask_id):
+    """Inputs of the next parallel drafting pass (see oracle.c).  target_hidden
+    [B][m_max+1][H] and h_shared [H] as float32 or uint16 (bf16 bits).  Returns
+    a dict of input_ids, positions, hidden_src [B][S], is_mask [B][S],
+    rejected [B][m_max], num_slots [B], draft_hidden [B][S][H], flags."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    B, M = tok.shape
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    MA = acc.shape[1]
+    th = np.ascontiguousarray(target_hidden)
+    hs = np.ascontiguousarray(h_shared)
+    if th.dtype not in (np.float32, np.uint16) or hs.dtype != th.dtype:
+        raise TypeError("hidden states must be float32 or uint16 (bf16 bits), both the same")
+    H = th.shape[-1]
+    S = MA + K
+    out = dict(input_ids=np.zeros((B, S), np.int32), positions=np.zeros((B, S), np.int32),
+               hidden_src=np.zeros((B, S), np.int32), is_mask=np.zeros((B, S), np.uint8),
+               rejected=np.zeros((B, M), np.uint8), num_slots=np.zeros(B, np.int32),
+               draft_hidden=np.zeros((B, S, H), th.dtype))
+    flags = np.zeros(2, np.int32)
+    arr = [np.ascontiguousarray(x, dtype=np.int32) for x in (num_nodes, accept_len, bonus, prefix_len)]
+    _check(lib().orc_pdraft_prepare(B, M, MA, K, H, mask_id, th.itemsize, _p(tok), _p(arr[0]), _p(acc), _p(arr[1]),
+                                    _p(arr[2]), _p(arr[3]), _p(th), _p(hs), _p(out["input_ids"]),
+                                    _p(out["positions"]), _p(out["hidden_src"]), _p(out["is_mask"]),
+                                    _p(out["rejected"]), _p(out["num_slots"]), _p(out["draft_hidden"]), _p(flags)),
+           "pdraft_prepare")
+    out["flags"] = (int(flags[0]), int(flags[1]))
+    return out
 
 
 def accept(mode, target_logits, tokens, parent, num_nodes, max_accept, rand_words=None, T=1.0):

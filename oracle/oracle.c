@@ -20,6 +20,9 @@
  *     "Verification"), so the accepted path's draft K/V are written at the
  *     next cache positions; tokens not kept map to slot -1 (P-EAGLE in vLLM, "KV
  *     cache and CUDA graphs");
+ *   - parallel-draft inputs: the ids, positions, masks and hidden states
+ *     of the next P-EAGLE drafting pass (P-EAGLE in vLLM, "Step 2: parallel
+ *     drafting", "Unified Triton kernel", "Hidden-state management");
  *   - acceptance: draft tokens are accepted by comparing draft and target
  *     distributions, the rest discarded after a rejection and a token
  *     resampled, leaving the target distribution unchanged (EAGLE-1 explainer,
@@ -605,6 +608,90 @@ int orc_kv_commit(const orc_attn_params *a, int cap, int batch, const void *k_dr
             ++n;
         }
         prefix_len_out[b] = L + n;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* parallel-draft inputs                                                */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The inputs of the next parallel drafting pass (P-EAGLE in vLLM, "Step 2:
+ * parallel drafting": a known position pairs its target hidden state with the
+ * token that follows it, the first drafting position pairs the new token with
+ * the last hidden state, and the K - 1 further positions carry the MASK token
+ * and the shared hidden state; "Unified Triton kernel" and "Hidden-state
+ * management" for the outputs).  For sequence b: L = prefix_len[b], the
+ * accepted path a_0..a_{A-1} (cut at the first node id outside [0, m_max),
+ * flags[0]; A clamped to [0, min(max_accept, m_max)], flags[0]), bonus t_A.
+ * The known positions are the root (the last prefix token, position L - 1,
+ * hidden row 0) and the accepted nodes (position L + j, hidden row a_j + 1);
+ * the token that follows position L - 1 + s is the token of a_s, or the bonus
+ * after the last.  S = max_accept + K slots; L < 1 is flagged (flags[1]).
+ * esz = bytes per hidden element; hidden rows are H elements.
+ */
+int orc_pdraft_prepare(int batch, int m_max, int max_accept, int K, int H, int mask_id, int esz,
+                       const int *tokens, const int *num_nodes, const int *accepted, const int *accept_len,
+                       const int *bonus, const int *prefix_len, const void *target_hidden, const void *h_shared,
+                       int *input_ids, int *positions, int *hidden_src, uint8_t *is_mask, uint8_t *rejected,
+                       int *num_slots, void *draft_hidden, int *flags)
+{
+    if (batch < 0 || m_max < 1 || m_max > 64 || max_accept < 1 || K < 1 || H < 1) return ORC_ERR_ARG;
+    const int S = max_accept + K;
+    const size_t row = (size_t)H * esz;
+    flags[0] = flags[1] = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int L = prefix_len[b];
+        const int amax = max_accept < m_max ? max_accept : m_max;
+        int A = accept_len[b];
+        if (A < 0 || A > amax) {
+            A = A < 0 ? 0 : amax;
+            flags[0]++;
+        }
+        const int *acc = accepted + (size_t)b * max_accept;
+        for (int j = 0; j < A; ++j)
+            if (acc[j] < 0 || acc[j] >= m_max) {
+                A = j;
+                flags[0]++;
+                break;
+            }
+        if (L < 1) flags[1]++;
+        num_slots[b] = A + K;
+        for (int s = 0; s < S; ++s) {
+            const size_t o = (size_t)b * S + s;
+            char *dst = (char *)draft_hidden + o * row;
+            const void *src = NULL;
+            if (s <= A) {
+                /* a known position: the root (s = 0) or accepted node a_{s-1} */
+                input_ids[o] = s < A ? tokens[(size_t)b * m_max + acc[s]] : bonus[b];
+                positions[o] = L - 1 + s;
+                hidden_src[o] = s == 0 ? 0 : acc[s - 1] + 1;
+                is_mask[o] = 0;
+                src = (const char *)target_hidden + ((size_t)b * (m_max + 1) + hidden_src[o]) * row;
+            } else if (s < A + K) {
+                /* a parallel-drafting position */
+                input_ids[o] = mask_id;
+                positions[o] = L - 1 + s;
+                hidden_src[o] = -1;
+                is_mask[o] = 1;
+                src = h_shared;
+            } else {
+                input_ids[o] = -1;
+                positions[o] = -1;
+                hidden_src[o] = -1;
+                is_mask[o] = 0;
+            }
+            if (src) memcpy(dst, src, row);
+            else memset(dst, 0, row);
+        }
+        int n = num_nodes[b];
+        n = n < 0 ? 0 : (n > m_max ? m_max : n);
+        for (int i = 0; i < m_max; ++i) {
+            int on_path = 0;
+            for (int j = 0; j < A; ++j) on_path |= acc[j] == i;
+            rejected[(size_t)b * m_max + i] = (uint8_t)(i < n && !on_path);
+        }
     }
     return ORC_OK;
 }

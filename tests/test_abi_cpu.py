@@ -153,6 +153,28 @@ def test_tree_expand_and_finish_reject_bad_params():
     assert L.eagle_tree_finish(C.byref(p), 0, x, x, x, x, x, x, ws, need, None) == E.EAGLE_OK
 
 
+def test_pdraft_prepare_rejects_bad_params():
+    L = E.lib()
+    x = C.c_void_p(1 << 24)
+    ws = C.c_void_p(1 << 21)
+
+    def call(p, align=0, wsb=256, null_hidden=False, batch=2):
+        th = C.c_void_p((1 << 24) + align)
+        return L.eagle_pdraft_prepare(C.byref(p), batch, x, x, x, x, x, x, None if null_hidden else th, x, x, x, x, x,
+                                      x, x, x, ws, wsb, None)
+
+    ok = E.PdraftParams(60, 6, 7, 4096, 5, E.EAGLE_BF16)
+    assert call(E.PdraftParams(60, 6, 0, 4096, 5, E.EAGLE_BF16)) == E.EAGLE_ERR_INVALID
+    assert call(E.PdraftParams(65, 6, 7, 4096, 5, E.EAGLE_BF16)) == E.EAGLE_ERR_INVALID
+    assert call(E.PdraftParams(60, 0, 7, 4096, 5, E.EAGLE_BF16)) == E.EAGLE_ERR_INVALID
+    assert call(E.PdraftParams(60, 6, 7, 4095, 5, E.EAGLE_BF16)) == E.EAGLE_ERR_UNSUPPORTED
+    assert call(E.PdraftParams(60, 6, 7, 4096, 5, 3)) == E.EAGLE_ERR_UNSUPPORTED
+    assert call(ok, null_hidden=True) == E.EAGLE_ERR_INVALID
+    assert call(ok, align=8) == E.EAGLE_ERR_UNSUPPORTED
+    assert call(ok, wsb=8) == E.EAGLE_ERR_WORKSPACE
+    assert call(ok, batch=0) == E.EAGLE_OK
+
+
 def test_accept_and_mask_reject_bad_params():
     L = E.lib()
     p = C.c_void_p(1 << 24)
