@@ -276,6 +276,8 @@ def main():
     commit = measure_commit(E, step, w, sets[0], kinds, K)
     log(f"[bench] kv commit {commit['avg_us']:.2f} us/call for {commit['tokens']} tokens")
     expand = measure_expand(E, step, w, sets[0], kinds, K)
+    pdraft = measure_pdraft(E, step, w, sets[0], kinds, K)
+    log(f"[bench] parallel-draft inputs {pdraft['avg_us']:.2f} us/call, {pdraft['hbm_gbs']:.0f} GB/s")
     if expand:
         log(f"[bench] incremental build {expand['total_us']:.1f} us for {expand['levels']} levels + finish")
 
@@ -337,6 +339,7 @@ def main():
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "kv_commit": commit,
         "tree_expand": expand,
+        "pdraft_prepare": pdraft,
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
         "launch": "hipGraph replay per step" if graphs is not None else "eager",
         "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
@@ -391,6 +394,66 @@ def measure_commit(E, step, w, S, kinds, reps):
     assert torch.equal(plo, plen + step.accept_len), "kv commit did not write every accepted token"
     return {"call": "eagle_kv_commit (k_kv_commit)", "avg_us": round(us, 2), "timed_calls": n * per_graph,
             "tokens": tokens, "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def measure_pdraft(E, step, w, S, kinds, reps):
+    """eagle_pdraft_prepare after input set 0's step (its accepted paths and
+    bonus tokens), outside the step: K = 7 parallel-draft slots, hidden size =
+    query heads x head_dim, synthetic target hidden states in the workload
+    dtype; HIP events around replays of a graph of 20 calls."""
+    import torch
+    a = S["attn"]
+    step.run(S["draft"], kinds, a.prefix_len, a.q, a.k_draft, a.v_draft, a.k_cache, a.v_cache, a.block_table,
+             S["target"], S["words"])
+    B, M, MA, K = w.batch, w.m_max, w.max_accept, 7
+    H = w.num_q_heads * w.head_dim
+    Sl = MA + K
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    th = torch.randn((B, M + 1, H), generator=g, device="cuda").to(w.dtype)
+    hs = torch.randn((H,), generator=g, device="cuda").to(w.dtype)
+    p = E.PdraftParams(M, MA, K, H, w.vocab, E.dtype_code(w.dtype))
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ids, pos, src = (torch.empty((B, Sl), **i32) for _ in range(3))
+    is_mask = torch.empty((B, Sl), dtype=torch.uint8, device="cuda")
+    rej = torch.empty((B, M), dtype=torch.uint8, device="cuda")
+    nsl = torch.empty((B,), **i32)
+    dh = torch.empty((B, Sl, H), dtype=w.dtype, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    E.workspace_init(ws)
+
+    def call():
+        E.pdraft_prepare(p, B, step.tokens, step.num_nodes, step.accepted, step.accept_len, step.bonus, a.prefix_len,
+                         th, hs, ids, pos, src, is_mask, rej, nsl, dh, ws)
+
+    per_graph = 20
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        call()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(per_graph):
+            call()
+    gr.replay()
+    n = max(1, reps // per_graph)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ea.record()
+    for _ in range(n):
+        gr.replay()
+    eb.record()
+    torch.cuda.synchronize()
+    us = ea.elapsed_time(eb) * 1e3 / (n * per_graph)
+    assert E.read_errors(ws) == 0, "parallel-draft preparation reported device errors"
+    esz = th.element_size()
+    known = int(step.accept_len.sum().item()) + B
+    nbytes = (B * Sl + known + 1) * H * esz   # every slot written; each known row and h_shared read once
+    return {"call": "eagle_pdraft_prepare (k_pdraft_prepare)", "k_draft": K, "hidden": H, "slots": B * Sl,
+            "avg_us": round(us, 2), "timed_calls": n * per_graph, "algorithmic_bytes": nbytes,
+            "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def measure_expand(E, step, w, S, kinds, reps):

@@ -42,10 +42,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_pdraft_prepare(PrepArgs a)
     if (tid < 64) {
         // accepted path: its usable length (up to the first invalid node id)
         const int amax = a.max_accept < a.m_max ? a.max_accept : a.m_max;
+        // the node ids are read alongside the length (lanes past it are not used)
+        const int node = tid < amax ? a.accepted[(size_t)b * a.max_accept + tid] : 0;
         int A = a.accept_len[b];
         const bool clamped = A < 0 || A > amax;
         A = A < 0 ? 0 : (A > amax ? amax : A);
-        const int node = tid < A ? a.accepted[(size_t)b * a.max_accept + tid] : 0;
         const unsigned long long bad = __ballot(tid < A && (node < 0 || node >= a.m_max));
         if (bad) A = __ffsll(bad) - 1;
         // the slot's target hidden row: 0 = the root, a_{s-1} + 1 = node a_{s-1}
@@ -60,11 +61,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_pdraft_prepare(PrepArgs a)
             // rejected nodes of the verified tree: present but not on the path
             int n = a.num_nodes[b];
             n = n < 0 ? 0 : (n > a.m_max ? a.m_max : n);
-            for (int i = tid; i < a.m_max; i += 64) {
-                bool on_path = false;
-                for (int j = 0; j < A; ++j) on_path |= a.accepted[(size_t)b * a.max_accept + j] == i;
-                a.rejected[(size_t)b * a.m_max + i] = (i < n && !on_path) ? 1 : 0;
-            }
+            // lane i checks node i against the path held across the lanes (m_max <= 64)
+            bool on_path = false;
+            for (int j = 0; j < A; ++j) on_path |= __shfl(node, j) == tid;
+            if (tid < a.m_max) a.rejected[(size_t)b * a.m_max + tid] = (tid < n && !on_path) ? 1 : 0;
         }
     }
     __syncthreads();
