@@ -114,18 +114,20 @@ def row_stats(logits, C: int, T: float = 1.0):
 
 
 class _TreeParams(C.Structure):
-    _fields_ = [(n, C.c_int) for n in ("depth", "topk", "children", "m", "chain_k", "vocab")]
+    _fields_ = [(n, C.c_int) for n in ("depth", "topk", "children", "m", "chain_k", "vocab", "policy")]
 
 
 def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_max=None,
-               debug=False):
-    """draft_logits [B][R_max][V] -> dict of tree arrays (rank order), plus candidates if debug."""
+               debug=False, policy=0):
+    """draft_logits [B][R_max][V] -> dict of tree arrays (output order), plus candidates if debug.
+    policy: 0 EAGLE-2, 1 no rerank, 2 confidence ranking, 3 confidence ranking without rerank
+    (see oracle.c)."""
     a, dt = _logits(draft_logits)
     B, R, V = a.shape
     if m_max is None:
         m_max = m
     kinds = np.zeros(B, np.int32) if kinds is None else np.ascontiguousarray(kinds, dtype=np.int32)
-    p = _TreeParams(depth, topk, children, m, chain_k, V)
+    p = _TreeParams(depth, topk, children, m, chain_k, V, policy)
     out = {k: np.zeros((B, m_max), np.int32) for k in ("tokens", "parent", "depth", "src_row")}
     out["score"] = np.zeros((B, m_max), np.float64)
     out["num_nodes"] = np.zeros(B, np.int32)
@@ -146,14 +148,14 @@ def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_
     return out
 
 
-def tree_frontiers(draft_logits, depth, topk, children, m, m_max=None):
+def tree_frontiers(draft_logits, depth, topk, children, m, m_max=None, policy=0):
     """The nodes expanded at each depth of the dynamic trees, as an incremental
     build returns them level by level: level l's frontier is the expanded
     nodes of depth l + 1 in expansion order (they own rows 1 + l * topk + p).
     Returns tokens, parent (index in the previous frontier, -1 at level 0) and
     score (V), each [depth][B][topk], padded with -1 / -1 / 0; the last level
     is empty (depth `depth` is not expanded)."""
-    t = build_tree(draft_logits, depth, topk, children, m, m_max=m_max, debug=True)
+    t = build_tree(draft_logits, depth, topk, children, m, m_max=m_max, debug=True, policy=policy)
     cd = t["cand"]
     B = cd["n"].shape[0]
     tok = np.full((depth, B, topk), -1, np.int32)

@@ -204,6 +204,7 @@ typedef struct {
     int parent;   /* creation index of the parent, -1 = root */
     int depth;    /* 1..D */
     double V;
+    double key;   /* ranking key: V, or the node's own confidence c (confidence policies) */
     int row;      /* draft row owned by this node if it was expanded, else -1 */
 } Cand;
 
@@ -214,7 +215,7 @@ static void sort_by_rank(const Cand *c, int *idx, int n)
         int best = i;
         for (int j = i + 1; j < n; ++j) {
             const Cand *x = &c[idx[j]], *y = &c[idx[best]];
-            if (x->V > y->V || (x->V == y->V && idx[j] < idx[best])) best = j;
+            if (x->key > y->key || (x->key == y->key && idx[j] < idx[best])) best = j;
         }
         int t = idx[i];
         idx[i] = idx[best];
@@ -222,8 +223,18 @@ static void sort_by_rank(const Cand *c, int *idx, int n)
     }
 }
 
+/*
+ * policy (EAGLE-2 explainer, "Results", ablation table: without the global
+ * acceptance probability, ranking by confidence only; without reranking):
+ *   0: nodes ranked by V for the expansion and the rerank (EAGLE-2);
+ *   1: ranked by V; no rerank: the tree is every depth's top-k;
+ *   2: ranked by the node's own confidence c; rerank: candidates taken in
+ *      that order, each with its missing ancestors, while the tree stays
+ *      within m nodes (the pages add the ancestors of selected tokens);
+ *   3: ranked by c; no rerank.
+ */
 typedef struct {
-    int depth, topk, children, m, chain_k, vocab;
+    int depth, topk, children, m, chain_k, vocab, policy;
 } orc_tree_params;
 
 /*
@@ -270,6 +281,8 @@ static int build_one(const orc_tree_params *p, int kind, const void *rows, int d
     }
 
     if (D < 1 || k < 1 || C < 1 || p->m < 1 || p->m > m_max) return ORC_ERR_ARG;
+    if (p->policy < 0 || p->policy > 3 || D > 64) return ORC_ERR_ARG;
+    const int conf_key = p->policy >= 2, rerank = p->policy == 0 || p->policy == 2;
     const int R = 1 + (D - 1) * k;
     const int Nmax = C + (D - 1) * k * C;
     Cand *cand = (Cand *)malloc(sizeof(Cand) * (size_t)Nmax);
@@ -293,6 +306,7 @@ static int build_one(const orc_tree_params *p, int kind, const void *rows, int d
         cand[N].parent = -1;
         cand[N].depth = 1;
         cand[N].V = 1.0 * (tw[j] / Wr[0]);
+        cand[N].key = conf_key ? tw[j] / Wr[0] : cand[N].V;
         cand[N].row = -1;
         ++N;
     }
@@ -312,6 +326,7 @@ static int build_one(const orc_tree_params *p, int kind, const void *rows, int d
                 cand[N].parent = par;
                 cand[N].depth = d + 1;
                 cand[N].V = cand[par].V * (tw[(size_t)r * C + j] / Wr[r]);
+                cand[N].key = conf_key ? tw[(size_t)r * C + j] / Wr[r] : cand[N].V;
                 cand[N].row = -1;
                 ++N;
             }
@@ -319,12 +334,46 @@ static int build_one(const orc_tree_params *p, int kind, const void *rows, int d
         begin = end;
         end = N;
     }
-    /* rerank: top-m of every generated candidate */
-    const int m = p->m;
-    if (N < m) { err = ORC_ERR_ARG; goto done; }
-    for (int i = 0; i < N; ++i) idx[i] = i;
-    sort_by_rank(cand, idx, N);
+    /* selection, in output order (idx[0..m)) */
+    int m = p->m;
     for (int i = 0; i < N; ++i) rank_of[i] = -1;
+    if (rerank && !conf_key) {
+        /* rerank: top-m of every generated candidate */
+        if (N < m) { err = ORC_ERR_ARG; goto done; }
+        for (int i = 0; i < N; ++i) idx[i] = i;
+        sort_by_rank(cand, idx, N);
+    } else if (rerank) {
+        /* candidates in key order, each added with its missing ancestors (root
+           first) while the tree stays within m nodes */
+        int *order = (int *)malloc(sizeof(int) * (size_t)N);
+        int chain[64];
+        for (int i = 0; i < N; ++i) order[i] = i;
+        sort_by_rank(cand, order, N);
+        int n_sel = 0;
+        for (int t = 0; t < N && n_sel < m; ++t) {
+            int nc = 0;
+            for (int a = order[t]; a >= 0 && rank_of[a] < 0; a = cand[a].parent) chain[nc++] = a;
+            if (nc == 0 || n_sel + nc > m) continue;
+            for (int q = nc - 1; q >= 0; --q) {
+                rank_of[chain[q]] = n_sel;
+                idx[n_sel++] = chain[q];
+            }
+        }
+        free(order);
+        m = n_sel;
+    } else {
+        /* no rerank: every depth's top-k by the key, depth by depth */
+        int n_sel = 0;
+        for (int d = 1; d <= D; ++d) {
+            int *lvl = idx + n_sel, cnt = 0;
+            for (int i = 0; i < N; ++i)
+                if (cand[i].depth == d) lvl[cnt++] = i;
+            sort_by_rank(cand, lvl, cnt);
+            n_sel += cnt < k ? cnt : k;
+        }
+        m = n_sel;
+        if (m > m_max) { err = ORC_ERR_ARG; goto done; }
+    }
     for (int r = 0; r < m; ++r) rank_of[idx[r]] = r;
     /* connected tree: every ancestor of a selected node must be selected */
     for (int r = 0; r < m; ++r) {

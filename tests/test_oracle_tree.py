@@ -295,3 +295,120 @@ def test_frontiers_follow_level_by_level_expansion(orc, base, seed, B, k):
             assert [float(x) for x in score[lv, b, :len(top)]] == [c[0] for c in top]
             assert (tok[lv, b, len(top):] == -1).all()
             front = [(c[0], 1 + lv * k + p) for p, c in enumerate(top)]
+
+
+def _cand_conf(logits_b, cd, C):
+    """c of every candidate (w / W of its parent's row at its sibling rank),
+    from the Spec S restatement in spec_emul."""
+    N = int(cd["n"])
+    stats, conf, sib = {}, np.zeros(N), {}
+    for i in range(N):
+        q = int(cd["parent"][i])
+        r = 0 if q < 0 else int(cd["row"][q])
+        if r not in stats:
+            stats[r] = spec_emul.row_stats(logits_b[r], C)
+        j = sib.get(q, 0)
+        sib[q] = j + 1
+        _, W, ids, ws = stats[r]
+        assert cd["token"][i] == ids[j]
+        conf[i] = ws[j] / W
+    return conf
+
+
+@pytest.mark.parametrize("base,seed", [(1, 31), (2, 32), (3, 33)])
+def test_no_rerank_policy_is_every_depths_top_k(orc, base, seed):
+    """Policy 1 (V, no rerank): the nodes of depths < D are exactly the nodes
+    the EAGLE-2 build expands (same V ranking), depth D adds its top-k by V;
+    output depth by depth, rank order inside a depth."""
+    w = synth.small_workload(base, batch=2)
+    logits = _rows_np(w, seed)
+    D, k, C = w.depth, w.topk, w.children
+    t0 = orc.build_tree(logits, D, k, C, w.m, m_max=64, debug=True, policy=0)
+    t1 = orc.build_tree(logits, D, k, C, w.m, m_max=64, debug=True, policy=1)
+    for b in range(2):
+        cd = {kk: v[b] for kk, v in t0["cand"].items()}
+        N = int(cd["n"])
+        want = []
+        for d in range(1, D + 1):
+            at_d = sorted([i for i in range(N) if cd["depth"][i] == d], key=lambda i: (-cd["V"][i], i))[:k]
+            if d < D:
+                assert all(cd["row"][i] >= 0 for i in at_d)   # the expanded nodes
+            want += at_d
+        n = int(t1["num_nodes"][b])
+        assert n == len(want) == min(C, k) + (D - 1) * k
+        assert t1["tokens"][b, :n].tolist() == [int(cd["token"][i]) for i in want]
+        assert t1["score"][b, :n].tolist() == [float(cd["V"][i]) for i in want]
+        assert all(t1["parent"][b, r] < r for r in range(n))
+        assert (t1["tokens"][b, n:] == -1).all()
+
+
+@pytest.mark.parametrize("base,seed", [(1, 41), (2, 42)])
+def test_confidence_policies(orc, base, seed):
+    """Policy 3 (c, no rerank): each depth's nodes are the top-k by c of the
+    children of the previous depth's nodes.  Policy 2 (c, rerank): a closed
+    tree of at most m nodes whose every node either ranks among the first by
+    c or is an ancestor of one that does; with rows made flatter at every
+    depth (c falls along every path), it is exactly the top-m by c."""
+    w = synth.small_workload(base, batch=1)
+    logits = _rows_np(w, seed)
+    D, k, C, m = w.depth, w.topk, w.children, w.m
+    t3 = orc.build_tree(logits, D, k, C, m, m_max=64, debug=True, policy=3)
+    cd = {kk: v[0] for kk, v in t3["cand"].items()}
+    conf = _cand_conf(logits[0], cd, C)
+    N = int(cd["n"])
+    front = [-1]
+    sel3 = []
+    for d in range(1, D + 1):
+        at_d = [i for i in range(N) if cd["depth"][i] == d and int(cd["parent"][i]) in front]
+        assert len(at_d) == sum(1 for i in range(N) if cd["depth"][i] == d)   # children of the kept nodes only
+        top = sorted(at_d, key=lambda i: (-conf[i], i))[:k]
+        sel3 += top
+        front = top
+    n3 = int(t3["num_nodes"][0])
+    assert t3["tokens"][0, :n3].tolist() == [int(cd["token"][i]) for i in sel3]
+    # policy 2 on rows whose top-C logits fall with the owner's depth (all
+    # others 0): c falls along every path, so the c order is closed under
+    # ancestors and the selection is the top-m by c
+    rng = np.random.default_rng(seed)
+    V = logits.shape[2]
+    flat = np.zeros((1, logits.shape[1], V), np.float32)
+    for r in range(flat.shape[1]):
+        dr = 0 if r == 0 else 1 + (r - 1) // k
+        flat[0, r, rng.choice(V, size=C, replace=False)] = 8.0 - 1.5 * dr
+    t2 = orc.build_tree(flat, D, k, C, m, m_max=64, debug=True, policy=2)
+    cd2 = {kk: v[0] for kk, v in t2["cand"].items()}
+    conf2 = _cand_conf(flat[0], cd2, C)
+    N2 = int(cd2["n"])
+    par = cd2["parent"]
+    assert all(conf2[i] < conf2[int(par[i])] for i in range(N2) if par[i] >= 0)
+    order = sorted(range(N2), key=lambda i: (-conf2[i], i))[:m]
+    n2 = int(t2["num_nodes"][0])
+    assert n2 == m
+    assert t2["tokens"][0, :n2].tolist() == [int(cd2["token"][i]) for i in order]
+    # policy 2 on the original rows: closed, within m, nodes in selection order
+    t2o = orc.build_tree(logits, D, k, C, m, m_max=64, debug=True, policy=2)
+    n = int(t2o["num_nodes"][0])
+    assert 0 < n <= m
+    assert all(t2o["parent"][0, r] < r for r in range(n))
+
+
+def test_confidence_rerank_hand_example(orc):
+    """Policy 2 with a candidate whose missing ancestors do not fit: D = 3,
+    k = 1, C = 2, vocabulary 4.  Root row: token 0 (c ~ .88), token 1 (~ .12);
+    token 0's row: tokens 2 (~ .52) and 3 (~ .48); token 2's row: token 0
+    (c ~ 1) and token 1.  By c the deepest token 0 comes first but needs its
+    two ancestors: with m = 2 it is skipped, and tokens 0 then 2 are taken
+    (depths 1 and 2); with m = 3 it fits, ancestors first."""
+    logits = np.array([[[2.0, 0.0, -10.0, -10.0],
+                        [-10.0, -10.0, 5.0, 4.9],
+                        [10.0, -10.0, -10.0, -10.0]]], np.float32)
+    t = orc.build_tree(logits, 3, 1, 2, 2, m_max=4, policy=2)
+    assert t["num_nodes"][0] == 2
+    assert t["tokens"][0, :2].tolist() == [0, 2] and t["parent"][0, :2].tolist() == [-1, 0]
+    assert t["depth"][0, :2].tolist() == [1, 2]
+    t = orc.build_tree(logits, 3, 1, 2, 3, m_max=4, policy=2)
+    assert t["tokens"][0, :3].tolist() == [0, 2, 0] and t["parent"][0, :3].tolist() == [-1, 0, 1]
+    assert t["depth"][0, :3].tolist() == [1, 2, 3]
+    # no rerank by c: depth 1 keeps token 0, depth 2 token 2, depth 3 token 0
+    t = orc.build_tree(logits, 3, 1, 2, 2, m_max=4, policy=3)
+    assert t["num_nodes"][0] == 3 and t["tokens"][0, :3].tolist() == [0, 2, 0]
