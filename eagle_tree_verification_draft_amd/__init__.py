@@ -26,6 +26,7 @@ EAGLE_OK, EAGLE_ERR_INVALID, EAGLE_ERR_UNSUPPORTED, EAGLE_ERR_WORKSPACE, EAGLE_E
 EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_TREE_DYNAMIC, EAGLE_TREE_CHAIN = 0, 1
 EAGLE_ACCEPT_GREEDY, EAGLE_ACCEPT_SAMPLE = 0, 1
+EAGLE_POLICY_EAGLE2, EAGLE_POLICY_NO_RERANK, EAGLE_POLICY_CONF, EAGLE_POLICY_CONF_NO_RERANK = 0, 1, 2, 3
 DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 0x1, 0x2, 0x4, 0x8, 0x10
 
 # every function exported by libeagle.so (the declarations of include/eagle.h)
@@ -49,7 +50,8 @@ class EagleError(RuntimeError):
 
 
 class TreeParams(C.Structure):
-    _fields_ = [(n, C.c_int32) for n in ("depth", "topk", "children", "m", "chain_k", "vocab", "m_max", "r_max")]
+    _fields_ = [(n, C.c_int32) for n in ("depth", "topk", "children", "m", "chain_k", "vocab", "m_max", "r_max",
+                                         "policy")]
 
 
 class AttnParams(C.Structure):

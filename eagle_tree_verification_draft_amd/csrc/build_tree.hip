@@ -309,7 +309,8 @@ struct TreeSmem {
     double conf[kMaxRows * kMaxChildren];   // c of every (row, child)
     int cid[kMaxRows * kMaxChildren];       // token of every (row, child)
     double V[kMaxCand + kMaxChildren];      // by creation index (+ slack: whole-list reads)
-    double sV[kMaxCand];                    // V in rank order, each depth at its offset
+    double key[kMaxCand + kMaxChildren];    // ranking key by creation index: V, or c (confidence policies)
+    double sV[kMaxCand];                    // keys in rank order, each depth at its offset
     int ord[kMaxCand];                      // creation index in rank order, each depth at its offset
     int tok[kMaxCand];
     int par[kMaxCand];
@@ -320,6 +321,9 @@ struct TreeSmem {
     int rank_of[kMaxCand];                  // overall rank, -1 if not selected
     int sel[kMaxMMax];                      // creation index by overall rank
     int prank[kMaxMMax];                    // parent's rank by rank (ancestor masks)
+    int gord[kMaxCand];                     // creation index by overall key order (policy 2)
+    int chain[kMaxDepth];                   // missing ancestors of one candidate (policy 2)
+    int m_out;                              // nodes selected
     int lvl_off[kMaxDepth + 1];             // first creation index of each depth, then N
 };
 
@@ -381,6 +385,7 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
     }
 
     const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
+    const bool conf_key = a.policy == EAGLE_POLICY_CONF || a.policy == EAGLE_POLICY_CONF_NO_RERANK;
     const int R = 1 + (D - 1) * k;
     // the rows' children in rank order, c = W35(l - M) / W
     for (int i = tid; i < R * C; i += NT) {
@@ -401,6 +406,7 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
     // depth 1: the children of the root's row 0, one list
     for (int j = tid; j < C; j += NT) {
         sm.V[j] = sm.conf[j];
+        sm.key[j] = sm.conf[j];
         sm.tok[j] = sm.cid[j];
         sm.par[j] = -1;
         sm.dep[j] = 1;
@@ -420,12 +426,12 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
             const int x0 = tid % lanes_x, q0 = tid / lanes_x;
             for (int x = x0; q0 < qstep && x < n; x += lanes_x) {
                 const int p = x / C, j = x - p * C;
-                const double vx = sm.V[off + x];
+                const double vx = sm.key[off + x];
                 int c = 0;
                 for (int q = q0; q < nl; q += qstep) {
                     // the whole list is read first (one LDS round trip); slots
                     // past C are read but not counted
-                    const double *L = sm.V + off + q * C;
+                    const double *L = sm.key + off + q * C;
                     double vl[kMaxChildren];
 #pragma unroll
                     for (int i = 0; i < kMaxChildren; ++i) vl[i] = L[i];
@@ -443,7 +449,7 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         for (int x = tid; x < n; x += NT) {
             const int r = sm.rank_d[off + x];
             sm.ord[off + r] = off + x;
-            sm.sV[off + r] = sm.V[off + x];
+            sm.sV[off + r] = sm.key[off + x];
         }
         __syncthreads();
         if (lv + 1 == D) break;
@@ -453,6 +459,7 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
             const int p = t / C, j = t - p * C;
             const int e = sm.ord[off + p], r = 1 + lv * k + p, g = noff + t;
             sm.V[g] = sm.V[e] * sm.conf[r * C + j];
+            sm.key[g] = conf_key ? sm.conf[r * C + j] : sm.V[g];
             sm.tok[g] = sm.cid[r * C + j];
             sm.par[g] = e;
             sm.dep[g] = lv + 2;
@@ -467,60 +474,131 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
     }
     const int N = off + n;
 
-    // ---- rerank: merge the depths' rank-ordered lists (first m of each) ----
-    // item = (entry i < m of depth lv, other depth od); the depth sizes follow
-    // from (C, k) alone, so items are located without reading LDS
     if (tid == 0) sm.lvl_off[D] = N;
     __syncthreads();
-    int items = 0;
-    if (D > 1) {
-        int nn = C;
-        for (int lv = 0; lv < D; ++lv) {
-            items += min(nn, m) * (D - 1);
-            nn = min(k, nn) * C;
-        }
-    }
-    for (int t = tid; t < items; t += NT) {
-        int lv = 0, nn = C, base = 0, o = 0;
-        while (base + min(nn, m) * (D - 1) <= t) {
-            base += min(nn, m) * (D - 1);
-            o += nn;
-            nn = min(k, nn) * C;
-            ++lv;
-        }
-        const int u = t - base, i = u / (D - 1);
-        int od = u - i * (D - 1);
-        od += od >= lv ? 1 : 0;
-        const double v = sm.sV[o + i];
-        const int so = sm.lvl_off[od];
-        const double *s = sm.sV + so;
-        const bool win_ties = od < lv;   // earlier depth: smaller creation indices
-        // the entries of od that come first are a prefix of its rank order
-        int lo = 0, hi = min(sm.lvl_off[od + 1] - so, m);
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            const double y = s[mid];
-            if (y > v || (win_ties && y == v)) lo = mid + 1;
-            else hi = mid;
-        }
-        if (lo) atomicAdd(&sm.ahead[sm.ord[o + i]], lo);
-    }
-    __syncthreads();
-    for (int g = tid; g < N; g += NT) {
-        const int rd = sm.rank_d[g];
-        if (rd < m) {
-            const int r = rd + sm.ahead[g];
-            if (r < m) {
-                sm.sel[r] = g;
-                sm.rank_of[g] = r;
+    if (a.policy == EAGLE_POLICY_EAGLE2) {
+        // ---- rerank: merge the depths' rank-ordered lists (first m of each) ----
+        // item = (entry i < m of depth lv, other depth od); the depth sizes follow
+        // from (C, k) alone, so items are located without reading LDS
+        int items = 0;
+        if (D > 1) {
+            int nn = C;
+            for (int lv = 0; lv < D; ++lv) {
+                items += min(nn, m) * (D - 1);
+                nn = min(k, nn) * C;
             }
         }
+        for (int t = tid; t < items; t += NT) {
+            int lv = 0, nn = C, base = 0, o = 0;
+            while (base + min(nn, m) * (D - 1) <= t) {
+                base += min(nn, m) * (D - 1);
+                o += nn;
+                nn = min(k, nn) * C;
+                ++lv;
+            }
+            const int u = t - base, i = u / (D - 1);
+            int od = u - i * (D - 1);
+            od += od >= lv ? 1 : 0;
+            const double v = sm.sV[o + i];
+            const int so = sm.lvl_off[od];
+            const double *s = sm.sV + so;
+            const bool win_ties = od < lv;   // earlier depth: smaller creation indices
+            // the entries of od that come first are a prefix of its rank order
+            int lo = 0, hi = min(sm.lvl_off[od + 1] - so, m);
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                const double y = s[mid];
+                if (y > v || (win_ties && y == v)) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo) atomicAdd(&sm.ahead[sm.ord[o + i]], lo);
+        }
+        __syncthreads();
+        for (int g = tid; g < N; g += NT) {
+            const int rd = sm.rank_d[g];
+            if (rd < m) {
+                const int r = rd + sm.ahead[g];
+                if (r < m) {
+                    sm.sel[r] = g;
+                    sm.rank_of[g] = r;
+                }
+            }
+        }
+        if (tid == 0) sm.m_out = m;
+        __syncthreads();
+    } else if (a.policy == EAGLE_POLICY_NO_RERANK || a.policy == EAGLE_POLICY_CONF_NO_RERANK) {
+        // no rerank: every depth's first k by the key, depth by depth
+        for (int g = tid; g < N; g += NT) {
+            const int lv = sm.dep[g] - 1, rd = sm.rank_d[g];
+            if (rd < k) {
+                int base = 0, nn = C;
+                for (int d = 0; d < lv; ++d) {
+                    base += min(k, nn);
+                    nn = min(k, nn) * C;
+                }
+                sm.sel[base + rd] = g;
+                sm.rank_of[g] = base + rd;
+            }
+        }
+        if (tid == 0) {
+            int tot = 0, nn = C;
+            for (int d = 0; d < D; ++d) {
+                tot += min(k, nn);
+                nn = min(k, nn) * C;
+            }
+            sm.m_out = tot;
+        }
+        __syncthreads();
+    } else {
+        // confidence rerank: every candidate's place in the overall key order
+        // (its rank in its depth plus, for every other depth, the entries that
+        // come first), then one thread takes the candidates in that order,
+        // each with its missing ancestors (root first), while the tree stays
+        // within m nodes
+        for (int t = tid; t < N * (D - 1); t += NT) {
+            const int g = t / (D - 1), lv = sm.dep[g] - 1;
+            int od = t - g * (D - 1);
+            od += od >= lv ? 1 : 0;
+            const double v = sm.key[g];
+            const int so = sm.lvl_off[od];
+            const double *sv = sm.sV + so;
+            const bool win_ties = od < lv;
+            int lo = 0, hi = sm.lvl_off[od + 1] - so;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                const double y = sv[mid];
+                if (y > v || (win_ties && y == v)) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo) atomicAdd(&sm.ahead[g], lo);
+        }
+        __syncthreads();
+        for (int g = tid; g < N; g += NT) {
+            const int r = sm.rank_d[g] + sm.ahead[g];
+            if (r < N) sm.gord[r] = g;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int n_sel = 0;
+            for (int t = 0; t < N && n_sel < m; ++t) {
+                int nc = 0;
+                for (int q = sm.gord[t]; q >= 0 && q < N && sm.rank_of[q] < 0 && nc < kMaxDepth; q = sm.par[q])
+                    sm.chain[nc++] = q;
+                if (nc == 0 || n_sel + nc > m) continue;
+                for (int c = nc - 1; c >= 0; --c) {
+                    sm.rank_of[sm.chain[c]] = n_sel;
+                    sm.sel[n_sel++] = sm.chain[c];
+                }
+            }
+            sm.m_out = n_sel;
+        }
+        __syncthreads();
     }
-    __syncthreads();
+    const int m_out = sm.m_out;
     // connected tree check: every selected node's parent is selected (then,
     // by induction, every ancestor is).  It holds by construction: c <= 1, so
     // V never grows along a path, and parents are created before children.
-    for (int r = tid; r < m; r += NT) {
+    for (int r = tid; r < m_out; r += NT) {
         const int i = sm.sel[r];
         const int q = sm.par[i];
         const int pr = q < 0 ? -1 : sm.rank_of[q];
@@ -532,10 +610,10 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         src_row[r] = sm.row[i];
         sm.prank[r] = pr;
     }
-    for (int r = m + tid; r < m_max; r += NT) {
+    for (int r = m_out + tid; r < m_max; r += NT) {
         tokens[r] = -1; parent[r] = -1; depth[r] = -1; score[r] = 0.0; src_row[r] = -1;
     }
-    if (tid == 0) a.num_nodes[b] = m;
+    if (tid == 0) a.num_nodes[b] = m_out;
     if (a.anc) {
         // ancestor masks: node r and the nodes on its path to the root (rank
         // order is topological, so parents have smaller ranks); position =
@@ -545,12 +623,12 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         for (int r = tid; r < m_max; r += NT) {
             uint64_t acc = 0;
             int pos = -1;
-            if (r < m) {
+            if (r < m_out) {
                 acc = 1ull << r;
                 // (bounded: a tree with non-finite scores, already reported,
                 // may leave ranks unassigned)
                 int q = sm.prank[r];
-                for (int it = 0; it < kMaxMMax && q >= 0 && q < m; ++it, q = sm.prank[q]) acc |= 1ull << q;
+                for (int it = 0; it < kMaxMMax && q >= 0 && q < m_out; ++it, q = sm.prank[q]) acc |= 1ull << q;
                 pos = L + __popcll(acc) - 1;
             }
             a.anc[(size_t)b * m_max + r] = acc;
@@ -574,6 +652,7 @@ constexpr int kFrontierThreads = 256;
 __global__ __launch_bounds__(kFrontierThreads) void k_tree_frontier(FrontierArgs a)
 {
     __shared__ double V[kMaxTopk * kMaxChildren];
+    __shared__ double key[kMaxTopk * kMaxChildren];   // ranking key: V, or c (confidence policies)
     __shared__ int in_order;
     const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x;
     const int C = a.children, k = a.topk, lv = a.level;
@@ -599,21 +678,22 @@ __global__ __launch_bounds__(kFrontierThreads) void k_tree_frontier(FrontierArgs
         const double W = a.W[r];
         const double c = (double)weight_of(a.top_v[r * C + j], M) / W;
         V[x] = lv == 0 ? c : fV[p] * c;
+        key[x] = (a.policy == EAGLE_POLICY_CONF || a.policy == EAGLE_POLICY_CONF_NO_RERANK) ? c : V[x];
         if (j == 0 && (!__builtin_isfinite(M) || !__builtin_isfinite(W))) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
     }
     __syncthreads();   // fV is read: it may now be overwritten
     const int ne = lv + 1 < a.depth_max ? min(k, n) : 0;   // depth D is not expanded
     for (int x = tid; x < n; x += NT) {
-        const double vx = V[x];
+        const double kx = key[x];
         int rk = 0;
-        for (int y = 0; y < n; ++y) rk += (V[y] > vx || (V[y] == vx && y < x)) ? 1 : 0;
+        for (int y = 0; y < n; ++y) rk += (key[y] > kx || (key[y] == kx && y < x)) ? 1 : 0;
         if (rk < ne) {
             const int p = x / C, j = x - p * C;
             const size_t r = rb + (lv == 0 ? 0 : 1 + (size_t)(lv - 1) * k + p);
             f_tok[rk] = a.top_id[r * C + j];
             f_par[rk] = lv == 0 ? -1 : p;
-            f_score[rk] = vx;
-            fV[rk] = vx;
+            f_score[rk] = V[x];
+            fV[rk] = V[x];
         }
     }
     if (tid == 0) {
@@ -738,6 +818,7 @@ static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const
     ta.chain_k = p->chain_k;
     ta.m_max = p->m_max;
     ta.r_max = p->r_max;
+    ta.policy = p->policy;
     ta.top_id = ra.top_id;
     ta.top_v = ra.top_v;
     ta.M = ra.M;
@@ -801,6 +882,7 @@ hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t
     fa.topk = p->topk;
     fa.children = p->children;
     fa.r_max = p->r_max;
+    fa.policy = p->policy;
     fa.M = ra.M;
     fa.W = ra.W;
     fa.top_id = ra.top_id;

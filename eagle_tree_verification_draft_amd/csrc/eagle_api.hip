@@ -67,6 +67,18 @@ eagle_status check_tree_params(const eagle_tree_params *p, int32_t batch)
     if (rows_dyn > p->r_max) return fail(EAGLE_ERR_INVALID, "dynamic trees use %lld rows > r_max %d", rows_dyn, p->r_max);
     if (p->chain_k < 0 || p->chain_k > p->m_max || p->chain_k > p->r_max)
         return fail(EAGLE_ERR_INVALID, "chain_k %d not in [0, min(m_max, r_max)]", p->chain_k);
+    if (p->policy < EAGLE_POLICY_EAGLE2 || p->policy > EAGLE_POLICY_CONF_NO_RERANK)
+        return fail(EAGLE_ERR_INVALID, "tree policy %d", p->policy);
+    if (p->policy == EAGLE_POLICY_NO_RERANK || p->policy == EAGLE_POLICY_CONF_NO_RERANK) {
+        // every depth's top k: sum over depths of min(k, candidates of the depth)
+        long long tot = 0, nn = p->children;
+        for (int d = 0; d < p->depth; ++d) {
+            tot += nn < p->topk ? nn : p->topk;
+            nn = (nn < p->topk ? nn : p->topk) * (long long)p->children;
+        }
+        if (tot > p->m_max)
+            return fail(EAGLE_ERR_INVALID, "a tree without rerank has %lld nodes > m_max %d", tot, p->m_max);
+    }
     return EAGLE_OK;
 }
 

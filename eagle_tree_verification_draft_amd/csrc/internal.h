@@ -32,7 +32,7 @@ struct RowStatsArgs {
 
 struct TreeSelectArgs {
     const int32_t *kind;
-    int depth_max, topk, children, m, chain_k, m_max, r_max;
+    int depth_max, topk, children, m, chain_k, m_max, r_max, policy;
     const float *M;
     const double *W;
     const int32_t *top_id;
@@ -49,7 +49,7 @@ struct TreeSelectArgs {
 
 // incremental build: one level of draft rows at a time
 struct FrontierArgs {
-    int level, depth_max, topk, children, r_max;
+    int level, depth_max, topk, children, r_max, policy;
     const float *M;
     const double *W;
     const int32_t *top_id;

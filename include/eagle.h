@@ -56,6 +56,15 @@ typedef enum {
 typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 typedef enum { EAGLE_TREE_DYNAMIC = 0, EAGLE_TREE_CHAIN = 1 } eagle_tree_kind;
 typedef enum { EAGLE_ACCEPT_GREEDY = 0, EAGLE_ACCEPT_SAMPLE = 1 } eagle_accept_mode;
+/* dynamic-tree policies; the last three are the ablations of EAGLE-2
+   explainer, "Results" (ablation table: no global acceptance probability,
+   i.e. ranking by confidence only; no rerank) */
+typedef enum {
+    EAGLE_POLICY_EAGLE2 = 0,          /* rank by V; rerank: the top m by V */
+    EAGLE_POLICY_NO_RERANK = 1,       /* rank by V; the tree is every depth's top k */
+    EAGLE_POLICY_CONF = 2,            /* rank by the node's own c; rerank within m (below) */
+    EAGLE_POLICY_CONF_NO_RERANK = 3   /* rank by c; the tree is every depth's top k */
+} eagle_tree_policy;
 
 /* device error bits (sticky until the workspace is re-initialised) */
 #define EAGLE_DEVERR_NONFINITE_ROW 0x1u  /* a logit row had a NaN, +Inf or all -Inf */
@@ -93,6 +102,21 @@ eagle_status eagle_read_errors(void *workspace, void *stream, uint32_t *host_bit
  * rank, child rank).  Chain sequences (P-EAGLE, "Parallel drafting": all K
  * tokens from one pass) take token i = argmax of row i (ties -> smallest id),
  * parent i-1, and own row i+1.
+ * Policies (EAGLE-2 explainer, "Results", ablation table) change the ranking
+ * key and the final selection; the expansion always takes each depth's
+ * first k by the key:
+ *   EAGLE2:          key V; the top m by V, output in that order;
+ *   NO_RERANK:       key V; the tree is every depth's first k (at most
+ *                    sum over depths of min(k, depth's candidates) <= m_max
+ *                    nodes), output depth by depth in key order;
+ *   CONF:            key c, the node's own confidence; the candidates are
+ *                    taken in key order, each with its ancestors not yet
+ *                    taken (root first), skipping any that would take the
+ *                    tree past m nodes (the pages add the ancestors of the
+ *                    selected tokens); output in the order taken, so num_nodes
+ *                    may be below m;
+ *   CONF_NO_RERANK:  key c; as NO_RERANK.
+ * score is V in every policy.
  */
 typedef struct {
     int32_t depth;      /* D >= 1: draft tokens sit at depths 1..D */
@@ -103,6 +127,7 @@ typedef struct {
     int32_t vocab;      /* V in [C, 131072] */
     int32_t m_max;      /* output slots per sequence, <= 64 */
     int32_t r_max;      /* draft rows per sequence in draft_logits (>= rows used) */
+    int32_t policy;     /* an eagle_tree_policy value, for dynamic trees (0: EAGLE-2) */
 } eagle_tree_params;
 
 size_t eagle_build_tree_workspace_size(const eagle_tree_params *p, int32_t batch);
@@ -111,13 +136,15 @@ size_t eagle_build_tree_workspace_size(const eagle_tree_params *p, int32_t batch
  * draft_logits [batch][r_max][row_stride] (dtype); row_stride >= vocab, in
  *   elements; rows used: 1 + (D-1)k for dynamic trees, K for chains.
  * kind [batch] eagle_tree_kind, or NULL for all-dynamic.
- * Outputs [batch][m_max], in rank order (topological: parent index < child
- * index), padded with -1 (score 0):
+ * Outputs [batch][m_max], in the policy's output order (topological: parent
+ * index < child index), padded with -1 (score 0):
  *   tokens   token ids;            parent   parent's index (-1 = root)
  *   depth    1..D (chains 1..K);   score    V as fp64
  *   src_row  draft row owned by the node if it was expanded, else -1
- * num_nodes [batch]: m for dynamic trees, K for chains.
- * Errors: EAGLE_ERR_INVALID for null pointers, m > candidates, rows > r_max;
+ * num_nodes [batch]: m for dynamic trees under EAGLE2 (the node count for
+ * the other policies), K for chains.
+ * Errors: EAGLE_ERR_INVALID for null pointers, m > candidates, rows > r_max,
+ * an unknown policy or a tree without rerank larger than m_max;
  * EAGLE_ERR_UNSUPPORTED past the v1 limits; EAGLE_ERR_WORKSPACE if the
  * workspace is smaller than eagle_build_tree_workspace_size().
  */

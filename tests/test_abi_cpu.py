@@ -175,6 +175,23 @@ def test_pdraft_prepare_rejects_bad_params():
     assert call(ok, batch=0) == E.EAGLE_OK
 
 
+def test_tree_policy_validation():
+    L = E.lib()
+    x = C.c_void_p(1 << 24)
+
+    def call(**over):
+        p = _tree(**over)
+        need = max(256, L.eagle_build_tree_workspace_size(C.byref(p), 1))
+        return L.eagle_build_tree(C.byref(p), 0, x, 1, 32000, None, x, x, x, x, x, x, C.c_void_p(1 << 21), need, None)
+
+    assert call(policy=4) == E.EAGLE_ERR_INVALID
+    assert call(policy=-1) == E.EAGLE_ERR_INVALID
+    assert call(policy=E.EAGLE_POLICY_CONF) == E.EAGLE_OK
+    # without rerank the tree has 10 + 5 * 10 = 60 nodes: m_max 59 is too small
+    assert call(policy=E.EAGLE_POLICY_NO_RERANK, m_max=59, m=50) == E.EAGLE_ERR_INVALID
+    assert call(policy=E.EAGLE_POLICY_CONF_NO_RERANK, m_max=60, m=50) == E.EAGLE_OK
+
+
 def test_accept_and_mask_reject_bad_params():
     L = E.lib()
     p = C.c_void_p(1 << 24)
