@@ -277,6 +277,7 @@ def main():
     log(f"[bench] kv commit {commit['avg_us']:.2f} us/call for {commit['tokens']} tokens")
     expand = measure_expand(E, step, w, sets[0], kinds, K)
     pdraft = measure_pdraft(E, step, w, sets[0], kinds, K)
+    policies = measure_policies(E, w, sets[0], kinds, K)
     log(f"[bench] parallel-draft inputs {pdraft['avg_us']:.2f} us/call, {pdraft['hbm_gbs']:.0f} GB/s")
     if expand:
         log(f"[bench] incremental build {expand['total_us']:.1f} us for {expand['levels']} levels + finish")
@@ -340,6 +341,7 @@ def main():
         "kv_commit": commit,
         "tree_expand": expand,
         "pdraft_prepare": pdraft,
+        "tree_policies": policies,
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
         "launch": "hipGraph replay per step" if graphs is not None else "eager",
         "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
@@ -394,6 +396,56 @@ def measure_commit(E, step, w, S, kinds, reps):
     assert torch.equal(plo, plen + step.accept_len), "kv commit did not write every accepted token"
     return {"call": "eagle_kv_commit (k_kv_commit)", "avg_us": round(us, 2), "timed_calls": n * per_graph,
             "tokens": tokens, "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def measure_policies(E, w, S, kinds, reps):
+    """eagle_build_tree under each tree policy on input set 0's draft rows
+    (outside the step; m_max 64 so that every policy's tree fits): HIP events
+    around replays of a graph of 10 calls.  us per call, and the mean node
+    count per sequence."""
+    import torch
+    out = {}
+    B = w.batch
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bufs = [torch.empty((B, 64), **i32) for _ in range(4)]
+    score = torch.empty((B, 64), dtype=torch.float64, device="cuda")
+    nn = torch.empty((B,), **i32)
+    names = {E.EAGLE_POLICY_EAGLE2: "eagle2", E.EAGLE_POLICY_NO_RERANK: "no_rerank",
+             E.EAGLE_POLICY_CONF: "confidence", E.EAGLE_POLICY_CONF_NO_RERANK: "confidence_no_rerank"}
+    for pol, name in names.items():
+        p = E.TreeParams(w.depth, w.topk, w.children, w.m, w.chain_k, w.vocab, 64, w.r_max, pol)
+        if E.build_tree_workspace_size(p, B) == 0:
+            out[name] = None   # the tree does not fit
+            continue
+        ws = torch.empty(E.build_tree_workspace_size(p, B), dtype=torch.uint8, device="cuda")
+        E.workspace_init(ws)
+
+        def call():
+            E.build_tree(p, B, S["draft"], kinds, bufs[0], bufs[1], bufs[2], score, bufs[3], nn, ws)
+
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            call()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(10):
+                call()
+        g.replay()
+        n = max(1, reps // 10)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record()
+        for _ in range(n):
+            g.replay()
+        eb.record()
+        torch.cuda.synchronize()
+        assert E.read_errors(ws) == 0, f"tree policy {name} reported device errors"
+        out[name] = {"build_us": round(ea.elapsed_time(eb) * 1e3 / (n * 10), 2),
+                     "mean_nodes": round(float(nn.float().mean().item()), 2)}
+    return out
 
 
 def measure_pdraft(E, step, w, S, kinds, reps):
