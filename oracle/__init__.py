@@ -49,6 +49,7 @@ def lib():
         L.orc_row_stats.argtypes = [vp, i32, i64, i32, i32, i32, f32, vp, vp, vp, vp]
         L.orc_build_tree.argtypes = [vp, i32, vp, i32, i64, i32, vp, i32, vp, vp, vp, vp, vp, vp,
                                      i32, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_build_tree_template.argtypes = [i32, i32, vp, vp, i32, i32, vp, i32, i64, i32, i32] + [vp] * 6
         L.orc_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp]
         L.orc_tree_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_tree_attn_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
@@ -56,7 +57,7 @@ def lib():
         L.orc_pdraft_prepare.argtypes = [i32] * 7 + [vp] * 16
         L.orc_accept.argtypes = [i32, f32, i32, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp]
         for f in ("orc_row_stats", "orc_build_tree", "orc_tree_mask", "orc_tree_attn",
-                  "orc_tree_attn_rows", "orc_kv_commit", "orc_pdraft_prepare", "orc_accept", "orc_num_threads"):
+                  "orc_tree_attn_rows", "orc_build_tree_template", "orc_kv_commit", "orc_pdraft_prepare", "orc_accept", "orc_num_threads"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -145,6 +146,24 @@ def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_
     _check(code, "build_tree")
     if debug:
         out["cand"] = dbg
+    return out
+
+
+def build_tree_template(draft_logits, tmpl_parent, tmpl_child, children, m_max=None):
+    """EAGLE-1 static tree: template node i is the tmpl_child[i]-th top token of
+    its parent's row (see oracle.c).  draft_logits [B][R_max][V]."""
+    a, dt = _logits(draft_logits)
+    B, R, V = a.shape
+    tp = np.ascontiguousarray(tmpl_parent, dtype=np.int32)
+    tc = np.ascontiguousarray(tmpl_child, dtype=np.int32)
+    n_t = len(tp)
+    m_max = n_t if m_max is None else m_max
+    out = {k: np.zeros((B, m_max), np.int32) for k in ("tokens", "parent", "depth", "src_row")}
+    out["score"] = np.zeros((B, m_max), np.float64)
+    out["num_nodes"] = np.zeros(B, np.int32)
+    _check(lib().orc_build_tree_template(B, n_t, _p(tp), _p(tc), children, V, _p(a), dt, V, R, m_max,
+                                         _p(out["tokens"]), _p(out["parent"]), _p(out["depth"]), _p(out["score"]),
+                                         _p(out["src_row"]), _p(out["num_nodes"])), "build_tree_template")
     return out
 
 

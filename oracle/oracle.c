@@ -444,6 +444,62 @@ int orc_build_tree(const orc_tree_params *p, int batch, const void *draft_logits
     return err;
 }
 
+/*
+ * EAGLE-1's static tree (EAGLE-2 explainer, "Differences from EAGLE-1": a
+ * fixed tree template, optimised offline, where EAGLE-2 builds the tree from
+ * the draft's confidences).  Template node i (parents first: tparent[i] in
+ * [-1, i), -1 = the root) is the tchild[i]-th token, by (logit desc, id asc),
+ * of its parent's draft row; the root owns row 0 and the q-th template node
+ * (in template order) that has children owns row 1 + q.  c and V as in the
+ * dynamic build; outputs in template order.
+ */
+int orc_build_tree_template(int batch, int n_t, const int *tparent, const int *tchild, int C, int V,
+                            const void *draft_logits, int dtype, int64_t row_stride, int r_max, int m_max,
+                            int *tokens, int *parent, int *depth, double *score, int *src_row, int *num_nodes)
+{
+    if (batch < 0 || n_t < 1 || n_t > m_max || m_max > 64 || C < 1 || C > 64 || V < C || V > (1 << 17))
+        return ORC_ERR_ARG;
+    int row_of[64], internal = 0;
+    for (int i = 0; i < n_t; ++i) {
+        if (tparent[i] < -1 || tparent[i] >= i || tchild[i] < 0 || tchild[i] >= C) return ORC_ERR_ARG;
+        row_of[i] = -1;
+    }
+    for (int i = 0; i < n_t; ++i)
+        for (int j = i + 1; j < n_t; ++j)
+            if (tparent[j] == i) { row_of[i] = 1 + internal++; break; }
+    if (1 + internal > r_max) return ORC_ERR_ARG;
+    const size_t esz = dtype == 0 ? 4 : 2;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        float M[65];
+        double W[65], tw[65 * 64], Vn[64];
+        int tid[65 * 64], dep[64];
+        const char *rows = (const char *)draft_logits + (size_t)b * r_max * row_stride * esz;
+        int e = ORC_OK;
+        for (int r = 0; r <= internal && e == ORC_OK; ++r)
+            e = row_stats_one(rows + (size_t)r * row_stride * esz, dtype, V, C, 1.0f, &M[r], &W[r],
+                              &tid[r * C], &tw[r * C]);
+        int *tk = tokens + (size_t)b * m_max, *pa = parent + (size_t)b * m_max, *de = depth + (size_t)b * m_max;
+        int *sr = src_row + (size_t)b * m_max;
+        double *sc = score + (size_t)b * m_max;
+        for (int i = 0; i < m_max; ++i) { tk[i] = -1; pa[i] = -1; de[i] = -1; sc[i] = 0.0; sr[i] = -1; }
+        if (e == ORC_OK) {
+            for (int i = 0; i < n_t; ++i) {
+                const int p = tparent[i], r = p < 0 ? 0 : row_of[p], j = tchild[i];
+                Vn[i] = (p < 0 ? 1.0 : Vn[p]) * (tw[r * C + j] / W[r]);
+                dep[i] = p < 0 ? 1 : dep[p] + 1;
+                tk[i] = tid[r * C + j]; pa[i] = p; de[i] = dep[i]; sc[i] = Vn[i]; sr[i] = row_of[i];
+            }
+            num_nodes[b] = n_t;
+        } else {
+#pragma omp critical
+            err = e;
+        }
+    }
+    return err;
+}
+
 /* ------------------------------------------------------------------ */
 /* ancestor mask and positions                                          */
 /* ------------------------------------------------------------------ */

@@ -412,3 +412,47 @@ def test_confidence_rerank_hand_example(orc):
     # no rerank by c: depth 1 keeps token 0, depth 2 token 2, depth 3 token 0
     t = orc.build_tree(logits, 3, 1, 2, 2, m_max=4, policy=3)
     assert t["num_nodes"][0] == 3 and t["tokens"][0, :3].tolist() == [0, 2, 0]
+
+
+def test_template_chain_equals_chain_mode(orc):
+    """A chain template (node i the top token of node i-1's row) is the chain
+    mode of the build: same tokens, parents, depths, rows and V bit for bit."""
+    w = synth.small_workload(2, batch=2, vocab=3000)
+    logits = _rows_np(w, 61)[:, :7]
+    K = 7
+    tc = orc.build_tree(logits, 1, 1, 1, 1, chain_k=K, kinds=[1, 1], m_max=K)
+    tt = orc.build_tree_template(logits, list(range(-1, K - 1)), [0] * K, children=4, m_max=K)
+    for k in ("tokens", "parent", "depth", "score", "src_row", "num_nodes"):
+        assert np.array_equal(tt[k], tc[k]), k
+
+
+@pytest.mark.parametrize("seed", [62, 63])
+def test_template_nodes_follow_their_parents_rows(orc, seed):
+    """A random template: each node is the chosen rank of its parent's row
+    (spec_emul restatement of Spec S), V the product of c from the root down,
+    rows owned by the nodes with children in template order."""
+    rng = np.random.default_rng(seed)
+    C, n_t = 5, 30
+    tp = [-1] + [int(rng.integers(-1, i)) for i in range(1, n_t)]
+    tch = [int(rng.integers(0, C)) for _ in range(n_t)]
+    internal = [i for i in range(n_t) if i in tp[i + 1:]]
+    w = synth.small_workload(1, batch=2, vocab=1000)
+    logits = _rows_np(w, seed)
+    R = 1 + len(internal)
+    if logits.shape[1] < R:
+        logits = np.concatenate([logits] * (R // logits.shape[1] + 1), axis=1)
+    logits = np.ascontiguousarray(logits[:, :R])
+    t = orc.build_tree_template(logits, tp, tch, children=C, m_max=32)
+    row_of = {i: 1 + q for q, i in enumerate(internal)}
+    for b in range(2):
+        V = {}
+        for i in range(n_t):
+            p = tp[i]
+            r = 0 if p < 0 else row_of[p]
+            _, W, ids, ws = spec_emul.row_stats(logits[b, r], C)
+            V[i] = (1.0 if p < 0 else V[p]) * (ws[tch[i]] / W)
+            assert t["tokens"][b, i] == ids[tch[i]]
+            assert t["score"][b, i] == V[i]
+            assert t["parent"][b, i] == p
+            assert t["src_row"][b, i] == row_of.get(i, -1)
+        assert t["num_nodes"][b] == n_t and (t["tokens"][b, n_t:] == -1).all()
