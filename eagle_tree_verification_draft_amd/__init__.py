@@ -33,7 +33,7 @@ DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 
 EXPORTS = (
     "eagle_workspace_init", "eagle_read_errors",
     "eagle_build_tree_workspace_size", "eagle_build_tree",
-    "eagle_build_tree_mask", "eagle_tree_expand", "eagle_tree_finish",
+    "eagle_build_tree_mask", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
     "eagle_tree_mask",
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
     "eagle_kv_commit",
@@ -90,6 +90,7 @@ def lib() -> C.CDLL:
                                        vp, sz, vp]
         L.eagle_build_tree_mask.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, sz, vp]
+        L.eagle_build_tree_template.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, i32] + [vp] * 9 + [sz, vp]
         L.eagle_tree_expand.argtypes = [C.POINTER(TreeParams), i32, i32, vp, C.c_int, i64, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_finish.argtypes = [C.POINTER(TreeParams), i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -108,8 +109,8 @@ def lib() -> C.CDLL:
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
         for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_build_tree_mask",
-                  "eagle_tree_expand", "eagle_tree_finish", "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit",
-                  "eagle_accept", "eagle_pdraft_prepare"):
+                  "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish", "eagle_tree_mask",
+                  "eagle_tree_attn", "eagle_kv_commit", "eagle_accept", "eagle_pdraft_prepare"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -194,6 +195,18 @@ def build_tree_mask(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind:
                                        _ptr(src_row), _ptr(num_nodes), _ptr(anc_mask), _ptr(pos), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_build_tree_mask")
+
+
+def build_tree_template(p: TreeParams, batch: int, draft_logits: torch.Tensor, tmpl_parent, tmpl_child, tokens,
+                        parent, depth, score, src_row, num_nodes, workspace: torch.Tensor, stream=None):
+    """EAGLE-1 static tree from a template (device int32 arrays)."""
+    rows, stride = _rows(draft_logits)
+    _check(lib().eagle_build_tree_template(C.byref(p), batch, rows, dtype_code(draft_logits.dtype), stride,
+                                           tmpl_parent.numel(), _ptr(tmpl_parent), _ptr(tmpl_child), _ptr(tokens),
+                                           _ptr(parent), _ptr(depth), _ptr(score), _ptr(src_row), _ptr(num_nodes),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)),
+           "eagle_build_tree_template")
 
 
 def tree_expand(p: TreeParams, batch: int, level: int, level_logits: torch.Tensor, frontier_tokens,

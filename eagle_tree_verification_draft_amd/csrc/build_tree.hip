@@ -703,6 +703,73 @@ __global__ __launch_bounds__(kFrontierThreads) void k_tree_frontier(FrontierArgs
 }
 
 // ---------------------------------------------------------------------------
+// EAGLE-1's static tree: template node i (parents first) is the tchild[i]-th
+// top token of its parent's row; the root owns row 0 and the q-th template
+// node with children owns row 1 + q.  One wave per sequence, lane i = node i
+// (templates of up to 64 nodes); V is formed root first by one lane, as the
+// dynamic build forms it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_tree_template(TemplateArgs a)
+{
+    __shared__ double sV[kMaxMMax];
+    __shared__ double sc[kMaxMMax];
+    __shared__ int sdep[kMaxMMax];
+    __shared__ int spar[kMaxMMax];
+    const int b = blockIdx.x, i = threadIdx.x, n = a.n_t, C = a.children;
+    const size_t rb = (size_t)b * a.r_max;
+    int32_t *tokens = a.tokens + (size_t)b * a.m_max, *parent = a.parent + (size_t)b * a.m_max;
+    int32_t *depth = a.depth + (size_t)b * a.m_max, *src_row = a.src_row + (size_t)b * a.m_max;
+    double *score = a.score + (size_t)b * a.m_max;
+    const int p = i < n ? a.tparent[i] : -1, j = i < n ? a.tchild[i] : 0;
+    const bool bad_node = i < n && (p < -1 || p >= i || j < 0 || j >= C);
+    // rows: node q owns one iff some node names it as parent
+    bool has_child = false;
+    for (int q = 0; q < n; ++q) has_child |= __shfl(p, q) == i;
+    const unsigned long long owners = __ballot(i < n && has_child);
+    const int row = has_child ? 1 + __popcll(owners & ((1ull << i) - 1)) : -1;
+    const bool bad = __ballot(bad_node) != 0 || 1 + __popcll(owners) > a.r_max;
+    if (bad) {
+        // an invalid template: an empty tree
+        if (i == 0) {
+            raise_error(a.err, EAGLE_DEVERR_TREE);
+            a.num_nodes[b] = 0;
+        }
+        if (i < a.m_max) { tokens[i] = -1; parent[i] = -1; depth[i] = -1; score[i] = 0.0; src_row[i] = -1; }
+        return;
+    }
+    // the parent's row and this node's token and confidence
+    const int prow_any = __shfl(row, p < 0 ? 0 : p);   // every lane takes part in the shuffle
+    const int prow = p < 0 ? 0 : prow_any;
+    int tok = -1;
+    spar[i] = p;
+    if (i < n) {
+        const size_t o = (rb + prow) * C + j;
+        const float M = a.M[rb + prow];
+        const double W = a.W[rb + prow];
+        tok = a.top_id[o];
+        sc[i] = (double)weight_of(a.top_v[o], M) / W;
+        if (!__builtin_isfinite(M) || !__builtin_isfinite(W)) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+    }
+    __syncthreads();
+    if (i == 0) {
+        for (int q = 0; q < n; ++q) {
+            const int pq = spar[q];
+            sV[q] = (pq < 0 ? 1.0 : sV[pq]) * sc[q];
+            sdep[q] = pq < 0 ? 1 : sdep[pq] + 1;
+        }
+    }
+    __syncthreads();
+    if (i < a.m_max) {
+        tokens[i] = i < n ? tok : -1;
+        parent[i] = i < n ? p : -1;
+        depth[i] = i < n ? sdep[i] : -1;
+        score[i] = i < n ? sV[i] : 0.0;
+        src_row[i] = i < n ? row : -1;
+    }
+    if (i == 0) a.num_nodes[b] = n;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 BuildLayout build_layout(const eagle_tree_params *p, int32_t batch)
@@ -863,6 +930,38 @@ hipError_t launch_build_tree_mask(const eagle_tree_params *p, int32_t batch, con
     if (e != hipSuccess) return e;
     return launch_select(p, batch, ra, kind, nullptr, tokens, parent, depth, score, src_row, num_nodes, st,
                          prefix_len, anc, pos);
+}
+
+hipError_t launch_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *logits,
+                                     eagle_dtype dt, int64_t row_stride, int32_t n_tmpl, const int32_t *tparent,
+                                     const int32_t *tchild, int32_t *tokens, int32_t *parent, int32_t *depth,
+                                     double *score, int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    RowStatsArgs ra = row_stats_args(p, batch, L, ws, logits, dt, row_stride, nullptr, p->r_max, 0);
+    ra.rows_dyn = p->r_max;   // every row of the template's layout
+    hipError_t e = launch_row_stats(ra, dt, st);
+    if (e != hipSuccess) return e;
+    TemplateArgs ta;
+    ta.n_t = n_tmpl;
+    ta.children = p->children;
+    ta.r_max = p->r_max;
+    ta.m_max = p->m_max;
+    ta.tparent = tparent;
+    ta.tchild = tchild;
+    ta.M = ra.M;
+    ta.W = ra.W;
+    ta.top_id = ra.top_id;
+    ta.top_v = ra.top_v;
+    ta.tokens = tokens;
+    ta.parent = parent;
+    ta.depth = depth;
+    ta.score = score;
+    ta.src_row = src_row;
+    ta.num_nodes = num_nodes;
+    ta.err = ra.err;
+    hipLaunchKernelGGL(k_tree_template, dim3((unsigned)batch), dim3(64), 0, st, ta);
+    return hipGetLastError();
 }
 
 hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level, const void *logits,

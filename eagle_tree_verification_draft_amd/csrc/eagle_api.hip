@@ -165,6 +165,35 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                       "build_tree_mask launch");
 }
 
+eagle_status eagle_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                       eagle_dtype dtype, int64_t row_stride, int32_t n_tmpl,
+                                       const int32_t *tmpl_parent, const int32_t *tmpl_child, int32_t *tokens,
+                                       int32_t *parent, int32_t *depth, double *score, int32_t *src_row,
+                                       int32_t *num_nodes, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!p) return fail(EAGLE_ERR_INVALID, "tree params are NULL");
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (p->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", p->vocab);
+    if (p->vocab > kMaxVocab) return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d > %d", p->vocab, kMaxVocab);
+    if (p->children < 1 || p->children > p->vocab)
+        return fail(EAGLE_ERR_INVALID, "children %d not in [1, vocab]", p->children);
+    if (p->children > kMaxChildren) return fail(EAGLE_ERR_UNSUPPORTED, "children %d > %d", p->children, kMaxChildren);
+    if (p->m_max < 1 || p->m_max > kMaxMMax) return fail(EAGLE_ERR_INVALID, "m_max %d not in [1, %d]", p->m_max, kMaxMMax);
+    if (p->r_max < 1) return fail(EAGLE_ERR_INVALID, "r_max %d < 1", p->r_max);
+    if (n_tmpl < 1 || n_tmpl > p->m_max) return fail(EAGLE_ERR_INVALID, "template of %d nodes not in [1, m_max]", n_tmpl);
+    if (!draft_logits || !tmpl_parent || !tmpl_child || !tokens || !parent || !depth || !score || !src_row || !num_nodes)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
+    eagle_status s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_build_tree_template(p, batch, draft_logits, dtype, row_stride, n_tmpl, tmpl_parent,
+                                                 tmpl_child, tokens, parent, depth, score, src_row, num_nodes,
+                                                 workspace, (hipStream_t)stream),
+                      "build_tree_template launch");
+}
+
 eagle_status eagle_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level,
                                const void *level_logits, eagle_dtype dtype, int64_t row_stride,
                                int32_t *frontier_tokens, int32_t *frontier_parent, double *frontier_score,

@@ -62,6 +62,20 @@ struct FrontierArgs {
     uint32_t *err;
 };
 
+// EAGLE-1 static template tree
+struct TemplateArgs {
+    int n_t, children, r_max, m_max;
+    const int32_t *tparent, *tchild;
+    const float *M;
+    const double *W;
+    const int32_t *top_id;
+    const float *top_v;
+    int32_t *tokens, *parent, *depth;
+    double *score;
+    int32_t *src_row, *num_nodes;
+    uint32_t *err;
+};
+
 struct BuildLayout {
     size_t off_M, off_W, off_id, off_v;
     size_t off_fV, off_fn, off_lv;   // incremental-build state
@@ -81,6 +95,10 @@ hipError_t launch_build_tree_mask(const eagle_tree_params *p, int32_t batch, con
                                   const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
                                   double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc,
                                   int32_t *pos, void *ws, hipStream_t st);
+hipError_t launch_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *logits,
+                                     eagle_dtype dt, int64_t row_stride, int32_t n_tmpl, const int32_t *tparent,
+                                     const int32_t *tchild, int32_t *tokens, int32_t *parent, int32_t *depth,
+                                     double *score, int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st);
 hipError_t launch_tree_expand(const eagle_tree_params *p, int32_t batch, int32_t level, const void *logits,
                               eagle_dtype dt, int64_t row_stride, int32_t *f_tok, int32_t *f_par,
                               double *f_score, void *ws, hipStream_t st);

@@ -167,6 +167,30 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                                    double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc_mask,
                                    int32_t *pos, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * EAGLE-1's static tree (EAGLE-2 explainer, "Differences from EAGLE-1": a
+ * fixed tree template, optimised offline, where EAGLE-2 builds the tree from
+ * the draft's confidences).  tmpl_parent / tmpl_child [n_tmpl] (device
+ * arrays, parents first: tmpl_parent[i] in [-1, i), -1 = the root;
+ * tmpl_child[i] in [0, children)): node i is the tmpl_child[i]-th token, by
+ * (logit desc, id asc), of its parent's draft row.  The root owns row 0 and
+ * the q-th node (in template order) with children owns row 1 + q, so the
+ * draft rows are [batch][r_max][row_stride] with r_max >= 1 + (nodes with
+ * children); every one of the r_max rows is read.  Outputs as
+ * eagle_build_tree, in template order; score is V; num_nodes = n_tmpl.  Uses
+ * children, vocab, m_max and r_max of the params.
+ * Device errors: EAGLE_DEVERR_TREE for an invalid template or one needing
+ * more than r_max rows (every sequence then gets an empty tree);
+ * NONFINITE_ROW as eagle_build_tree.
+ * Errors: EAGLE_ERR_INVALID for null pointers or n_tmpl outside [1, m_max];
+ * the other parameter checks of eagle_build_tree.
+ */
+eagle_status eagle_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                       eagle_dtype dtype, int64_t row_stride, int32_t n_tmpl,
+                                       const int32_t *tmpl_parent, const int32_t *tmpl_child, int32_t *tokens,
+                                       int32_t *parent, int32_t *depth, double *score, int32_t *src_row,
+                                       int32_t *num_nodes, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Incremental tree build                                              */
 /* ------------------------------------------------------------------ */

@@ -192,6 +192,26 @@ def test_tree_policy_validation():
     assert call(policy=E.EAGLE_POLICY_CONF_NO_RERANK, m_max=60, m=50) == E.EAGLE_OK
 
 
+def test_build_tree_template_rejects_bad_params():
+    L = E.lib()
+    x = C.c_void_p(1 << 24)
+    ws = C.c_void_p(1 << 21)
+
+    def call(n=10, tmpl=True, **over):
+        p = _tree(**over)
+        need = max(256, L.eagle_build_tree_workspace_size(C.byref(_tree()), 2))
+        return L.eagle_build_tree_template(C.byref(p), 2, x, 1, 32000, n, x if tmpl else None, x, x, x, x, x, x, x,
+                                           ws, need, None)
+
+    assert call(n=0) == E.EAGLE_ERR_INVALID
+    assert call(n=61) == E.EAGLE_ERR_INVALID          # above m_max 60
+    assert call(tmpl=False) == E.EAGLE_ERR_INVALID
+    assert call(children=17) == E.EAGLE_ERR_UNSUPPORTED
+    assert call(r_max=0) == E.EAGLE_ERR_INVALID
+    assert L.eagle_build_tree_template(C.byref(_tree()), 0, x, 1, 32000, 10, x, x, x, x, x, x, x, x, ws, 1 << 20,
+                                       None) == E.EAGLE_OK
+
+
 def test_accept_and_mask_reject_bad_params():
     L = E.lib()
     p = C.c_void_p(1 << 24)
