@@ -47,7 +47,7 @@ def lib():
         L.orc_weight.restype = f64
         L.orc_weight.argtypes = [f32, f32, f32]
         L.orc_row_stats.argtypes = [vp, i32, i64, i32, i32, i32, f32, vp, vp, vp, vp]
-        L.orc_build_tree.argtypes = [vp, i32, vp, i32, i64, i32, vp, i32, vp, vp, vp, vp, vp, vp,
+        L.orc_build_tree.argtypes = [vp, i32, vp, i32, i64, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                      i32, vp, vp, vp, vp, vp, vp, vp]
         L.orc_build_tree_template.argtypes = [i32, i32, vp, vp, i32, i32, vp, i32, i64, i32, i32] + [vp] * 6
         L.orc_tree_mask.argtypes = [i32, i32, vp, vp, vp, vp, vp]
@@ -55,9 +55,10 @@ def lib():
         L.orc_tree_attn_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
         L.orc_kv_commit.argtypes = [vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.orc_pdraft_prepare.argtypes = [i32] * 7 + [vp] * 16
+        L.orc_accept_rrs.argtypes = [f32, i32, i32, i32, i32, vp, vp, i32, i32] + [vp] * 8
         L.orc_accept.argtypes = [i32, f32, i32, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp]
         for f in ("orc_row_stats", "orc_build_tree", "orc_tree_mask", "orc_tree_attn",
-                  "orc_tree_attn_rows", "orc_build_tree_template", "orc_kv_commit", "orc_pdraft_prepare", "orc_accept", "orc_num_threads"):
+                  "orc_tree_attn_rows", "orc_build_tree_template", "orc_kv_commit", "orc_pdraft_prepare", "orc_accept_rrs", "orc_accept", "orc_num_threads"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -119,10 +120,11 @@ class _TreeParams(C.Structure):
 
 
 def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_max=None,
-               debug=False, policy=0):
+               debug=False, policy=0, child_words=None):
     """draft_logits [B][R_max][V] -> dict of tree arrays (output order), plus candidates if debug.
     policy: 0 EAGLE-2, 1 no rerank, 2 confidence ranking, 3 confidence ranking without rerank
-    (see oracle.c)."""
+    (see oracle.c).  child_words [B][R_max][children] uint32: children drawn from
+    the draft rows (the tree is then every candidate, in creation order)."""
     a, dt = _logits(draft_logits)
     B, R, V = a.shape
     if m_max is None:
@@ -138,8 +140,11 @@ def build_tree(draft_logits, depth, topk, children, m, chain_k=0, kinds=None, m_
         dbg = {k: np.zeros((B, nmax), np.int32) for k in ("token", "parent", "depth", "row", "rank")}
         dbg["V"] = np.zeros((B, nmax), np.float64)
         dbg["n"] = np.zeros(B, np.int32)
+    cw = None if child_words is None else np.ascontiguousarray(child_words).view(np.uint32)
+    if cw is not None and cw.shape != (B, R, children):
+        raise ValueError("child_words must be [B][R_max][children]")
     code = lib().orc_build_tree(
-        C.byref(p), B, _p(a), dt, V, R, _p(kinds), m_max,
+        C.byref(p), B, _p(a), dt, V, R, _p(kinds), m_max, _p(cw),
         _p(out["tokens"]), _p(out["parent"]), _p(out["depth"]), _p(out["score"]), _p(out["src_row"]),
         _p(out["num_nodes"]), nmax, _p(dbg.get("n")), _p(dbg.get("token")), _p(dbg.get("parent")),
         _p(dbg.get("depth")), _p(dbg.get("V")), _p(dbg.get("row")), _p(dbg.get("rank")))
@@ -323,6 +328,27 @@ def pdraft_prepare(tokens, num_nodes, accepted, accept_len, bonus, prefix_len, t
            "pdraft_prepare")
     out["flags"] = (int(flags[0]), int(flags[1]))
     return out
+
+
+def accept_rrs(target_logits, draft_logits, tokens, parent, src_row, num_nodes, max_accept, rand_words, T=1.0):
+    """Recursive rejection sampling over drawn children (see oracle.c):
+    target_logits [B][m_max+1][V], draft_logits [B][R_max][V] (same dtype),
+    tree arrays [B][m_max], rand_words [B][m_max+1] uint32.
+    -> (accepted [B][max_accept], accept_len [B], bonus [B])."""
+    t, dt = _logits(target_logits)
+    d, dd = _logits(draft_logits)
+    if dd != dt:
+        raise TypeError("target and draft logits must share a dtype")
+    B, M1, V = t.shape
+    arrs = [np.ascontiguousarray(x, dtype=np.int32) for x in (tokens, parent, src_row, num_nodes)]
+    rw = np.ascontiguousarray(rand_words).view(np.uint32)
+    acc = np.zeros((B, max_accept), np.int32)
+    alen = np.zeros(B, np.int32)
+    bon = np.zeros(B, np.int32)
+    _check(lib().orc_accept_rrs(T, B, M1 - 1, max_accept, V, _p(t), _p(d), d.shape[1], dt, _p(arrs[0]),
+                                _p(arrs[1]), _p(arrs[2]), _p(arrs[3]), _p(rw), _p(acc), _p(alen), _p(bon)),
+           "accept_rrs")
+    return acc, alen, bon
 
 
 def accept(mode, target_logits, tokens, parent, num_nodes, max_accept, rand_words=None, T=1.0):

@@ -47,6 +47,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+typedef unsigned __int128 u128;
+
 #define ORC_OK 0
 #define ORC_ERR_ARG (-1)
 #define ORC_ERR_DATA (-2)     /* non-finite row statistics */
@@ -175,6 +177,45 @@ static int row_stats_one(const void *row, int dtype, int V, int C, float T,
     return ORC_OK;
 }
 
+/*
+ * C tokens drawn without replacement from the row's softmax at temperature 1
+ * (the draft's own distribution), in draw order, by exact inverse-CDF draws
+ * on the integer weights: with R the weight left, draw t takes word r_t and
+ * s = floor(r_t * R / 2^32), and returns the smallest token not yet drawn
+ * whose inclusive cumulative weight (over tokens not yet drawn, in id order)
+ * exceeds s; if no weight is left it returns the smallest token not yet drawn.
+ */
+static int row_draws_one(const void *row, int dtype, int V, int C, const uint32_t *words,
+                         float *M_out, double *W_out, int *ids, double *ws)
+{
+    float M = -INFINITY;
+    for (int v = 0; v < V; ++v) M = fmaxf(M, elem_f32(row, dtype, v));
+    double W = 0.0;
+    for (int v = 0; v < V; ++v) W += weight_l(elem_f32(row, dtype, v), M, 1.0f);
+    *M_out = M;
+    *W_out = W;
+    if (!isfinite(M) || !isfinite(W)) return ORC_ERR_DATA;
+    uint64_t R = (uint64_t)W;
+    for (int t = 0; t < C; ++t) {
+        const uint64_t target = (uint64_t)(((u128)words[t] * R) >> 32);
+        uint64_t cum = 0;
+        int x = -1, first_free = -1;
+        for (int v = 0; v < V && x < 0; ++v) {
+            int drawn = 0;
+            for (int q = 0; q < t; ++q) drawn |= ids[q] == v;
+            if (drawn) continue;
+            if (first_free < 0) first_free = v;
+            cum += (uint64_t)weight_l(elem_f32(row, dtype, v), M, 1.0f);
+            if (cum > target) x = v;
+        }
+        if (x < 0) x = first_free;
+        ids[t] = x;
+        ws[t] = x < 0 ? 0.0 : weight_l(elem_f32(row, dtype, x), M, 1.0f);
+        R -= (uint64_t)ws[t];
+    }
+    return ORC_OK;
+}
+
 /* rows x V block with the given row stride (elements). C <= 64. */
 int orc_row_stats(const void *logits, int dtype, int64_t row_stride, int rows, int V, int C,
                   float T, float *M, double *W, int *top_id, double *top_w)
@@ -244,7 +285,7 @@ typedef struct {
  * cand_rank (-1 if not selected), and *n_cand.
  */
 static int build_one(const orc_tree_params *p, int kind, const void *rows, int dtype,
-                     int64_t row_stride, int m_max,
+                     int64_t row_stride, int m_max, const uint32_t *child_words,
                      int *tokens, int *parent, int *depth, double *score, int *src_row, int *num_nodes,
                      int *n_cand, int *cand_token, int *cand_parent, int *cand_depth, double *cand_V,
                      int *cand_row, int *cand_rank)
@@ -295,8 +336,11 @@ static int build_one(const orc_tree_params *p, int kind, const void *rows, int d
     int err = ORC_OK;
 
     for (int r = 0; r < R && err == ORC_OK; ++r)
-        err = row_stats_one((const char *)rows + (size_t)r * row_stride * esz, dtype, V, C, 1.0f,
-                            &Mr[r], &Wr[r], &tid[(size_t)r * C], &tw[(size_t)r * C]);
+        err = child_words
+                  ? row_draws_one((const char *)rows + (size_t)r * row_stride * esz, dtype, V, C,
+                                  child_words + (size_t)r * C, &Mr[r], &Wr[r], &tid[(size_t)r * C], &tw[(size_t)r * C])
+                  : row_stats_one((const char *)rows + (size_t)r * row_stride * esz, dtype, V, C, 1.0f,
+                                  &Mr[r], &Wr[r], &tid[(size_t)r * C], &tw[(size_t)r * C]);
     if (err != ORC_OK) goto done;
 
     /* depth 1: the children of the root's row 0 */
@@ -337,7 +381,12 @@ static int build_one(const orc_tree_params *p, int kind, const void *rows, int d
     /* selection, in output order (idx[0..m)) */
     int m = p->m;
     for (int i = 0; i < N; ++i) rank_of[i] = -1;
-    if (rerank && !conf_key) {
+    if (child_words) {
+        /* sampled children: the tree is every candidate, in creation order */
+        if (N > m_max) { err = ORC_ERR_ARG; goto done; }
+        for (int i = 0; i < N; ++i) idx[i] = i;
+        m = N;
+    } else if (rerank && !conf_key) {
         /* rerank: top-m of every generated candidate */
         if (N < m) { err = ORC_ERR_ARG; goto done; }
         for (int i = 0; i < N; ++i) idx[i] = i;
@@ -405,8 +454,11 @@ done:
     return err;
 }
 
+/* child_words [batch][r_max][children] (may be NULL): children drawn from the
+   draft rows instead of taken as their top tokens; the tree is then every
+   candidate, in creation order (dynamic trees only) */
 int orc_build_tree(const orc_tree_params *p, int batch, const void *draft_logits, int dtype,
-                   int64_t row_stride, int r_max, const int *kind, int m_max,
+                   int64_t row_stride, int r_max, const int *kind, int m_max, const uint32_t *child_words,
                    int *tokens, int *parent, int *depth, double *score, int *src_row, int *num_nodes,
                    int n_max_dbg, int *n_cand, int *cand_token, int *cand_parent, int *cand_depth,
                    double *cand_V, int *cand_row, int *cand_rank)
@@ -425,6 +477,7 @@ int orc_build_tree(const orc_tree_params *p, int batch, const void *draft_logits
         } else {
             const char *rows = (const char *)draft_logits + (size_t)b * r_max * row_stride * esz;
             e = build_one(p, kd, rows, dtype, row_stride, m_max,
+                          child_words && kd == 0 ? child_words + (size_t)b * r_max * p->children : NULL,
                           tokens + (size_t)b * m_max, parent + (size_t)b * m_max,
                           depth + (size_t)b * m_max, score + (size_t)b * m_max,
                           src_row + (size_t)b * m_max, num_nodes + b,
@@ -805,8 +858,6 @@ int orc_pdraft_prepare(int batch, int m_max, int max_accept, int K, int H, int m
 /* acceptance                                                           */
 /* ------------------------------------------------------------------ */
 
-typedef unsigned __int128 u128;
-
 /* argmax by (value desc, id asc); -1 if the row holds a NaN */
 static int argmax_row(const void *row, int dtype, int V)
 {
@@ -902,6 +953,129 @@ int orc_accept(int mode, float T, int batch, int m_max, int max_accept, int V,
         }
         accept_len[b] = len;
         bonus[b] = bon;
+        if (e != ORC_OK) {
+#pragma omp critical
+            err = e;
+        }
+    }
+    return err;
+}
+
+/* bit length of x (0 for 0) */
+static int bitlen128(u128 x)
+{
+    int n = 0;
+    while (x) { ++n; x >>= 1; }
+    return n;
+}
+
+/*
+ * Recursive rejection sampling over drawn children (EAGLE-1 explainer,
+ * "Verification": tokens accepted by the ratio of the target and draft
+ * distributions, the rest discarded after a rejection and a token
+ * resampled, leaving the target distribution unchanged).  The children of a
+ * node are draws without replacement from its draft row's softmax q (the
+ * sampled build); at node u with target weights P (row u + 1 at temperature
+ * T) and draft weights Q (u's draft row, temperature 1), the children x in
+ * draw order are tested:
+ *   accept iff floor(r_x * Q(x) * SP / 2^32) < P(x) * SQ  (u < p(x) / q(x));
+ *   otherwise P <- max(0, P * SQ - Q * SP) >> s, with s the shift that keeps
+ *   the sum below 2^52 (the residual max(0, p - q), renormalised), and
+ *   Q(x) <- 0 (q renormalised without x).  A child with Q(x) = 0 is rejected
+ *   and changes nothing; a residual that sums to 0 leaves P unchanged.
+ * With no child accepted the bonus is the inverse-CDF draw from P with
+ * r = rand_words[b][m_max].  src_row [B][m_max] gives each node's draft row
+ * (the root's is row 0); draft_logits [B][r_max][V].
+ */
+int orc_accept_rrs(float T, int batch, int m_max, int max_accept, int V, const void *target_logits,
+                   const void *draft_logits, int r_max, int dtype, const int *tokens, const int *parent,
+                   const int *src_row, const int *num_nodes, const uint32_t *rand_words, int *accepted,
+                   int *accept_len, int *bonus)
+{
+    if (batch < 0 || m_max <= 0 || m_max > 64 || max_accept <= 0 || V <= 0 || V > (1 << 17) || !(T > 0.0f))
+        return ORC_ERR_ARG;
+    const size_t esz = dtype == 0 ? 4 : 2;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        uint64_t *P = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)V);
+        uint64_t *Q = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)V);
+        uint64_t *Pn = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)V);
+        const int *tk = tokens + (size_t)b * m_max, *pa = parent + (size_t)b * m_max;
+        const int *sr = src_row + (size_t)b * m_max;
+        const uint32_t *rw = rand_words + (size_t)b * (m_max + 1);
+        const int n = num_nodes[b];
+        int *acc = accepted + (size_t)b * max_accept;
+        for (int j = 0; j < max_accept; ++j) acc[j] = -1;
+        int len = 0, cur = -1, bon = -1, e = ORC_OK;
+        while (1) {
+            /* target weights of the current node */
+            const char *trow = (const char *)target_logits + ((size_t)b * (m_max + 1) + (size_t)(cur + 1)) * V * esz;
+            float M = -INFINITY;
+            for (int v = 0; v < V; ++v) M = fmaxf(M, elem_f32(trow, dtype, v));
+            uint64_t SP = 0;
+            for (int v = 0; v < V; ++v) {
+                P[v] = (uint64_t)weight_l(elem_f32(trow, dtype, v), M, T);
+                SP += P[v];
+            }
+            if (!isfinite(M) || SP == 0) { e = ORC_ERR_DATA; break; }
+            int next = -1, has_children = 0;
+            for (int x = 0; x < n; ++x) has_children |= pa[x] == cur;
+            if (has_children) {
+                const int dr = cur < 0 ? 0 : sr[cur];
+                if (dr < 0 || dr >= r_max) { e = ORC_ERR_ARG; break; }
+                const char *drow = (const char *)draft_logits + ((size_t)b * r_max + (size_t)dr) * V * esz;
+                float Md = -INFINITY;
+                for (int v = 0; v < V; ++v) Md = fmaxf(Md, elem_f32(drow, dtype, v));
+                uint64_t SQ = 0;
+                for (int v = 0; v < V; ++v) {
+                    Q[v] = (uint64_t)weight_l(elem_f32(drow, dtype, v), Md, 1.0f);
+                    SQ += Q[v];
+                }
+                for (int x = 0; x < n && next < 0; ++x) {
+                    if (pa[x] != cur) continue;
+                    const int t = tk[x];
+                    const uint64_t q = Q[t], pt = P[t];
+                    if (q == 0) continue;
+                    if ((((u128)rw[x] * q * SP) >> 32) < (u128)pt * SQ) {
+                        next = x;
+                        break;
+                    }
+                    /* residual max(0, p - q) over the common denominator SP * SQ, shifted so
+                       that its sum stays below 2^52 */
+                    const int bl = bitlen128((u128)SP * SQ), sh = bl > 52 ? bl - 52 : 0;
+                    uint64_t SPn = 0;
+                    for (int v = 0; v < V; ++v) {
+                        const u128 a = (u128)P[v] * SQ, c = (u128)Q[v] * SP;
+                        Pn[v] = a > c ? (uint64_t)((a - c) >> sh) : 0;
+                        SPn += Pn[v];
+                    }
+                    if (SPn > 0) {
+                        for (int v = 0; v < V; ++v) P[v] = Pn[v];
+                        SP = SPn;
+                    }
+                    Q[t] = 0;
+                    SQ -= q;
+                }
+            }
+            if (next < 0) {
+                const uint64_t target = (uint64_t)(((u128)rw[m_max] * SP) >> 32);
+                uint64_t cum = 0;
+                for (int v = 0; v < V; ++v) {
+                    cum += P[v];
+                    if (cum > target) { bon = v; break; }
+                }
+                break;
+            }
+            if (len >= max_accept) { e = ORC_ERR_PATH; break; }
+            acc[len++] = next;
+            cur = next;
+        }
+        accept_len[b] = len;
+        bonus[b] = bon;
+        free(P);
+        free(Q);
+        free(Pn);
         if (e != ORC_OK) {
 #pragma omp critical
             err = e;
