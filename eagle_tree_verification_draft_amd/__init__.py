@@ -33,12 +33,12 @@ DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 
 EXPORTS = (
     "eagle_workspace_init", "eagle_read_errors",
     "eagle_build_tree_workspace_size", "eagle_build_tree",
-    "eagle_build_tree_mask", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
+    "eagle_build_tree_mask", "eagle_build_tree_sampled", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
     "eagle_tree_mask",
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
     "eagle_kv_commit",
     "eagle_accept_workspace_size", "eagle_accept",
-    "eagle_pdraft_prepare",
+    "eagle_pdraft_prepare", "eagle_accept_rrs_workspace_size", "eagle_accept_rrs",
     "eagle_status_string", "eagle_last_error",
 )
 
@@ -90,6 +90,7 @@ def lib() -> C.CDLL:
                                        vp, sz, vp]
         L.eagle_build_tree_mask.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, sz, vp]
+        L.eagle_build_tree_sampled.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64] + [vp] * 8 + [sz, vp]
         L.eagle_build_tree_template.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, i32] + [vp] * 9 + [sz, vp]
         L.eagle_tree_expand.argtypes = [C.POINTER(TreeParams), i32, i32, vp, C.c_int, i64, vp, vp, vp, vp, sz, vp]
         L.eagle_tree_finish.argtypes = [C.POINTER(TreeParams), i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -103,14 +104,18 @@ def lib() -> C.CDLL:
         L.eagle_accept_workspace_size.restype = sz
         L.eagle_accept.argtypes = [C.POINTER(AcceptParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]
+        L.eagle_accept_rrs_workspace_size.argtypes = [C.POINTER(AcceptParams), i32]
+        L.eagle_accept_rrs_workspace_size.restype = sz
+        L.eagle_accept_rrs.argtypes = [C.POINTER(AcceptParams), i32, vp, vp, C.c_int, i64, i64, i32] + [vp] * 9 + [sz, vp]
         L.eagle_pdraft_prepare.argtypes = [C.POINTER(PdraftParams), i32] + [vp] * 16 + [sz, vp]
         L.eagle_status_string.argtypes = [C.c_int]
         L.eagle_status_string.restype = C.c_char_p
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
         for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_build_tree_mask",
-                  "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish", "eagle_tree_mask",
-                  "eagle_tree_attn", "eagle_kv_commit", "eagle_accept", "eagle_pdraft_prepare"):
+                  "eagle_build_tree_sampled", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
+                  "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit", "eagle_accept", "eagle_accept_rrs",
+                  "eagle_pdraft_prepare"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -197,6 +202,17 @@ def build_tree_mask(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind:
            "eagle_build_tree_mask")
 
 
+def build_tree_sampled(p: TreeParams, batch: int, draft_logits: torch.Tensor, child_words, tokens, parent, depth,
+                       score, src_row, num_nodes, workspace: torch.Tensor, stream=None):
+    """Children drawn from the draft rows; child_words [batch][r_max][children] (int32 bit patterns)."""
+    rows, stride = _rows(draft_logits)
+    _check(lib().eagle_build_tree_sampled(C.byref(p), batch, rows, dtype_code(draft_logits.dtype), stride,
+                                          _ptr(child_words), _ptr(tokens), _ptr(parent), _ptr(depth), _ptr(score),
+                                          _ptr(src_row), _ptr(num_nodes), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_build_tree_sampled")
+
+
 def build_tree_template(p: TreeParams, batch: int, draft_logits: torch.Tensor, tmpl_parent, tmpl_child, tokens,
                         parent, depth, score, src_row, num_nodes, workspace: torch.Tensor, stream=None):
     """EAGLE-1 static tree from a template (device int32 arrays)."""
@@ -271,6 +287,23 @@ def accept(a: AcceptParams, batch: int, target_logits: torch.Tensor, tokens, par
                               _ptr(rand_words), _ptr(accepted), _ptr(accept_len), _ptr(bonus_token),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_accept")
+
+
+def accept_rrs_workspace_size(a: AcceptParams, batch: int) -> int:
+    return lib().eagle_accept_rrs_workspace_size(C.byref(a), batch)
+
+
+def accept_rrs(a: AcceptParams, batch: int, target_logits: torch.Tensor, draft_logits: torch.Tensor, tokens, parent,
+               src_row, num_nodes, rand_words, accepted, accept_len, bonus_token, workspace: torch.Tensor, stream=None):
+    trows, tstride = _rows(target_logits)
+    drows, dstride = _rows(draft_logits)
+    if draft_logits.dtype != target_logits.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    _check(lib().eagle_accept_rrs(C.byref(a), batch, trows, drows, dtype_code(target_logits.dtype), tstride, dstride,
+                                  draft_logits.shape[-2], _ptr(tokens), _ptr(parent), _ptr(src_row), _ptr(num_nodes),
+                                  _ptr(rand_words), _ptr(accepted), _ptr(accept_len), _ptr(bonus_token),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_accept_rrs")
 
 
 def pdraft_prepare(p: PdraftParams, batch: int, tokens, num_nodes, accepted, accept_len, bonus_token, prefix_len,

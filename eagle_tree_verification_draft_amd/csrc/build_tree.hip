@@ -291,6 +291,162 @@ __global__ __launch_bounds__(1024) void k_row_stats_stream(RowStatsArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Children drawn from the draft (sampled build), one workgroup per draft row:
+// M and the exact weight sum W as above, then `children` draws without
+// replacement by the inverse CDF of the integer weights.  With R the weight
+// left and word r, the target is s = floor(r R / 2^32) and the drawn token is
+// the first, in id order, of the tokens not yet drawn whose inclusive
+// cumulative weight exceeds s (the first token not yet drawn when no weight
+// is left).  Each thread owns a contiguous chunk of the row and keeps its
+// chunk's undrawn weight, so a draw is one block scan of those sums plus one
+// thread's walk through its chunk.  The drawn ids, in draw order, and their
+// logits take the place of the top-C lists.
+// ---------------------------------------------------------------------------
+struct DrawSmem {
+    unsigned long long part[16];
+    float fmax[16];
+    int drawn[kMaxChildren];
+    float drawn_w[kMaxChildren];
+    float drawn_l[kMaxChildren];
+    int first_free[16];
+};
+
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, DrawSmem &sm)
+{
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sm.part[w] = v;
+    __syncthreads();
+    unsigned long long r = 0;
+    for (int j = 0; j < nw; ++j) r += sm.part[j];
+    return r;
+}
+
+// exclusive prefix sum over the block's threads
+__device__ __forceinline__ unsigned long long block_exclusive_u64(unsigned long long v, DrawSmem &sm)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    unsigned long long incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    __syncthreads();
+    if (lane == 63) sm.part[w] = incl;
+    __syncthreads();
+    unsigned long long base = 0;
+    for (int j = 0; j < w; ++j) base += sm.part[j];
+    return base + incl - v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void k_row_draws(RowStatsArgs a, const uint32_t *words)
+{
+    __shared__ DrawSmem sm;
+    const int g = blockIdx.x;
+    const int b = g / a.rows_in, r = a.row_base + g % a.rows_in;
+    const size_t r_all = (size_t)b * a.r_max + r;
+    if (r >= a.rows_dyn) return;
+    const int C = a.children, V = a.vocab, NT = blockDim.x, tid = threadIdx.x;
+    const T *row = static_cast<const T *>(a.logits) + (size_t)g * (size_t)a.row_stride;
+    // this thread's chunk [lo, hi), a multiple of 8 elements long
+    const int per = ((V + NT - 1) / NT + 7) / 8 * 8;
+    const int lo = min(V, tid * per), hi = min(V, lo + per);
+    float lmax = -__builtin_inff();
+    for (int v = lo; v < hi; ++v) lmax = fmaxf(lmax, load_scalar<T>(row + v));
+    lmax = wave_max(lmax);
+    if ((tid & 63) == 0) sm.fmax[tid >> 6] = lmax;
+    __syncthreads();
+    float M = sm.fmax[0];
+    for (int j = 1; j < (NT >> 6); ++j) M = fmaxf(M, sm.fmax[j]);
+    unsigned long long own = 0;
+    for (int v = lo; v < hi; ++v) own += (unsigned long long)weight_of(load_scalar<T>(row + v), M);
+    int32_t *out_id = a.top_id + r_all * a.children;
+    float *out_v = a.top_v + r_all * a.children;
+    if (!__builtin_isfinite(M)) {
+        // a NaN or infinite logit: reported, no draws (every thread leaves here)
+        if (tid == 0) {
+            raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
+            a.W[r_all] = 0.0;
+            a.M[r_all] = M;
+        }
+        for (int t = tid; t < C; t += NT) { out_id[t] = -1; out_v[t] = -__builtin_inff(); }
+        return;
+    }
+    const unsigned long long W = block_sum_u64(own, sm);
+    unsigned long long R = W;
+    for (int t = 0; t < C; ++t) {
+        if (tid == 0) {
+            sm.drawn[t] = -1;
+            sm.drawn_w[t] = 0.0f;
+            sm.drawn_l[t] = -__builtin_inff();
+        }
+        const uint32_t word = words[r_all * C + t];
+        // s = floor(word * R / 2^32), R < 2^53
+        const unsigned long long s = (unsigned long long)word * (R >> 32) +
+                                     (((unsigned long long)word * (R & 0xffffffffull)) >> 32);
+        const unsigned long long excl = block_exclusive_u64(own, sm);
+        int first = 0x7fffffff;
+        if (R > 0 && excl <= s && s < excl + own) {
+            // the target falls in this chunk: walk it
+            unsigned long long cum = excl;
+            for (int v = lo; v < hi; ++v) {
+                bool taken = false;
+                for (int q = 0; q < t; ++q) taken |= sm.drawn[q] == v;
+                if (taken) continue;
+                const float l = load_scalar<T>(row + v);
+                const float w = weight_of(l, M);
+                cum += (unsigned long long)w;
+                if (cum > s) {
+                    sm.drawn[t] = v;
+                    sm.drawn_w[t] = w;
+                    sm.drawn_l[t] = l;
+                    break;
+                }
+            }
+        } else if (R == 0) {
+            // no weight left: the first token not yet drawn
+            for (int v = lo; v < hi && first == 0x7fffffff; ++v) {
+                bool taken = false;
+                for (int q = 0; q < t; ++q) taken |= sm.drawn[q] == v;
+                if (!taken) first = v;
+            }
+        }
+        if (R == 0) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+            if ((tid & 63) == 0) sm.first_free[tid >> 6] = first;
+        }
+        __syncthreads();
+        if (R == 0 && tid == 0) {
+            int f = sm.first_free[0];
+            for (int j = 1; j < (NT >> 6); ++j) f = min(f, sm.first_free[j]);
+            if (f < V) {   // (C <= V: a token is always left)
+                sm.drawn[t] = f;
+                sm.drawn_l[t] = load_scalar<T>(row + f);
+                sm.drawn_w[t] = weight_of(sm.drawn_l[t], M);
+            }
+        }
+        __syncthreads();
+        const int x = sm.drawn[t];
+        const unsigned long long wx = (unsigned long long)sm.drawn_w[t];
+        if (x >= lo && x < hi) own -= wx;
+        R -= wx;
+        if (tid == 0) {
+            out_id[t] = x;
+            out_v[t] = sm.drawn_l[t];
+        }
+    }
+    if (tid == 0) {
+        a.W[r_all] = (double)W;
+        a.M[r_all] = M;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2: one workgroup per sequence, everything in LDS.  Candidates are
 // numbered in creation order; the candidates of one depth form lists of C
 // (the children of one expanded node, or of the root), and every entry of a
@@ -476,7 +632,15 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
 
     if (tid == 0) sm.lvl_off[D] = N;
     __syncthreads();
-    if (a.policy == EAGLE_POLICY_EAGLE2) {
+    if (a.policy == kPolicyAllCandidates) {
+        // sampled children: the tree is every candidate, in creation order
+        for (int g = tid; g < N; g += NT) {
+            sm.sel[g] = g;
+            sm.rank_of[g] = g;
+        }
+        if (tid == 0) sm.m_out = N;
+        __syncthreads();
+    } else if (a.policy == EAGLE_POLICY_EAGLE2) {
         // ---- rerank: merge the depths' rank-ordered lists (first m of each) ----
         // item = (entry i < m of depth lv, other depth od); the depth sizes follow
         // from (C, k) alone, so items are located without reading LDS
@@ -873,8 +1037,24 @@ static RowStatsArgs row_stats_args(const eagle_tree_params *p, int32_t batch, co
 static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const RowStatsArgs &ra,
                                 const int32_t *kind, const int32_t *levels, int32_t *tokens, int32_t *parent,
                                 int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                                hipStream_t st, const int32_t *prefix_len, uint64_t *anc, int32_t *pos,
+                                int policy);
+
+static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const RowStatsArgs &ra,
+                                const int32_t *kind, const int32_t *levels, int32_t *tokens, int32_t *parent,
+                                int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
                                 hipStream_t st, const int32_t *prefix_len = nullptr, uint64_t *anc = nullptr,
                                 int32_t *pos = nullptr)
+{
+    return launch_select(p, batch, ra, kind, levels, tokens, parent, depth, score, src_row, num_nodes, st, prefix_len,
+                         anc, pos, p->policy);
+}
+
+static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const RowStatsArgs &ra,
+                                const int32_t *kind, const int32_t *levels, int32_t *tokens, int32_t *parent,
+                                int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                                hipStream_t st, const int32_t *prefix_len, uint64_t *anc, int32_t *pos,
+                                int policy)
 {
     TreeSelectArgs ta;
     ta.kind = kind;
@@ -885,7 +1065,7 @@ static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const
     ta.chain_k = p->chain_k;
     ta.m_max = p->m_max;
     ta.r_max = p->r_max;
-    ta.policy = p->policy;
+    ta.policy = policy;
     ta.top_id = ra.top_id;
     ta.top_v = ra.top_v;
     ta.M = ra.M;
@@ -930,6 +1110,27 @@ hipError_t launch_build_tree_mask(const eagle_tree_params *p, int32_t batch, con
     if (e != hipSuccess) return e;
     return launch_select(p, batch, ra, kind, nullptr, tokens, parent, depth, score, src_row, num_nodes, st,
                          prefix_len, anc, pos);
+}
+
+hipError_t launch_build_tree_sampled(const eagle_tree_params *p, int32_t batch, const void *logits,
+                                    eagle_dtype dt, int64_t row_stride, const uint32_t *child_words,
+                                    int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                                    int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st)
+{
+    const BuildLayout L = build_layout(p, batch);
+    const RowStatsArgs ra = row_stats_args(p, batch, L, ws, logits, dt, row_stride, nullptr, p->r_max, 0);
+    if (ra.rows > 0) {
+        int nt = ((p->vocab + 7) / 8 + 63) / 64 * 64;
+        nt = nt < 64 ? 64 : (nt > 1024 ? 1024 : nt);
+        if (dt == EAGLE_F32)
+            hipLaunchKernelGGL(k_row_draws<float>, dim3((unsigned)ra.rows), dim3(nt), 0, st, ra, child_words);
+        else
+            hipLaunchKernelGGL(k_row_draws<uint16_t>, dim3((unsigned)ra.rows), dim3(nt), 0, st, ra, child_words);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_select(p, batch, ra, nullptr, nullptr, tokens, parent, depth, score, src_row, num_nodes, st,
+                         nullptr, nullptr, nullptr, kPolicyAllCandidates);
 }
 
 hipError_t launch_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *logits,

@@ -165,6 +165,34 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                       "build_tree_mask launch");
 }
 
+eagle_status eagle_build_tree_sampled(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                      eagle_dtype dtype, int64_t row_stride, const uint32_t *child_words,
+                                      int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                                      int32_t *src_row, int32_t *num_nodes, void *workspace, size_t workspace_bytes,
+                                      void *stream)
+{
+    eagle_status s = check_tree_params(p, batch);
+    if (s != EAGLE_OK) return s;
+    if (p->policy != EAGLE_POLICY_EAGLE2) return fail(EAGLE_ERR_INVALID, "sampled children take the EAGLE-2 policy");
+    long long tot = 0, nn = p->children;
+    for (int d = 0; d < p->depth; ++d) {
+        tot += nn;
+        nn = (nn < p->topk ? nn : p->topk) * (long long)p->children;
+    }
+    if (tot > p->m_max)
+        return fail(EAGLE_ERR_INVALID, "a sampled tree keeps all %lld candidates > m_max %d", tot, p->m_max);
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!draft_logits || !child_words || !tokens || !parent || !depth || !score || !src_row || !num_nodes)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
+    s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_build_tree_sampled(p, batch, draft_logits, dtype, row_stride, child_words, tokens, parent,
+                                                depth, score, src_row, num_nodes, workspace, (hipStream_t)stream),
+                      "build_tree_sampled launch");
+}
+
 eagle_status eagle_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
                                        eagle_dtype dtype, int64_t row_stride, int32_t n_tmpl,
                                        const int32_t *tmpl_parent, const int32_t *tmpl_child, int32_t *tokens,
@@ -374,6 +402,45 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
                                     accepted, accept_len, bonus_token, static_cast<uint32_t *>(workspace),
                                     (hipStream_t)stream),
                       "accept launch");
+}
+
+size_t eagle_accept_rrs_workspace_size(const eagle_accept_params *a, int32_t batch)
+{
+    if (!a || batch < 0 || a->vocab < 1) return kWsHeader;
+    return accept_rrs_layout_bytes(a, batch);
+}
+
+eagle_status eagle_accept_rrs(const eagle_accept_params *a, int32_t batch, const void *target_logits,
+                              const void *draft_logits, eagle_dtype dtype, int64_t target_row_stride,
+                              int64_t draft_row_stride, int32_t r_max, const int32_t *tokens, const int32_t *parent,
+                              const int32_t *src_row, const int32_t *num_nodes, const uint32_t *rand_words,
+                              int32_t *accepted, int32_t *accept_len, int32_t *bonus_token, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    if (!a) return fail(EAGLE_ERR_INVALID, "accept params are NULL");
+    if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!(a->temperature > 0.0f && std::isfinite(a->temperature)))
+        return fail(EAGLE_ERR_INVALID, "recursive rejection sampling needs a finite temperature > 0");
+    if (a->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", a->vocab);
+    if (a->vocab > kMaxVocab) return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d > %d", a->vocab, kMaxVocab);
+    if (a->m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", a->m_max);
+    if (a->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", a->m_max, kMaxMMax);
+    if (a->max_accept < 1) return fail(EAGLE_ERR_INVALID, "max_accept %d < 1", a->max_accept);
+    if (r_max < 1) return fail(EAGLE_ERR_INVALID, "r_max %d < 1", r_max);
+    if (target_row_stride < a->vocab || draft_row_stride < a->vocab)
+        return fail(EAGLE_ERR_INVALID, "row strides %lld, %lld below vocab %d", (long long)target_row_stride,
+                    (long long)draft_row_stride, a->vocab);
+    if (!target_logits || !draft_logits || !tokens || !parent || !src_row || !num_nodes || !rand_words || !accepted ||
+        !accept_len || !bonus_token)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    eagle_status s = check_workspace(workspace, workspace_bytes, accept_rrs_layout_bytes(a, batch));
+    if (s != EAGLE_OK) return s;
+    if (batch == 0) return ok();
+    return hip_status(launch_accept_rrs(a, batch, target_logits, draft_logits, dtype, target_row_stride,
+                                        draft_row_stride, r_max, tokens, parent, src_row, num_nodes, rand_words,
+                                        accepted, accept_len, bonus_token, workspace, (hipStream_t)stream),
+                      "accept_rrs launch");
 }
 
 eagle_status eagle_pdraft_prepare(const eagle_pdraft_params *p, int32_t batch, const int32_t *tokens,

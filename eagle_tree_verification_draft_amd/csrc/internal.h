@@ -30,6 +30,9 @@ struct RowStatsArgs {
     bool vec_ok;
 };
 
+// tree-kernel selection for sampled children: every candidate, in creation order
+constexpr int kPolicyAllCandidates = 16;
+
 struct TreeSelectArgs {
     const int32_t *kind;
     int depth_max, topk, children, m, chain_k, m_max, r_max, policy;
@@ -95,6 +98,10 @@ hipError_t launch_build_tree_mask(const eagle_tree_params *p, int32_t batch, con
                                   const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
                                   double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc,
                                   int32_t *pos, void *ws, hipStream_t st);
+hipError_t launch_build_tree_sampled(const eagle_tree_params *p, int32_t batch, const void *logits,
+                                    eagle_dtype dt, int64_t row_stride, const uint32_t *child_words,
+                                    int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                                    int32_t *src_row, int32_t *num_nodes, void *ws, hipStream_t st);
 hipError_t launch_build_tree_template(const eagle_tree_params *p, int32_t batch, const void *logits,
                                      eagle_dtype dt, int64_t row_stride, int32_t n_tmpl, const int32_t *tparent,
                                      const int32_t *tchild, int32_t *tokens, int32_t *parent, int32_t *depth,
@@ -156,6 +163,14 @@ hipError_t launch_accept(const eagle_accept_params *a, int32_t batch, const void
                          hipStream_t st);
 
 size_t accept_layout_bytes(const eagle_accept_params *p, int32_t batch);
+
+// recursive rejection sampling over drawn children
+size_t accept_rrs_layout_bytes(const eagle_accept_params *p, int32_t batch);
+hipError_t launch_accept_rrs(const eagle_accept_params *p, int32_t batch, const void *target, const void *draft,
+                             eagle_dtype dt, int64_t t_stride, int64_t d_stride, int32_t r_max,
+                             const int32_t *tokens, const int32_t *parent, const int32_t *src_row,
+                             const int32_t *num_nodes, const uint32_t *words, int32_t *accepted,
+                             int32_t *accept_len, int32_t *bonus, void *ws, hipStream_t st);
 
 // ---- misc ----------------------------------------------------------------
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);

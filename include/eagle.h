@@ -168,6 +168,30 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                                    int32_t *pos, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * A dynamic tree whose children are drawn from the draft instead of taken
+ * as its top tokens, for lossless acceptance by eagle_accept_rrs (EAGLE-1
+ * explainer, "Draft generation flow": tokens are sampled from the draft's
+ * next-token distribution; "Verification": the ratio test).  Each used row's
+ * `children` tokens are drawn without replacement from its softmax at
+ * temperature 1, in draw order, by the inverse CDF of the integer weights:
+ * with R the weight left and r = child_words[b][row][t], the target is
+ * s = floor(r * R / 2^32) and the draw is the first token not yet drawn, in
+ * id order, whose inclusive cumulative weight exceeds s (the first token not
+ * yet drawn when no weight is left).  c and V as in eagle_build_tree; the
+ * expansion takes each depth's top k by V; the tree is every candidate, in
+ * creation order (rows [batch][r_max][row_stride], dynamic trees only).
+ * child_words [batch][r_max][children] uint32 (device).
+ * Errors: those of eagle_build_tree; EAGLE_ERR_INVALID for a policy other
+ * than EAGLE2 or when all candidates (children + (depth-1) topk children
+ * when children >= topk) exceed m_max.
+ */
+eagle_status eagle_build_tree_sampled(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                      eagle_dtype dtype, int64_t row_stride, const uint32_t *child_words,
+                                      int32_t *tokens, int32_t *parent, int32_t *depth, double *score,
+                                      int32_t *src_row, int32_t *num_nodes, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/*
  * EAGLE-1's static tree (EAGLE-2 explainer, "Differences from EAGLE-1": a
  * fixed tree template, optimised offline, where EAGLE-2 builds the tree from
  * the draft's confidences).  tmpl_parent / tmpl_child [n_tmpl] (device
@@ -396,6 +420,44 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
                           const uint32_t *rand_words, int32_t *accepted, int32_t *accept_len,
                           int32_t *bonus_token, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Recursive rejection sampling over children drawn from the draft
+ * (eagle_build_tree_sampled trees; EAGLE-1 explainer, "Verification": draft
+ * tokens accepted by the ratio of the target and draft distributions, the
+ * rest discarded after a rejection and a token resampled, leaving the target
+ * distribution unchanged).  From the root, at node u with target weights P
+ * (Spec S integers of row u + 1 at temperature T, sum SP) and draft weights Q
+ * (u's own draft row, src_row[u], the root's being row 0, temperature 1, sum
+ * SQ), u's children x are tested in index (draw) order:
+ *   accept iff floor(r_x * Q(x) * SP / 2^32) < P(x) * SQ, r_x = rand_words[b][x];
+ *   otherwise P <- max(0, P * SQ - Q * SP) >> s, s = max(0, bitlen(SP * SQ)
+ *   - 52) (the residual max(0, p - q), summing below 2^52), unless it sums to
+ *   0, and Q(x) <- 0 (q without x); a child with Q(x) = 0 is skipped.
+ * No child accepted: the bonus is the smallest v whose inclusive cumulative
+ * P exceeds floor(r * SP / 2^32), r = rand_words[b][m_max].  The emitted
+ * tokens follow the target distribution up to the residuals' rounding
+ * (relative 2^-52 per element and step).
+ * Inputs: target_logits [batch][m_max+1][target_row_stride]; draft_logits
+ *   [batch][r_max][draft_row_stride] (the rows the tree was drawn from);
+ *   tokens, parent, src_row [batch][m_max] and num_nodes [batch]
+ *   (eagle_build_tree_sampled); rand_words [batch][m_max+1].  Uses m_max,
+ *   vocab, max_accept and temperature of the params (mode is ignored).
+ * Outputs as eagle_accept.  Device errors: NONFINITE_ROW for a row with a
+ *   NaN or infinite maximum or no weight; TREE for a num_nodes outside
+ *   [0, m_max], a token outside [0, vocab) or a draft row outside [0, r_max);
+ *   PATH as eagle_accept.
+ * Workspace: eagle_accept_rrs_workspace_size (two residual buffers of vocab
+ *   64-bit integers per sequence).
+ */
+size_t eagle_accept_rrs_workspace_size(const eagle_accept_params *a, int32_t batch);
+
+eagle_status eagle_accept_rrs(const eagle_accept_params *a, int32_t batch, const void *target_logits,
+                              const void *draft_logits, eagle_dtype dtype, int64_t target_row_stride,
+                              int64_t draft_row_stride, int32_t r_max, const int32_t *tokens, const int32_t *parent,
+                              const int32_t *src_row, const int32_t *num_nodes, const uint32_t *rand_words,
+                              int32_t *accepted, int32_t *accept_len, int32_t *bonus_token, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Parallel-draft inputs (P-EAGLE)                                     */

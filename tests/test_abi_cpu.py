@@ -212,6 +212,37 @@ def test_build_tree_template_rejects_bad_params():
                                        None) == E.EAGLE_OK
 
 
+def test_sampled_build_and_rrs_reject_bad_params():
+    L = E.lib()
+    x = C.c_void_p(1 << 24)
+    ws = C.c_void_p(1 << 21)
+
+    # (every call below is rejected before a launch, or has batch 0)
+    def build(batch=2, **over):
+        d = dict(depth=3, topk=2, children=3, m=3, m_max=15, r_max=5)
+        d.update(over)
+        p = _tree(**d)
+        need = max(256, L.eagle_build_tree_workspace_size(C.byref(_tree(**d)), 2))
+        return L.eagle_build_tree_sampled(C.byref(p), batch, x, 1, 32000, x, x, x, x, x, x, x, ws, need, None)
+
+    assert build(batch=0) == E.EAGLE_OK                   # 3 + 6 + 6 = 15 candidates fit m_max 15
+    assert build(m_max=14) == E.EAGLE_ERR_INVALID
+    assert build(policy=E.EAGLE_POLICY_CONF) == E.EAGLE_ERR_INVALID
+
+    def rrs(T=1.0, wsb=None, tgt=x, **over):
+        d = dict(mode=E.EAGLE_ACCEPT_SAMPLE, temperature=T, m_max=21, vocab=32000, max_accept=3)
+        d.update(over)
+        a = E.AcceptParams(**d)
+        need = L.eagle_accept_rrs_workspace_size(C.byref(a), 2) if wsb is None else wsb
+        return L.eagle_accept_rrs(C.byref(a), 2, tgt, x, 1, 32000, 32000, 5, x, x, x, x, x, x, x, x, ws, need, None)
+
+    assert rrs(T=0.0) == E.EAGLE_ERR_INVALID
+    assert rrs(tgt=None) == E.EAGLE_ERR_INVALID
+    assert rrs(wsb=256) == E.EAGLE_ERR_WORKSPACE
+    assert rrs(max_accept=0) == E.EAGLE_ERR_INVALID
+    assert L.eagle_accept_rrs_workspace_size(C.byref(E.AcceptParams(1, 1.0, 21, 32000, 3)), 2) >= 2 * 2 * 32000 * 8
+
+
 def test_accept_and_mask_reject_bad_params():
     L = E.lib()
     p = C.c_void_p(1 << 24)
