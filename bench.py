@@ -278,6 +278,8 @@ def main():
     expand = measure_expand(E, step, w, sets[0], kinds, K)
     pdraft = measure_pdraft(E, step, w, sets[0], kinds, K)
     policies = measure_policies(E, w, sets[0], kinds, K)
+    rrs = measure_rrs(E, w, K)
+    log(f"[bench] sampled build {rrs['build_us']:.1f} us, recursive rejection sampling {rrs['accept_us']:.1f} us")
     log(f"[bench] parallel-draft inputs {pdraft['avg_us']:.2f} us/call, {pdraft['hbm_gbs']:.0f} GB/s")
     if expand:
         log(f"[bench] incremental build {expand['total_us']:.1f} us for {expand['levels']} levels + finish")
@@ -342,6 +344,7 @@ def main():
         "tree_expand": expand,
         "pdraft_prepare": pdraft,
         "tree_policies": policies,
+        "sampled_rrs": rrs,
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
         "launch": "hipGraph replay per step" if graphs is not None else "eager",
         "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
@@ -396,6 +399,73 @@ def measure_commit(E, step, w, S, kinds, reps):
     assert torch.equal(plo, plen + step.accept_len), "kv commit did not write every accepted token"
     return {"call": "eagle_kv_commit (k_kv_commit)", "avg_us": round(us, 2), "timed_calls": n * per_graph,
             "tokens": tokens, "algorithmic_bytes": nbytes, "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def measure_rrs(E, w, reps):
+    """Children drawn from the draft (depth 4, top 3 expanded, 3 drawn children:
+    30 nodes, every one kept) and recursive rejection sampling over them, on
+    the workload's batch, vocabulary and dtype: synthetic draft rows N(0, 9),
+    target rows = the node's own draft row + N(0, 1).  Graph replays of 10
+    calls each, HIP events; mean accepted length."""
+    import numpy as np
+    import torch
+    D, k, C = 4, 3, 3
+    B, V = w.batch, w.vocab
+    R = 1 + (D - 1) * k
+    N = C + (D - 1) * k * C
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    draft = (torch.randn((B, R, V), generator=g, device="cuda") * 3.0).to(w.dtype)
+    words_c = torch.randint(-(1 << 31), 1 << 31, (B, R, C), generator=g, device="cuda", dtype=torch.int64).to(torch.int32)
+    words = torch.randint(-(1 << 31), 1 << 31, (B, N + 1), generator=g, device="cuda", dtype=torch.int64).to(torch.int32)
+    p = E.TreeParams(D, k, C, 1, 0, V, N, R, 0)
+    ws_t = torch.empty(max(256, E.build_tree_workspace_size(p, B)), dtype=torch.uint8, device="cuda")
+    E.workspace_init(ws_t)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    tok, par, dep, srow = (torch.empty((B, N), **i32) for _ in range(4))
+    score = torch.empty((B, N), dtype=torch.float64, device="cuda")
+    nn = torch.empty((B,), **i32)
+    E.build_tree_sampled(p, B, draft, words_c, tok, par, dep, score, srow, nn, ws_t)
+    torch.cuda.synchronize()
+    rows = torch.where(srow >= 0, srow, torch.zeros_like(srow)).long()
+    target = torch.empty((B, N + 1, V), dtype=w.dtype, device="cuda")
+    target[:, 0] = draft[:, 0]
+    target[:, 1:] = torch.gather(draft, 1, rows[:, :, None].expand(B, N, V))
+    target = (target.float() + torch.randn(target.shape, generator=g, device="cuda")).to(w.dtype)
+    a = E.AcceptParams(E.EAGLE_ACCEPT_SAMPLE, 1.0, N, V, D)
+    ws_a = torch.empty(E.accept_rrs_workspace_size(a, B), dtype=torch.uint8, device="cuda")
+    E.workspace_init(ws_a)
+    acc = torch.empty((B, D), **i32)
+    alen = torch.empty((B,), **i32)
+    bon = torch.empty((B,), **i32)
+
+    def timed(fn):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            fn()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(10):
+                fn()
+        gr.replay()
+        n = max(1, reps // 10)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record()
+        for _ in range(n):
+            gr.replay()
+        eb.record()
+        torch.cuda.synchronize()
+        return ea.elapsed_time(eb) * 1e3 / (n * 10)
+
+    build_us = timed(lambda: E.build_tree_sampled(p, B, draft, words_c, tok, par, dep, score, srow, nn, ws_t))
+    accept_us = timed(lambda: E.accept_rrs(a, B, target, draft, tok, par, srow, nn, words, acc, alen, bon, ws_a))
+    assert E.read_errors(ws_t) == 0 and E.read_errors(ws_a) == 0, "sampled build or RRS reported device errors"
+    return {"tree": f"depth {D}, top {k} expanded, {C} drawn children, {N} nodes", "build_us": round(build_us, 2),
+            "accept_us": round(accept_us, 2), "mean_accept_len": round(float(alen.float().mean().item()), 3)}
 
 
 def measure_policies(E, w, S, kinds, reps):

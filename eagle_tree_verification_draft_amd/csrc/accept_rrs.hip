@@ -14,9 +14,9 @@
 // sums to 0 leaves P as it was.  With no child accepted the bonus is the
 // inverse-CDF draw from P with the word r_{m_max}.
 //
-// One workgroup per sequence; each thread owns a contiguous chunk of the
-// vocabulary, so the sums, the residual passes and the bonus scan are chunk
-// loops plus block reductions.  P lives in the workspace (two buffers per
+// One workgroup per sequence.  The row passes (maxima, weights, residuals)
+// take coalesced 16-byte vectors, the bonus scan a contiguous chunk of the
+// vocabulary per thread, with block reductions.  P lives in the workspace (two buffers per
 // sequence: a residual is written beside the current P and taken only if it
 // is not all zero); Q is recomputed from the draft row where it is needed.
 #include "common.h"
@@ -93,7 +93,7 @@ struct RrsArgs {
     int64_t t_stride, d_stride;
     int m_max, vocab, max_accept, r_max;
     float temperature;
-    bool unit_t;
+    bool unit_t, t_vec_ok, d_vec_ok;
     const int32_t *tokens, *parent, *src_row, *num_nodes;
     const uint32_t *words;
     int32_t *accepted, *accept_len, *bonus;
@@ -105,8 +105,11 @@ template <typename T>
 __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
 {
     __shared__ RrsSmem sm;
+    constexpr int VEC = Vec<T>::n;
     const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x, V = a.vocab, m_max = a.m_max;
-    const int per = ((V + NT - 1) / NT + 7) / 8 * 8;
+    // row passes take 16-byte vectors j = tid + i NT (coalesced); the bonus
+    // scan takes a contiguous chunk [lo, hi) of the residual per thread
+    const int per = (V + NT - 1) / NT;
     const int lo = min(V, tid * per), hi = min(V, lo + per);
     int n = a.num_nodes[b];
     if (n < 0 || n > m_max) {
@@ -127,18 +130,28 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
         // ---- target weights of node `cur` ----
         const T *trow = static_cast<const T *>(a.target) + ((size_t)b * (m_max + 1) + (size_t)(cur + 1)) * a.t_stride;
         float lmax = -__builtin_inff();
-        for (int v = lo; v < hi; ++v) lmax = fmaxf(lmax, load_scalar<T>(trow + v));
+        for (int j = tid; j * VEC < V; j += NT) {
+            float f[VEC];
+            unpack<T>(load_vec<T>(trow, j * VEC, V, a.t_vec_ok), f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
+        }
         const float M = rrs_max(lmax, sm);
         if (!__builtin_isfinite(M)) {
             if (tid == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
             break;
         }
         unsigned long long own = 0;
-        for (int v = lo; v < hi; ++v) {
-            const unsigned long long w =
-                (unsigned long long)weight_of_t(load_scalar<T>(trow + v), M, a.temperature, a.unit_t);
-            P[v] = w;
-            own += w;
+        for (int j = tid; j * VEC < V; j += NT) {
+            float f[VEC];
+            unpack<T>(load_vec<T>(trow, j * VEC, V, a.t_vec_ok), f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if (j * VEC + e >= V) break;
+                const unsigned long long w = (unsigned long long)weight_of_t(f[e], M, a.temperature, a.unit_t);
+                P[j * VEC + e] = w;
+                own += w;
+            }
         }
         unsigned long long SP = rrs_sum(own, sm);
         if (SP == 0) {
@@ -156,14 +169,24 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
             }
             const T *drow = static_cast<const T *>(a.draft) + ((size_t)b * a.r_max + dr) * a.d_stride;
             float dmax = -__builtin_inff();
-            for (int v = lo; v < hi; ++v) dmax = fmaxf(dmax, load_scalar<T>(drow + v));
+            for (int j = tid; j * VEC < V; j += NT) {
+                float f[VEC];
+                unpack<T>(load_vec<T>(drow, j * VEC, V, a.d_vec_ok), f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) dmax = fmaxf(dmax, f[e]);
+            }
             const float Md = rrs_max(dmax, sm);
             if (!__builtin_isfinite(Md)) {
                 if (tid == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
                 break;
             }
             unsigned long long qown = 0;
-            for (int v = lo; v < hi; ++v) qown += (unsigned long long)weight_of(load_scalar<T>(drow + v), Md);
+            for (int j = tid; j * VEC < V; j += NT) {
+                float f[VEC];
+                unpack<T>(load_vec<T>(drow, j * VEC, V, a.d_vec_ok), f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) qown += (unsigned long long)weight_of(f[e], Md);   // -inf past V: 0
+            }
             unsigned long long SQ = rrs_sum(qown, sm);
             int nrem = 0;
             for (int x = 0; x < n && next < 0; ++x) {
@@ -185,14 +208,20 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
                 // residual max(0, p - q) over SP * SQ, shifted below 2^52 in sum
                 const int bl = bitlen_u128((unsigned __int128)SP * SQ), sh = bl > 52 ? bl - 52 : 0;
                 unsigned long long rown = 0;
-                for (int v = lo; v < hi; ++v) {
-                    bool rem = false;
-                    for (int j = 0; j < nrem; ++j) rem |= sm.removed[j] == v;
-                    const unsigned long long qv = rem ? 0ull : (unsigned long long)weight_of(load_scalar<T>(drow + v), Md);
-                    const unsigned __int128 pa = (unsigned __int128)P[v] * SQ, qa = (unsigned __int128)qv * SP;
-                    const unsigned long long d = pa > qa ? (unsigned long long)((pa - qa) >> sh) : 0ull;
-                    Pn[v] = d;
-                    rown += d;
+                for (int j = tid; j * VEC < V; j += NT) {
+                    float f[VEC];
+                    unpack<T>(load_vec<T>(drow, j * VEC, V, a.d_vec_ok), f);
+                    for (int e = 0; e < VEC; ++e) {
+                        const int v = j * VEC + e;
+                        if (v >= V) break;
+                        bool rem = false;
+                        for (int q = 0; q < nrem; ++q) rem |= sm.removed[q] == v;
+                        const unsigned long long qv = rem ? 0ull : (unsigned long long)weight_of(f[e], Md);
+                        const unsigned __int128 pa = (unsigned __int128)P[v] * SQ, qa = (unsigned __int128)qv * SP;
+                        const unsigned long long d = pa > qa ? (unsigned long long)((pa - qa) >> sh) : 0ull;
+                        Pn[v] = d;
+                        rown += d;
+                    }
                 }
                 const unsigned long long SPn = rrs_sum(rown, sm);
                 if (SPn > 0) {
@@ -266,6 +295,9 @@ hipError_t launch_accept_rrs(const eagle_accept_params *p, int32_t batch, const 
     a.r_max = r_max;
     a.temperature = p->temperature;
     a.unit_t = p->temperature == 1.0f;
+    const size_t esz = dt == EAGLE_F32 ? 4 : 2;
+    a.t_vec_ok = ((uintptr_t)target % 16 == 0) && ((size_t)t_stride * esz % 16 == 0);
+    a.d_vec_ok = ((uintptr_t)draft % 16 == 0) && ((size_t)d_stride * esz % 16 == 0);
     a.tokens = tokens;
     a.parent = parent;
     a.src_row = src_row;

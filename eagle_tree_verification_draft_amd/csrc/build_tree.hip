@@ -351,19 +351,30 @@ __global__ __launch_bounds__(1024) void k_row_draws(RowStatsArgs a, const uint32
     const size_t r_all = (size_t)b * a.r_max + r;
     if (r >= a.rows_dyn) return;
     const int C = a.children, V = a.vocab, NT = blockDim.x, tid = threadIdx.x;
+    constexpr int VEC = Vec<T>::n;
     const T *row = static_cast<const T *>(a.logits) + (size_t)g * (size_t)a.row_stride;
-    // this thread's chunk [lo, hi), a multiple of 8 elements long
-    const int per = ((V + NT - 1) / NT + 7) / 8 * 8;
+    // this thread's chunk [lo, hi): whole 16-byte vectors
+    const int per = ((V + NT - 1) / NT + VEC - 1) / VEC * VEC;
     const int lo = min(V, tid * per), hi = min(V, lo + per);
     float lmax = -__builtin_inff();
-    for (int v = lo; v < hi; ++v) lmax = fmaxf(lmax, load_scalar<T>(row + v));
+    for (int j = tid; j * VEC < V; j += NT) {   // coalesced
+        float f[VEC];
+        unpack<T>(load_vec<T>(row, j * VEC, V, a.vec_ok), f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lmax = fmaxf(lmax, f[e]);
+    }
     lmax = wave_max(lmax);
     if ((tid & 63) == 0) sm.fmax[tid >> 6] = lmax;
     __syncthreads();
     float M = sm.fmax[0];
     for (int j = 1; j < (NT >> 6); ++j) M = fmaxf(M, sm.fmax[j]);
     unsigned long long own = 0;
-    for (int v = lo; v < hi; ++v) own += (unsigned long long)weight_of(load_scalar<T>(row + v), M);
+    for (int v0 = lo; v0 < hi; v0 += VEC) {
+        float f[VEC];
+        unpack<T>(load_vec<T>(row, v0, V, a.vec_ok), f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) own += (unsigned long long)weight_of(f[e], M);   // -inf past V: 0
+    }
     int32_t *out_id = a.top_id + r_all * a.children;
     float *out_v = a.top_v + r_all * a.children;
     if (!__builtin_isfinite(M)) {
@@ -393,18 +404,24 @@ __global__ __launch_bounds__(1024) void k_row_draws(RowStatsArgs a, const uint32
         if (R > 0 && excl <= s && s < excl + own) {
             // the target falls in this chunk: walk it
             unsigned long long cum = excl;
-            for (int v = lo; v < hi; ++v) {
-                bool taken = false;
-                for (int q = 0; q < t; ++q) taken |= sm.drawn[q] == v;
-                if (taken) continue;
-                const float l = load_scalar<T>(row + v);
-                const float w = weight_of(l, M);
-                cum += (unsigned long long)w;
-                if (cum > s) {
-                    sm.drawn[t] = v;
-                    sm.drawn_w[t] = w;
-                    sm.drawn_l[t] = l;
-                    break;
+            bool found = false;
+            for (int v0 = lo; v0 < hi && !found; v0 += VEC) {
+                float f[VEC];
+                unpack<T>(load_vec<T>(row, v0, V, a.vec_ok), f);
+                for (int e = 0; e < VEC && !found; ++e) {
+                    const int v = v0 + e;
+                    if (v >= hi) break;
+                    bool taken = false;
+                    for (int q = 0; q < t; ++q) taken |= sm.drawn[q] == v;
+                    if (taken) continue;
+                    const float w = weight_of(f[e], M);
+                    cum += (unsigned long long)w;
+                    if (cum > s) {
+                        sm.drawn[t] = v;
+                        sm.drawn_w[t] = w;
+                        sm.drawn_l[t] = f[e];
+                        found = true;
+                    }
                 }
             }
         } else if (R == 0) {
