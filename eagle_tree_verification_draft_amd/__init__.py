@@ -6,8 +6,8 @@ The functions here carry the names of the C entry points declared in
 pointers, the current torch stream becomes the HIP stream, and a non-OK
 status becomes an ``EagleError``.  Every step of the computation runs in the
 HIP kernels of libeagle.so; there is no fallback.  ``VerifyStep`` allocates
-the outputs and workspaces of one step for fixed shapes and runs the four
-calls in order on one stream.
+the outputs and workspaces of one step for fixed shapes and runs its calls
+in order on one stream.
 """
 from __future__ import annotations
 
@@ -352,7 +352,8 @@ class StepShape:
 
 
 class VerifyStep:
-    """Outputs and workspaces of one step; run() enqueues the four calls."""
+    """Outputs and workspaces of one step; run() enqueues the fused build and
+    mask, the attention and the acceptance; commit() the KV commit."""
 
     def __init__(self, s: StepShape, device="cuda"):
         self.s = s
