@@ -732,56 +732,143 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: one wave per output row (sequence, node, q head), exact fp32
-// arithmetic on the vector ALUs, 64 keys per step with an online softmax.
+// fp32 path: exact fp32 arithmetic on the vector ALUs.  A workgroup serves
+// four rows (node, q head) of one (sequence, kv head) with KG key groups of
+// four waves.  The keys go by in chunks of 64 (the prefix, then the draft
+// nodes); group g takes chunks g, g + KG, ..., stages each chunk's K and V^T
+// once in its own LDS buffer with coalesced loads (the next chunk's loads are
+// issued before the current chunk's products), and keeps an online softmax
+// per row.  The groups' partial (max, sum, output) are merged in LDS at the
+// end.  QK: lane = key; PV: lane = dimension (two at D = 128).  Padded LDS
+// rows (D + 4, 68 floats) keep the 16-byte reads of both products free of
+// bank conflicts.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_tree_attn_f32(AttnArgs a)
+constexpr int kF32Rows = 4;
+
+template <int D, int KG>
+struct F32Smem {
+    float k[KG][64][D + 4];      // K chunk, key-major
+    float v[KG][D][68];          // V^T chunk, dimension-major
+    float q[kF32Rows][D];
+    float p[KG * kF32Rows][64];
+    float mo[KG][kF32Rows][D];   // partial outputs
+    float2 ml[KG][kF32Rows];     // partial (max, sum)
+};
+
+template <int D, int KG, bool kPaged>
+__global__ __launch_bounds__(64 * kF32Rows * KG) void k_tree_attn_f32(AttnArgs a)
 {
-    __shared__ float s_q[kHD];
-    __shared__ float s_p[64];
-    const int lane = threadIdx.x;
-    const int h = blockIdx.x % a.Hq;
-    const int i = (blockIdx.x / a.Hq) % a.m_max;
-    const int b = blockIdx.x / (a.Hq * a.m_max);
-    const int kvh = h / a.G, d = a.d, m_max = a.m_max;
-    float *out = static_cast<float *>(a.out) + (((size_t)b * m_max + i) * a.Hq + h) * d;
+    constexpr int kT = 64 * kF32Rows;           // threads of one key group
+    constexpr int kPer = 64 * D / kT;           // K (and V) elements per thread per chunk
+    __shared__ F32Smem<D, KG> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int w = wv % kF32Rows, g = wv / kF32Rows, gt = tid % kT;
+    const int m_max = a.m_max, G = a.G;
+    const int nrb = (m_max * G + kF32Rows - 1) / kF32Rows;
+    const int rb = blockIdx.x % nrb;
+    const int kvh = (blockIdx.x / nrb) % a.Hkv;
+    const int b = blockIdx.x / (nrb * a.Hkv);
+    const int r = rb * kF32Rows + w;           // row = node * G + q head within the kv head
+    const int i = r / G, h = kvh * G + r % G;
     int n = a.num_nodes[b];
     n = n < 0 ? 0 : (n > m_max ? m_max : n);
-    if (i >= n) {
-        for (int e = lane; e < d; e += 64) out[e] = 0.0f;
-        return;
-    }
     int L = a.prefix_len[b];
     if (L < 0 || L > a.cap) {
-        if (lane == 0 && i == 0 && h == 0) raise_error(a.err, EAGLE_DEVERR_PREFIX);
+        if (tid == 0 && rb == 0 && kvh == 0) raise_error(a.err, EAGLE_DEVERR_PREFIX);
         L = L < 0 ? 0 : a.cap;
     }
-    const float *q = static_cast<const float *>(a.q) + (((size_t)b * m_max + i) * a.Hq + h) * d;
-    for (int e = lane; e < d; e += 64) s_q[e] = q[e];
-    const uint64_t bits = a.anc[(size_t)b * m_max + i];
-    __syncthreads();
+    const bool live = i < m_max && i < n;      // wave-uniform
+    if (live && g == 0) {
+        const float *q = static_cast<const float *>(a.q) + (((size_t)b * m_max + i) * a.Hq + h) * D;
+        for (int e = lane; e < D; e += 64) sm.q[w][e] = q[e];
+    }
+    const uint64_t bits = live ? a.anc[(size_t)b * m_max + i] : 0;
+    const int npc = (L + 63) / 64, nchunks = npc + 1;
+    float kr[kPer], vr[kPer];
+    const float *kd0 = static_cast<const float *>(a.kd) + ((size_t)b * m_max * a.Hkv + kvh) * D;
+    const float *vd0 = static_cast<const float *>(a.vd) + ((size_t)b * m_max * a.Hkv + kvh) * D;
+    // contiguous cache slice of (b, kvh); unused by the paged kernel
+    const float *kc0 = static_cast<const float *>(a.kc) + (kPaged ? 0 : ((size_t)b * a.Hkv + kvh) * (size_t)a.cap * D);
+    const float *vc0 = static_cast<const float *>(a.vc) + (kPaged ? 0 : ((size_t)b * a.Hkv + kvh) * (size_t)D * a.cap);
     float m_run = -__builtin_inff(), l_run = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
-    const int nchunks = (L + 63) / 64 + 1;
-    for (int c = 0; c < nchunks; ++c) {
-        const bool draft = c == nchunks - 1;
-        const int key = draft ? lane : c * 64 + lane;
-        bool ok;
-        const float *kp;
-        if (draft) {
-            ok = key < n && ((bits >> key) & 1ull);
-            kp = static_cast<const float *>(a.kd) + (((size_t)b * m_max + (ok ? key : 0)) * a.Hkv + kvh) * d;
-        } else {
-            ok = key < L;
-            kp = k_row<float>(a, b, kvh, ok ? key : 0);
+    const int rounds = (nchunks + KG - 1) / KG;
+    // Round j stages chunk (j - 1) * KG + g (held in registers) in LDS, issues
+    // the loads of chunk j * KG + g, then computes the staged chunk.
+    for (int j = 0; j <= rounds; ++j) {
+        const int c = (j - 1) * KG + g;
+        if (j > 0) {
+            __syncthreads();             // the previous chunk's LDS reads are done
+            if (c < nchunks) {
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int idx = u * kT + gt;
+                    if constexpr (kPaged) sm.k[g][gt % 64][gt / 64 + u * (kT / 64)] = kr[u];
+                    else sm.k[g][idx / D][idx % D] = kr[u];
+                    sm.v[g][idx / 64][idx % 64] = vr[u];
+                }
+            }
+            __syncthreads();
         }
-        float sc = -__builtin_inff();
-        if (ok) {
-            float dot = 0.0f;
-            for (int e = 0; e < d; ++e) dot = __builtin_fmaf(s_q[e], kp[e], dot);
-            sc = dot * a.scale_log2;
+        const int cn = j * KG + g;
+        if (cn < nchunks) {
+            // K element (key, e) with e fastest, V^T element (e, key) with key
+            // fastest; keys past the chunk's end read as zero
+            const bool draft = cn == npc;
+            const int kmax = draft ? n : min(64, L - cn * 64);
+            // Per-thread element pointers advanced by a fixed stride per step
+            // u.  Contiguous kernel: K element (key, e) = idx / D, idx % D.
+            // Paged kernel: K element (gt % 64, gt / 64 + u * kT / 64), so
+            // that each thread looks up one page per chunk.  V^T element
+            // (e, key) = idx / 64, idx % 64 in both.
+            const float *kp, *vp;
+            size_t ks, vs;
+            if (draft) {
+                if constexpr (kPaged) {
+                    kp = kd0 + (size_t)(gt % 64) * a.Hkv * D + gt / 64;
+                    ks = kT / 64;
+                } else {
+                    kp = kd0 + (size_t)(gt / D) * a.Hkv * D + gt % D;
+                    ks = (size_t)(kT / D) * a.Hkv * D;
+                }
+                vp = vd0 + (size_t)(gt % 64) * a.Hkv * D + gt / 64;
+                vs = kT / 64;
+            } else if constexpr (kPaged) {
+                const int key = cn * 64 + (gt % 64 < kmax ? gt % 64 : 0);
+                kp = k_row<float>(a, b, kvh, key) + gt / 64;
+                ks = kT / 64;
+                vp = v_elem<float>(a, b, kvh, gt / 64, key);
+                vs = (size_t)(kT / 64) * a.block_size;
+            } else {
+                kp = kc0 + (size_t)cn * 64 * D + gt;
+                ks = kT;
+                vp = vc0 + (size_t)(gt / 64) * a.cap + cn * 64 + gt % 64;
+                vs = (size_t)(kT / 64) * a.cap;
+            }
+            const bool vok = gt % 64 < kmax;
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const bool kok = kPaged ? vok : (u * kT + gt) / D < kmax;
+                kr[u] = kok ? *kp : 0.0f;
+                vr[u] = vok ? *vp : 0.0f;
+                kp += ks;
+                vp += vs;
+            }
         }
-        const float cm = wave_max(sc);
-        const float m_new = fmaxf(m_run, cm);
+        if (j == 0 || !live || c >= nchunks) continue;
+        const bool draft = c == npc;
+        const bool ok = draft ? (lane < n && ((bits >> lane) & 1ull)) : (c * 64 + lane < L);
+        float dot = 0.0f;
+#pragma unroll 4
+        for (int e = 0; e < D; e += 4) {
+            const float4 kq = *reinterpret_cast<const float4 *>(&sm.k[g][lane][e]);
+            const float4 qq = *reinterpret_cast<const float4 *>(&sm.q[w][e]);
+            dot = __builtin_fmaf(qq.x, kq.x, dot);
+            dot = __builtin_fmaf(qq.y, kq.y, dot);
+            dot = __builtin_fmaf(qq.z, kq.z, dot);
+            dot = __builtin_fmaf(qq.w, kq.w, dot);
+        }
+        const float sc = ok ? dot * a.scale_log2 : -__builtin_inff();
+        const float m_new = fmaxf(m_run, wave_max(sc));
         const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
         const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
         const float p = __builtin_amdgcn_exp2f(sc - m_use);
@@ -790,28 +877,51 @@ __global__ __launch_bounds__(64) void k_tree_attn_f32(AttnArgs a)
         for (int o = 32; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
         l_run = l_run * corr + ps;
         m_run = m_new;
-        __syncthreads();
-        s_p[lane] = p;
-        __syncthreads();
+        sm.p[wv][lane] = p;              // read back by this wave only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         acc0 *= corr;
         acc1 *= corr;
-        const int kmax = draft ? n : min(64, L - c * 64);
-        for (int t = 0; t < kmax; ++t) {
-            const float pt = s_p[t];
-            if (pt == 0.0f) continue;
-            if (draft) {
-                const float *vp = static_cast<const float *>(a.vd) + (((size_t)b * m_max + t) * a.Hkv + kvh) * d;
-                acc0 = __builtin_fmaf(pt, vp[lane], acc0);
-                if (d > 64) acc1 = __builtin_fmaf(pt, vp[lane + 64], acc1);
-            } else {
-                acc0 = __builtin_fmaf(pt, *v_elem<float>(a, b, kvh, lane, c * 64 + t), acc0);
-                if (d > 64) acc1 = __builtin_fmaf(pt, *v_elem<float>(a, b, kvh, lane + 64, c * 64 + t), acc1);
+#pragma unroll 4
+        for (int t = 0; t < 64; t += 4) {
+            const float4 pp = *reinterpret_cast<const float4 *>(&sm.p[wv][t]);
+            const float4 v0 = *reinterpret_cast<const float4 *>(&sm.v[g][lane][t]);
+            acc0 = __builtin_fmaf(pp.x, v0.x, acc0);
+            acc0 = __builtin_fmaf(pp.y, v0.y, acc0);
+            acc0 = __builtin_fmaf(pp.z, v0.z, acc0);
+            acc0 = __builtin_fmaf(pp.w, v0.w, acc0);
+            if constexpr (D > 64) {
+                const float4 v1 = *reinterpret_cast<const float4 *>(&sm.v[g][lane + 64][t]);
+                acc1 = __builtin_fmaf(pp.x, v1.x, acc1);
+                acc1 = __builtin_fmaf(pp.y, v1.y, acc1);
+                acc1 = __builtin_fmaf(pp.z, v1.z, acc1);
+                acc1 = __builtin_fmaf(pp.w, v1.w, acc1);
             }
         }
     }
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    out[lane] = acc0 * inv;
-    if (d > 64) out[lane + 64] = acc1 * inv;
+    // merge the key groups: rescale each to the common maximum
+    if (lane == 0) sm.ml[g][w] = make_float2(m_run, l_run);
+    sm.mo[g][w][lane] = acc0;
+    if constexpr (D > 64) sm.mo[g][w][lane + 64] = acc1;
+    __syncthreads();
+    if (g != 0 || i >= m_max) return;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < KG; ++u) M = fmaxf(M, sm.ml[u][w].x);
+    float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+        const float2 ml = sm.ml[u][w];
+        const float s = ml.x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ml.x - M);
+        l = __builtin_fmaf(ml.y, s, l);
+        o0 = __builtin_fmaf(sm.mo[u][w][lane], s, o0);
+        if constexpr (D > 64) o1 = __builtin_fmaf(sm.mo[u][w][lane + 64], s, o1);
+    }
+    float *out = static_cast<float *>(a.out) + (((size_t)b * m_max + i) * a.Hq + h) * D;
+    const float inv = live && l > 0.0f ? 1.0f / l : 0.0f;
+    out[lane] = live ? o0 * inv : 0.0f;
+    if constexpr (D > 64) out[lane + 64] = live ? o1 * inv : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -894,8 +1004,17 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     const float scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     a.scale_log2 = scale * 1.4426950408889634f;
     if (p->dtype == EAGLE_F32) {
-        const dim3 g((unsigned)(batch * p->m_max * p->num_q_heads));
-        hipLaunchKernelGGL(k_tree_attn_f32, g, dim3(64), 0, st, a);
+        // key groups: four at D = 64, two at D = 128 (the LDS buffers of one workgroup)
+        const int nrb = (P.rows + kF32Rows - 1) / kF32Rows;
+        const dim3 g((unsigned)(batch * p->num_kv_heads * nrb));
+        const bool paged = p->block_size > 0;
+        if (p->head_dim == 64) {
+            if (paged) hipLaunchKernelGGL((k_tree_attn_f32<64, 4, true>), g, dim3(64 * kF32Rows * 4), 0, st, a);
+            else hipLaunchKernelGGL((k_tree_attn_f32<64, 4, false>), g, dim3(64 * kF32Rows * 4), 0, st, a);
+        } else {
+            if (paged) hipLaunchKernelGGL((k_tree_attn_f32<128, 2, true>), g, dim3(64 * kF32Rows * 2), 0, st, a);
+            else hipLaunchKernelGGL((k_tree_attn_f32<128, 2, false>), g, dim3(64 * kF32Rows * 2), 0, st, a);
+        }
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
         const bool contiguous = p->block_size == 0;
