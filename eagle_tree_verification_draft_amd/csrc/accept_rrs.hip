@@ -14,11 +14,14 @@
 // sums to 0 leaves P as it was.  With no child accepted the bonus is the
 // inverse-CDF draw from P with the word r_{m_max}.
 //
-// One workgroup per sequence.  The row passes (maxima, weights, residuals)
-// take coalesced 16-byte vectors, the bonus scan a contiguous chunk of the
-// vocabulary per thread, with block reductions.  P lives in the workspace (two buffers per
+// One workgroup per sequence.  The row maxima take coalesced 16-byte
+// vectors; the weight and residual passes one element per lane, so that the
+// 64-bit stores coalesce too; the bonus scan sums 64-token segments, scans
+// the segment sums, then one segment.  P lives in the workspace (two buffers per
 // sequence: a residual is written beside the current P and taken only if it
-// is not all zero); Q is recomputed from the draft row where it is needed.
+// is not all zero).  Q is written once per node to a third buffer, and a
+// rejected child's entry is set to 0 there, so the residual passes read Q
+// instead of recomputing the exact weights.
 #include "common.h"
 #include "internal.h"
 #include "rowvec.h"
@@ -34,7 +37,9 @@ struct RrsSmem {
     float fmax[16];
     int tok[kMaxMMax], par[kMaxMMax], srow[kMaxMMax];
     int removed[kMaxMMax];   // tokens taken out of q at the current node
-    int pick;
+    unsigned long long seg[kMaxVocab / 64];   // sums of 64-token segments of P
+    unsigned long long pick_base;
+    int pick, pick_seg;
 };
 
 __device__ __forceinline__ unsigned long long rrs_sum(unsigned long long v, RrsSmem &sm)
@@ -97,7 +102,7 @@ struct RrsArgs {
     const int32_t *tokens, *parent, *src_row, *num_nodes;
     const uint32_t *words;
     int32_t *accepted, *accept_len, *bonus;
-    unsigned long long *pbuf;   // [batch][2][vocab]
+    unsigned long long *pbuf;   // [batch][3][vocab]: P, the next P, Q
     uint32_t *err;
 };
 
@@ -107,10 +112,8 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
     __shared__ RrsSmem sm;
     constexpr int VEC = Vec<T>::n;
     const int b = blockIdx.x, tid = threadIdx.x, NT = blockDim.x, V = a.vocab, m_max = a.m_max;
-    // row passes take 16-byte vectors j = tid + i NT (coalesced); the bonus
-    // scan takes a contiguous chunk [lo, hi) of the residual per thread
-    const int per = (V + NT - 1) / NT;
-    const int lo = min(V, tid * per), hi = min(V, lo + per);
+    // the maxima take 16-byte vectors j = tid + i NT, the weights and
+    // residuals one element v = tid + i NT per lane (all coalesced)
     int n = a.num_nodes[b];
     if (n < 0 || n > m_max) {
         if (tid == 0) raise_error(a.err, EAGLE_DEVERR_TREE);
@@ -123,13 +126,14 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
     }
     __syncthreads();
     const uint32_t *rw = a.words + (size_t)b * (m_max + 1);
-    unsigned long long *P = a.pbuf + (size_t)b * 2 * V, *Pn = P + V;
+    unsigned long long *P = a.pbuf + (size_t)b * 3 * V, *Pn = P + V, *Qw = P + 2 * V;
     int32_t *acc = a.accepted + (size_t)b * a.max_accept;
     int cur = -1, len = 0, bonus = -1;
     while (true) {
         // ---- target weights of node `cur` ----
         const T *trow = static_cast<const T *>(a.target) + ((size_t)b * (m_max + 1) + (size_t)(cur + 1)) * a.t_stride;
         float lmax = -__builtin_inff();
+#pragma unroll 4
         for (int j = tid; j * VEC < V; j += NT) {
             float f[VEC];
             unpack<T>(load_vec<T>(trow, j * VEC, V, a.t_vec_ok), f);
@@ -141,15 +145,23 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
             if (tid == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
             break;
         }
+        // weights with one element per lane, so that the 64-bit stores coalesce
+        // (the temperature test is taken outside the loop: the division is
+        // computed only where it is used)
         unsigned long long own = 0;
-        for (int j = tid; j * VEC < V; j += NT) {
-            float f[VEC];
-            unpack<T>(load_vec<T>(trow, j * VEC, V, a.t_vec_ok), f);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                if (j * VEC + e >= V) break;
-                const unsigned long long w = (unsigned long long)weight_of_t(f[e], M, a.temperature, a.unit_t);
-                P[j * VEC + e] = w;
+        if (a.unit_t) {
+#pragma unroll 8
+            for (int v = tid; v < V; v += NT) {
+                const unsigned long long w = (unsigned long long)weight_of(load_scalar<T>(trow + v), M);
+                P[v] = w;
+                own += w;
+            }
+        } else {
+#pragma unroll 8
+            for (int v = tid; v < V; v += NT) {
+                const unsigned long long w =
+                    (unsigned long long)weight_of_t(load_scalar<T>(trow + v), M, a.temperature, false);
+                P[v] = w;
                 own += w;
             }
         }
@@ -169,6 +181,7 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
             }
             const T *drow = static_cast<const T *>(a.draft) + ((size_t)b * a.r_max + dr) * a.d_stride;
             float dmax = -__builtin_inff();
+#pragma unroll 4
             for (int j = tid; j * VEC < V; j += NT) {
                 float f[VEC];
                 unpack<T>(load_vec<T>(drow, j * VEC, V, a.d_vec_ok), f);
@@ -181,11 +194,11 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
                 break;
             }
             unsigned long long qown = 0;
-            for (int j = tid; j * VEC < V; j += NT) {
-                float f[VEC];
-                unpack<T>(load_vec<T>(drow, j * VEC, V, a.d_vec_ok), f);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) qown += (unsigned long long)weight_of(f[e], Md);   // -inf past V: 0
+#pragma unroll 8
+            for (int v = tid; v < V; v += NT) {
+                const unsigned long long w = (unsigned long long)weight_of(load_scalar<T>(drow + v), Md);
+                Qw[v] = w;
+                qown += w;
             }
             unsigned long long SQ = rrs_sum(qown, sm);
             int nrem = 0;
@@ -208,20 +221,15 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
                 // residual max(0, p - q) over SP * SQ, shifted below 2^52 in sum
                 const int bl = bitlen_u128((unsigned __int128)SP * SQ), sh = bl > 52 ? bl - 52 : 0;
                 unsigned long long rown = 0;
-                for (int j = tid; j * VEC < V; j += NT) {
-                    float f[VEC];
-                    unpack<T>(load_vec<T>(drow, j * VEC, V, a.d_vec_ok), f);
-                    for (int e = 0; e < VEC; ++e) {
-                        const int v = j * VEC + e;
-                        if (v >= V) break;
-                        bool rem = false;
-                        for (int q = 0; q < nrem; ++q) rem |= sm.removed[q] == v;
-                        const unsigned long long qv = rem ? 0ull : (unsigned long long)weight_of(f[e], Md);
-                        const unsigned __int128 pa = (unsigned __int128)P[v] * SQ, qa = (unsigned __int128)qv * SP;
-                        const unsigned long long d = pa > qa ? (unsigned long long)((pa - qa) >> sh) : 0ull;
-                        Pn[v] = d;
-                        rown += d;
-                    }
+#pragma unroll 8
+                for (int v = tid; v < V; v += NT) {
+                    // both products are below 2^105, so a negative difference
+                    // sets the top bit; sh < 64 and the shifted value fits in 64 bits
+                    const unsigned __int128 df = (unsigned __int128)P[v] * SQ - (unsigned __int128)Qw[v] * SP;
+                    const unsigned long long lo = (unsigned long long)df, hi = (unsigned long long)(df >> 64);
+                    const unsigned long long d = (long long)hi < 0 ? 0ull : (lo >> sh) | ((hi << 1) << (63 - sh));
+                    Pn[v] = d;
+                    rown += d;
                 }
                 const unsigned long long SPn = rrs_sum(rown, sm);
                 if (SPn > 0) {
@@ -230,29 +238,61 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
                     Pn = tmp;
                     SP = SPn;
                 }
-                if (tid == 0) sm.removed[nrem] = t;
+                if (tid == 0) {
+                    sm.removed[nrem] = t;
+                    Qw[t] = 0;
+                }
                 ++nrem;
                 SQ -= q;
-                __syncthreads();   // the removed list
+                __syncthreads();   // the removed list and Q(t) = 0
             }
         }
         if (next < 0) {
-            // bonus: inverse CDF of P
+            // bonus: inverse CDF of P.  Segments of 64 tokens are summed by
+            // waves (coalesced), a block scan over the segment sums finds the
+            // segment holding the draw, and one wave scans inside it.
             const unsigned long long s = (unsigned long long)(((unsigned __int128)rw[m_max] * SP) >> 32);
-            unsigned long long pown = 0;
-            for (int v = lo; v < hi; ++v) pown += P[v];
-            const unsigned long long excl = rrs_exclusive(pown, sm);
-            if (tid == 0) sm.pick = -1;
+            const int lane = tid & 63, wv = tid >> 6, nw = NT >> 6, nseg = (V + 63) / 64;
+            for (int g = wv; g < nseg; g += nw) {
+                const int v = g * 64 + lane;
+                unsigned long long x = v < V ? P[v] : 0ull;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+                if (lane == 0) sm.seg[g] = x;
+            }
+            if (tid == 0) {
+                sm.pick = -1;
+                sm.pick_seg = 0;
+                sm.pick_base = 0;
+            }
             __syncthreads();
-            if (excl <= s && s < excl + pown) {
+            const int sper = (nseg + NT - 1) / NT;
+            const int s_lo = min(nseg, tid * sper), s_hi = min(nseg, s_lo + sper);
+            unsigned long long sown = 0;
+            for (int g = s_lo; g < s_hi; ++g) sown += sm.seg[g];
+            const unsigned long long excl = rrs_exclusive(sown, sm);
+            if (excl <= s && s < excl + sown) {
                 unsigned long long cum = excl;
-                for (int v = lo; v < hi; ++v) {
-                    cum += P[v];
-                    if (cum > s) {
-                        sm.pick = v;
+                for (int g = s_lo; g < s_hi; ++g) {
+                    if (s < cum + sm.seg[g]) {
+                        sm.pick_seg = g;
+                        sm.pick_base = cum;
                         break;
                     }
+                    cum += sm.seg[g];
                 }
+            }
+            __syncthreads();
+            if (wv == 0) {
+                const int g = sm.pick_seg, v = g * 64 + lane;
+                unsigned long long incl = v < V ? P[v] : 0ull;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned long long t = __shfl_up(incl, o);
+                    if (lane >= o) incl += t;
+                }
+                const unsigned long long hit = __ballot(sm.pick_base + incl > s);
+                if (lane == 0 && hit) sm.pick = g * 64 + __ffsll((long long)hit) - 1;
             }
             __syncthreads();
             bonus = sm.pick;
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(kRrsThreads) void k_accept_rrs(RrsArgs a)
 
 size_t accept_rrs_layout_bytes(const eagle_accept_params *p, int32_t batch)
 {
-    return kWsHeader + align_up((size_t)batch * 2 * (size_t)p->vocab * sizeof(unsigned long long), 256);
+    return kWsHeader + align_up((size_t)batch * 3 * (size_t)p->vocab * sizeof(unsigned long long), 256);
 }
 
 hipError_t launch_accept_rrs(const eagle_accept_params *p, int32_t batch, const void *target, const void *draft,

@@ -447,8 +447,9 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
  *   NaN or infinite maximum or no weight; TREE for a num_nodes outside
  *   [0, m_max], a token outside [0, vocab) or a draft row outside [0, r_max);
  *   PATH as eagle_accept.
- * Workspace: eagle_accept_rrs_workspace_size (two residual buffers of vocab
- *   64-bit integers per sequence).
+ * Workspace: eagle_accept_rrs_workspace_size (three buffers of vocab 64-bit
+ *   integers per sequence: the target weights, their residual, the draft
+ *   weights).
  */
 size_t eagle_accept_rrs_workspace_size(const eagle_accept_params *a, int32_t batch);
 

@@ -240,7 +240,7 @@ def test_sampled_build_and_rrs_reject_bad_params():
     assert rrs(tgt=None) == E.EAGLE_ERR_INVALID
     assert rrs(wsb=256) == E.EAGLE_ERR_WORKSPACE
     assert rrs(max_accept=0) == E.EAGLE_ERR_INVALID
-    assert L.eagle_accept_rrs_workspace_size(C.byref(E.AcceptParams(1, 1.0, 21, 32000, 3)), 2) >= 2 * 2 * 32000 * 8
+    assert L.eagle_accept_rrs_workspace_size(C.byref(E.AcceptParams(1, 1.0, 21, 32000, 3)), 2) >= 2 * 3 * 32000 * 8
 
 
 def test_accept_and_mask_reject_bad_params():
