@@ -309,6 +309,8 @@ struct DrawSmem {
     float drawn_w[kMaxChildren];
     float drawn_l[kMaxChildren];
     int first_free[16];
+    int walk_lo, walk_hi;              // the chunk holding the draw
+    unsigned long long walk_excl;      // undrawn weight before it
 };
 
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, DrawSmem &sm)
@@ -402,28 +404,10 @@ __global__ __launch_bounds__(1024) void k_row_draws(RowStatsArgs a, const uint32
         const unsigned long long excl = block_exclusive_u64(own, sm);
         int first = 0x7fffffff;
         if (R > 0 && excl <= s && s < excl + own) {
-            // the target falls in this chunk: walk it
-            unsigned long long cum = excl;
-            bool found = false;
-            for (int v0 = lo; v0 < hi && !found; v0 += VEC) {
-                float f[VEC];
-                unpack<T>(load_vec<T>(row, v0, V, a.vec_ok), f);
-                for (int e = 0; e < VEC && !found; ++e) {
-                    const int v = v0 + e;
-                    if (v >= hi) break;
-                    bool taken = false;
-                    for (int q = 0; q < t; ++q) taken |= sm.drawn[q] == v;
-                    if (taken) continue;
-                    const float w = weight_of(f[e], M);
-                    cum += (unsigned long long)w;
-                    if (cum > s) {
-                        sm.drawn[t] = v;
-                        sm.drawn_w[t] = w;
-                        sm.drawn_l[t] = f[e];
-                        found = true;
-                    }
-                }
-            }
+            // the target falls in this chunk: wave 0 walks it below
+            sm.walk_lo = lo;
+            sm.walk_hi = hi;
+            sm.walk_excl = excl;
         } else if (R == 0) {
             // no weight left: the first token not yet drawn
             for (int v = lo; v < hi && first == 0x7fffffff; ++v) {
@@ -438,6 +422,40 @@ __global__ __launch_bounds__(1024) void k_row_draws(RowStatsArgs a, const uint32
             if ((tid & 63) == 0) sm.first_free[tid >> 6] = first;
         }
         __syncthreads();
+        if (R > 0 && tid < 64) {
+            // wave 0 walks the chunk 64 tokens at a time: the draw is the
+            // first undrawn token whose running weight passes s
+            const int wlo = sm.walk_lo, whi = sm.walk_hi;
+            unsigned long long cum = sm.walk_excl;
+            for (int v0 = wlo; v0 < whi; v0 += 64) {
+                const int v = v0 + tid;
+                float l = -__builtin_inff(), w = 0.0f;
+                if (v < whi) {
+                    bool taken = false;
+                    for (int q = 0; q < t; ++q) taken |= sm.drawn[q] == v;
+                    l = load_scalar<T>(row + v);
+                    if (!taken) w = weight_of(l, M);
+                }
+                unsigned long long incl = (unsigned long long)w;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned long long u = __shfl_up(incl, o);
+                    if (tid >= o) incl += u;
+                }
+                const unsigned long long hit = __ballot(cum + incl > s);
+                if (hit) {
+                    const int f = __ffsll((long long)hit) - 1;
+                    const float lf = __shfl(l, f), wf = __shfl(w, f);
+                    if (tid == 0) {
+                        sm.drawn[t] = v0 + f;
+                        sm.drawn_w[t] = wf;
+                        sm.drawn_l[t] = lf;
+                    }
+                    break;
+                }
+                cum += __shfl(incl, 63);
+            }
+        }
         if (R == 0 && tid == 0) {
             int f = sm.first_free[0];
             for (int j = 1; j < (NT >> 6); ++j) f = min(f, sm.first_free[j]);
