@@ -92,6 +92,13 @@ SMALL = {
     # fp32 GQA, head_dim 128, paged with poisoned tails
     "f32-gqa-paged": lambda: _small(1, num_q_heads=8, num_kv_heads=2, head_dim=128, prefix=(1, 300),
                                     block_size=16, batch=3, kinds=[0, 0, 0], poison_tail=True),
+    # fp32 kernels by head_dim and cache layout: head_dim 128 contiguous over
+    # many key chunks (several rounds of the two key groups, ragged tail);
+    # head_dim 64 paged (four key groups) with poisoned tails; empty prefix
+    "f32-d128-contig-L1000": lambda: _small(1, num_q_heads=8, num_kv_heads=4, head_dim=128, prefix=(700, 1000),
+                                            batch=2, kinds=[0, 0]),
+    "f32-d64-paged": lambda: _small(1, prefix=(1, 900), block_size=16, batch=3, kinds=[0, 0, 0], poison_tail=True),
+    "f32-L0": lambda: _small(1, prefix=0, vocab=1000),
     # bf16 contiguous, prefix shorter than one tile, and empty prefix
     "bf16-L13": lambda: _small(2, prefix=13, vocab=5000),
     "bf16-L0": lambda: _small(2, prefix=0, vocab=5000),
