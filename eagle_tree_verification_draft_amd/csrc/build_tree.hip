@@ -389,6 +389,11 @@ __global__ __launch_bounds__(1024) void k_row_draws(RowStatsArgs a, const uint32
         for (int t = tid; t < C; t += NT) { out_id[t] = -1; out_v[t] = -__builtin_inff(); }
         return;
     }
+    if (tid == 0) {
+        // an empty walk until a chunk claims the draw (one always does: s < R)
+        sm.walk_lo = sm.walk_hi = 0;
+        sm.walk_excl = 0;
+    }
     const unsigned long long W = block_sum_u64(own, sm);
     unsigned long long R = W;
     for (int t = 0; t < C; ++t) {
