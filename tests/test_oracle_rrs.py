@@ -157,3 +157,39 @@ def test_draft_on_a_token_the_target_never_emits_is_rejected():
     counts = np.bincount(bon, minlength=4)
     p = _target_probs(target_row)
     assert counts[3] == 0 and scipy.stats.chisquare(counts[:3], p[:3] / p[:3].sum() * trials).pvalue > 1e-3
+
+
+def test_bonus_after_one_rejection_is_the_exact_residual_inverse_cdf():
+    """One child x with q(x) > p(x), rejected by a word at the top of its
+    range; the bonus token for a word r must be the inverse CDF at r / 2^32 of
+    the residual max(0, p - q) / sum, computed here in exact rationals from the
+    Spec S weights (the oracle works in shifted integers; words closer than
+    1e-6 to a CDF step are skipped)."""
+    from fractions import Fraction
+    V = 6
+    target_row = np.array([1.0, 0.2, -0.5, 0.7, -2.0, 0.0], np.float32)
+    draft_row = np.array([-0.3, 1.2, 0.4, -1.0, 0.9, 0.1], np.float32)
+    P = [int(w) for w in spec_emul.weights(target_row, np.float32(target_row.max()))]
+    Q = [int(w) for w in spec_emul.weights(draft_row, np.float32(draft_row.max()))]
+    SP, SQ = sum(P), sum(Q)
+    x = 1
+    assert Fraction(P[x], SP) < Fraction(Q[x], SQ)
+    # child word in the middle of token x's draft interval
+    cw = ((sum(Q[:x]) * 2 + Q[x]) << 31) // SQ
+    res = [max(Fraction(0), Fraction(P[v], SP) - Fraction(Q[v], SQ)) for v in range(V)]
+    Z = sum(res)
+    cdf = np.cumsum([float(r / Z) for r in res])
+    words_r = np.linspace(0, (1 << 32) - 1, 4001).astype(np.uint64)
+    keep = np.array([np.min(np.abs(cdf - float(r) / 2**32)) > 1e-6 for r in words_r])
+    words_r = words_r[keep].astype(np.uint32)
+    T = len(words_r)
+    t = oracle.build_tree(np.tile(draft_row, (T, 1, 1)), 1, 1, 1, 1, m_max=1,
+                          child_words=np.full((T, 1, 1), cw, np.uint32))
+    assert (t["tokens"][:, 0] == x).all()
+    words = np.stack([np.full(T, (1 << 32) - 1, np.uint32), words_r], axis=1)
+    acc, alen, bon = oracle.accept_rrs(np.tile(target_row, (T, 2, 1)), np.tile(draft_row, (T, 1, 1)), t["tokens"],
+                                       t["parent"], t["src_row"], t["num_nodes"], 1, words)
+    assert (alen == 0).all()
+    want = np.searchsorted(cdf, words_r.astype(np.float64) / 2**32, side="right")
+    assert np.array_equal(bon, want)
+    assert res[x] == 0 and not (bon == x).any()
