@@ -109,7 +109,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification step of one "
-              "sequence batch does not span GPUs in this build", file=sys.stderr)
+              "sequence batch runs on a single GPU, and sharding sequences over GPUs is not implemented",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:
