@@ -3,12 +3,12 @@ tree construction" and its Python concept sketch) and ancestor mask ("Attention
 mask adjustment").
 
 Pins: a hand-derived golden example; the concept sketch's own special case
-(every parent at a depth shares one children list); invariants recomputed with
+(every parent at a depth shares one children list) against brute force over
+the full C-ary tree; invariants recomputed with
 library sorts and exact integer weights; degenerate shapes that reduce to a
 sort of one row or to a greedy chain; brute-force reflexive-transitive closure
 for the mask.
 """
-import heapq
 import json
 import math
 import os
@@ -52,44 +52,51 @@ def test_hand_example_tree_mask_greedy(orc):
 
 
 # ---------------------------------------------------------------------------
-# the concept sketch's special case: shared children per depth
+# the concept sketch's special case: shared children per depth, against brute
+# force over the full C-ary tree
 # ---------------------------------------------------------------------------
 
-def _sketch_semantics(per_depth, m, k, max_depth):
-    """Independent restatement of the sketch's behaviour: stable sort of the
-    current layer by V (descending) and keep k; every kept parent gets the
-    depth's (token, conf) list; V = parent V * conf; then the m largest V over
-    all generated nodes (heapq.nlargest keeps first-seen order among equals);
-    then ancestors of the selection are appended if missing."""
-    nodes = []                       # (token, V, depth, parent_index or -1)
-    layer = [(-1, 1.0)]              # (node index or -1 for the root, V)
-    for depth in range(1, max_depth + 1):
-        if depth - 1 >= len(per_depth):
+def _brute_force_shared_children(per_depth, m, k, max_depth):
+    """Every node of the full C-ary tree of depth max_depth, identified by its
+    path of child ranks; V is the explicit product of the confidences along
+    the path, multiplied root first.  A node of depth d >= 2 is generated iff
+    its parent is generated and among the first k generated nodes of depth
+    d - 1 in the order (V desc, creation asc), where creation order is
+    (depth, the parent's rank in that order, child rank).  Returns the
+    generated nodes' records and the first m of them in (V desc, creation asc)
+    order."""
+    C = len(per_depth[0])
+    rec = {}                                    # path -> dict(V, depth, creation key, token)
+    rank_in_depth = {}
+    for d in range(1, max_depth + 1):
+        if d - 1 >= len(per_depth):
             break
-        keep = sorted(layer, key=lambda t: t[1], reverse=True)[:k]
-        nxt = []
-        for par_idx, par_v in keep:
-            for tok, conf in per_depth[depth - 1]:
-                nodes.append((tok, par_v * conf, depth, par_idx))
-                nxt.append((len(nodes) - 1, par_v * conf))
-        layer = nxt
-    chosen = heapq.nlargest(m, range(len(nodes)), key=lambda i: nodes[i][1])
-    have = set(chosen)
-    for i in list(chosen):
-        a = nodes[i][3]
-        while a >= 0:
-            if a not in have:
-                chosen.append(a)
-                have.add(a)
-            a = nodes[a][3]
-    return nodes, chosen
+        if d == 1:
+            gen = [(r,) for r in range(C)]
+        else:
+            gen = [p + (r,) for p in rec if len(p) == d - 1 and rank_in_depth[p] < k for r in range(C)]
+        for p in gen:
+            v = 1.0
+            for depth_i, r in enumerate(p):
+                v = v * per_depth[depth_i][r][1]
+            parent_rank = rank_in_depth[p[:-1]] if d > 1 else 0
+            rec[p] = dict(V=v, depth=d, key=(d, parent_rank, p[-1]), token=per_depth[d - 1][p[-1]][0])
+        order = sorted(gen, key=lambda p: (-rec[p]["V"], rec[p]["key"]))
+        for r, p in enumerate(order):
+            rank_in_depth[p] = r
+    ranked = sorted(rec, key=lambda p: (-rec[p]["V"], rec[p]["key"]))
+    return rec, ranked[:m]
 
 
-@pytest.mark.parametrize("seed,V,dt", [(0, 50, "f32"), (1, 300, "bf16"), (2, 1000, "f32")])
+@pytest.mark.parametrize("seed,V,dt", [(0, 50, "f32"), (1, 300, "bf16"), (2, 1000, "f32"), (3, 40, "ties")])
 def test_sketch_special_case_shared_children(orc, seed, V, dt):
     D, k, C, m = 4, 3, 4, 12
     rng = np.random.default_rng(seed)
     base = (rng.standard_normal((D, V)) * 2).astype(np.float32)
+    if dt == "ties":
+        # few distinct logits: equal confidences among siblings and equal V
+        # across nodes, so the creation-order tie rule decides the ranking
+        base = rng.integers(0, 3, size=(D, V)).astype(np.float32)
     R = 1 + (D - 1) * k
     rows = np.zeros((R, V), np.float32)
     rows[0] = base[0]
@@ -104,13 +111,14 @@ def test_sketch_special_case_shared_children(orc, seed, V, dt):
         r = 0 if d == 0 else 1 + (d - 1) * k
         M, W, ids, ws = spec_emul.row_stats(rows[r], C)
         per_depth.append([(int(i), w / W) for i, w in zip(ids, ws)])
-    nodes, chosen = _sketch_semantics(per_depth, m, k, D)
-    assert len(chosen) == m                                     # closure added nothing
-    assert list(t["tokens"][0]) == [nodes[i][0] for i in chosen]
-    assert list(t["score"][0]) == [nodes[i][1] for i in chosen]
-    assert list(t["depth"][0]) == [nodes[i][2] for i in chosen]
-    pos_of = {n: r for r, n in enumerate(chosen)}
-    assert list(t["parent"][0]) == [-1 if nodes[i][3] < 0 else pos_of[nodes[i][3]] for i in chosen]
+    rec, chosen = _brute_force_shared_children(per_depth, m, k, D)
+    assert len(chosen) == m
+    assert all(p[:-1] in chosen for p in chosen if len(p) > 1)   # closed: adding ancestors adds nothing
+    assert list(t["tokens"][0]) == [rec[p]["token"] for p in chosen]
+    assert list(t["score"][0]) == [rec[p]["V"] for p in chosen]
+    assert list(t["depth"][0]) == [rec[p]["depth"] for p in chosen]
+    pos_of = {p: r for r, p in enumerate(chosen)}
+    assert list(t["parent"][0]) == [-1 if len(p) == 1 else pos_of[p[:-1]] for p in chosen]
 
 
 # ---------------------------------------------------------------------------
