@@ -39,7 +39,7 @@ ACCEPT_SAMPLE = 1
 # independent random streams per workload
 _STREAMS = {
     "draft": 0, "target": 1, "q": 2, "kv": 3, "draft_kv": 4,
-    "prefix": 5, "blocks": 6, "words": 7, "fresh": 8,
+    "prefix": 5, "blocks": 6, "words": 7, "fresh": 8, "plant": 9,
 }
 
 
@@ -65,7 +65,7 @@ class Workload:
     temperature: float
     target_kind: str              # "iid" or "draft_plus_noise"
     target_sigma: float = 1.0     # noise sd (draft_plus_noise) or iid sd
-    poison_tail: bool = False     # NaN in unused slots of each last page
+    poison_tail: bool = False     # NaN in the cache slots past each prefix (last page tail, or contiguous tail)
 
     @property
     def rows_dynamic(self) -> int:
@@ -236,6 +236,11 @@ def attn_inputs(w: Workload, seed: int, device="cpu", prefix_seed: Optional[int]
         L = (int(plen.max()) + 7) // 8 * 8
         k_cache = _normal((B, Hkv, L, d), 1.0, w.dtype, gkv, device)
         v_cache = _normal((B, Hkv, d, L), 1.0, w.dtype, gkv, device)
+        if w.poison_tail:
+            for b in range(B):
+                used = int(plen[b])
+                k_cache[b, :, used:, :] = float("nan")
+                v_cache[b, :, :, used:] = float("nan")
         return AttnInputs(q, k_draft, v_draft, k_cache, v_cache, None, plen.to(device), 0, L)
     bs = w.block_size
     nblk = [(int(x) + bs - 1) // bs for x in plen]
@@ -259,6 +264,29 @@ def attn_inputs(w: Workload, seed: int, device="cpu", prefix_seed: Optional[int]
                 v_cache[blk, :, :, used:] = float("nan")
     return AttnInputs(q, k_draft, v_draft, k_cache, v_cache, table.to(device), plen.to(device),
                       bs, int(plen.max()))
+
+
+def plant_draft_keys(attn: AttnInputs, w: Workload, seed: int, gamma: float = 1.2) -> AttnInputs:
+    """A copy of `attn` in which the draft keys carry most of every query's
+    attention mass, so that which draft keys a query sees changes its output
+    by O(1) even over a prefix of 32k keys.
+
+    Per (sequence b, kv head) one direction u ~ N(0, 1)^d is drawn; every
+    query head of that kv head gets q + u, and every draft key of it becomes
+    gamma * u + k_draft.  A query then scores a draft key near
+    gamma * d * scale (about 13.6 at d = 128 and scale 1/sqrt(d)), while its
+    prefix scores stay N(0, 2); the prefix keys keep a small share.  Values
+    are drawn and combined in fp32 and rounded (RNE) to the workload dtype.
+    """
+    B, Hkv, d = w.batch, w.num_kv_heads, w.head_dim
+    G = w.num_q_heads // Hkv
+    dev = attn.q.device
+    g = _gen(seed, "plant", "cpu")
+    u = torch.randn((B, Hkv, d), generator=g, dtype=torch.float32).to(dev)
+    uq = u.repeat_interleave(G, dim=1)                               # [B][Hq][d]
+    q = (attn.q.to(torch.float32) + uq[:, None]).to(w.dtype)
+    kd = (attn.k_draft.to(torch.float32) + gamma * u[:, None]).to(w.dtype)
+    return dataclasses.replace(attn, q=q, k_draft=kd)
 
 
 def rand_words(w: Workload, seed: int, device="cpu") -> torch.Tensor:

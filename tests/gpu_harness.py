@@ -91,8 +91,8 @@ def oracle_mask(c: Case):
     return oracle.tree_mask(c.otree["parent"], c.otree["num_nodes"], c.attn.prefix_len.cpu().numpy())
 
 
-def attn_host(c: Case):
-    a = c.attn
+def attn_host(c: Case, attn=None):
+    a = c.attn if attn is None else attn
     return dict(q=to_np(a.q), k_draft=to_np(a.k_draft), v_draft=to_np(a.v_draft), k_cache=to_np(a.k_cache),
                 v_cache=to_np(a.v_cache), block_table=None if a.block_table is None else to_np(a.block_table),
                 prefix_len=to_np(a.prefix_len))
@@ -102,19 +102,38 @@ def gpu_out_f64(c: Case) -> np.ndarray:
     return c.step.out.to(torch.float64).cpu().numpy()
 
 
-def check_attn_rows(c: Case, sel, tol) -> float:
-    """Compares selected output rows (b, i, h) against the oracle; returns max-abs error."""
-    h = attn_host(c)
+def oracle_attn_rows(h: dict, sel, anc) -> np.ndarray:
+    return oracle.tree_attn_rows(h["q"], h["k_draft"], h["v_draft"], h["k_cache"], h["v_cache"],
+                                 h["block_table"], h["prefix_len"], anc, sel)
+
+
+def check_attn_rows(c: Case, sel, tol, attn=None, power=None):
+    """Compares selected output rows (b, i, h) against the oracle.
+
+    Returns (max-abs error, relative L2 error over the selected rows).  With
+    power = f, each row's error must also stay below f times that row's
+    max-abs gap between the oracle with and without the draft keys, so the
+    check is sensitive to the tree part of the keys."""
     anc, _ = oracle_mask(c)
-    ref = oracle.tree_attn_rows(h["q"], h["k_draft"], h["v_draft"], h["k_cache"], h["v_cache"],
-                                h["block_table"], h["prefix_len"], anc, sel)
+    h = attn_host(c, attn)
+    ref = oracle_attn_rows(h, sel, anc)
     got = gpu_out_f64(c)
     g = np.stack([got[b, i, hh] for b, i, hh in sel])
     err = np.abs(g - ref)
     assert np.isfinite(g).all(), "non-finite attention output"
     mx = float(err.max()) if err.size else 0.0
+    den = float(np.sqrt((ref * ref).sum()))
+    rl2 = float(np.sqrt(((g - ref) ** 2).sum())) / den if den > 0 else 0.0
     assert mx <= tol, f"attention max-abs error {mx} > {tol} at row {sel[int(np.argmax(err.max(axis=1)))]}"
-    return mx
+    if power is not None:
+        nodraft = oracle_attn_rows(h, sel, np.zeros_like(anc))
+        gap = np.abs(nodraft - ref).max(axis=1)
+        row_err = err.max(axis=1)
+        worst = int(np.argmax(row_err / np.maximum(gap, 1e-300)))
+        assert (row_err <= power * gap).all(), \
+            f"row {sel[worst]}: error {row_err[worst]} not below {power} x draft-key gap {gap[worst]}"
+        assert float(gap.min()) > 10 * tol, f"draft keys move row {sel[int(np.argmin(gap))]} by only {gap.min()}"
+    return mx, rl2
 
 
 def sample_rows(c: Case, n_rows: int, rng) -> list:
