@@ -266,26 +266,28 @@ def attn_inputs(w: Workload, seed: int, device="cpu", prefix_seed: Optional[int]
                       bs, int(plen.max()))
 
 
-def plant_draft_keys(attn: AttnInputs, w: Workload, seed: int, gamma: float = 1.2) -> AttnInputs:
+def plant_draft_keys(attn: AttnInputs, w: Workload, seed: int, gamma: float = 1.5) -> AttnInputs:
     """A copy of `attn` in which the draft keys carry most of every query's
     attention mass, so that which draft keys a query sees changes its output
     by O(1) even over a prefix of 32k keys.
 
-    Per (sequence b, kv head) one direction u ~ N(0, 1)^d is drawn; every
-    query head of that kv head gets q + u, and every draft key of it becomes
-    gamma * u + k_draft.  A query then scores a draft key near
-    gamma * d * scale (about 13.6 at d = 128 and scale 1/sqrt(d)), while its
-    prefix scores stay N(0, 2); the prefix keys keep a small share.  Values
-    are drawn and combined in fp32 and rounded (RNE) to the workload dtype.
+    Per (sequence b, kv head) one direction u is drawn, N(0, 1)^d rescaled to
+    |u|^2 = d; every query head of that kv head becomes u + q / 2 and every
+    draft key of it gamma * u + k_draft / 2.  At scale 1/sqrt(d) a query then
+    scores a draft key near gamma * sqrt(d) (about 17 at d = 128) with a
+    spread near 1, and a prefix key N(0, 1.25): the draft keys on a query's
+    path hold most of its softmax mass, and the prefix keeps a small share.
+    Values are combined in fp32 and rounded (RNE) to the workload dtype.
     """
     B, Hkv, d = w.batch, w.num_kv_heads, w.head_dim
     G = w.num_q_heads // Hkv
     dev = attn.q.device
     g = _gen(seed, "plant", "cpu")
-    u = torch.randn((B, Hkv, d), generator=g, dtype=torch.float32).to(dev)
+    u = torch.randn((B, Hkv, d), generator=g, dtype=torch.float32)
+    u = (u * (math.sqrt(d) / u.norm(dim=-1, keepdim=True))).to(dev)
     uq = u.repeat_interleave(G, dim=1)                               # [B][Hq][d]
-    q = (attn.q.to(torch.float32) + uq[:, None]).to(w.dtype)
-    kd = (attn.k_draft.to(torch.float32) + gamma * u[:, None]).to(w.dtype)
+    q = (0.5 * attn.q.to(torch.float32) + uq[:, None]).to(w.dtype)
+    kd = (0.5 * attn.k_draft.to(torch.float32) + gamma * u[:, None]).to(w.dtype)
     return dataclasses.replace(attn, q=q, k_draft=kd)
 
 
