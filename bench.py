@@ -79,6 +79,22 @@ def traffic_note(w):
     return float(note["traffic_bytes_per_call"]), os.path.relpath(path, ROOT)
 
 
+def mfma_note(w):
+    """Counter-derived matrix-core utilisation of the attention kernel from the
+    committed note for this workload (rocprofv3 MfmaUtil), or None when there
+    is no note or the kernel source changed since its counters were taken."""
+    from eagle_tree_verification_draft_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"tree_attn.{w.name}.mfma.txt")
+    if not os.path.exists(path):
+        return None, "no counter note for this workload"
+    note = profiling.read_note(path)
+    srcs = [os.path.join(ROOT, s) for s in note.get("source", "").split(",") if s]
+    if not srcs or any(not os.path.exists(s) for s in srcs) or \
+            profiling.source_hash(srcs) != note.get("source_sha256") or "mfma_util" not in note:
+        return None, "kernel source changed since the counters were taken"
+    return float(note["mfma_util"]), os.path.relpath(path, ROOT)
+
+
 def copy_calibration(nbytes):
     """A plain copy of known size (read nbytes, write nbytes) for scaling the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -347,6 +363,7 @@ def bench_workload(n, args, extras, cpu_seconds):
         bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
     value = tokens_per_step / (ms_per_step * 1e-3)
     traffic, traffic_src = traffic_note(w)
+    mfma_util, mfma_src = mfma_note(w)
 
     # ---- the oracle on the host cores (whole steps) ----------------------
     cpu = None
@@ -374,7 +391,9 @@ def bench_workload(n, args, extras, cpu_seconds):
                      "avg_us": round(attn_avg_ms * 1e3, 2), "timed_calls": attn_calls,
                      "eager_event_us": round(attn_eager_ms * 1e3, 2),
                      "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "tflops": round(tflops, 2), "mfma_frac": round(mfma_frac, 4)},
+                     "tflops": round(tflops, 2), "mfma_frac": round(mfma_frac, 4),
+                     "mfma_frac_is": "algorithmic flops / call time / bf16 dense peak",
+                     "mfma_util_counter": mfma_util, "mfma_util_source": mfma_src},
         "cpu_baseline": cpu,
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},

@@ -14,7 +14,14 @@
         Prints a text note whose 'source_sha256' line lets bench.py tell
         whether the kernel source changed since the counters were taken.
 
-Both read rocprofv3's own output files only; nothing here touches the GPU.
+    python -m eagle_tree_verification_draft_amd.profiling mfma --pmc DIR \
+        --kernels k_tree_attn_bf16 --workload NAME --source FILE[,FILE...] [--command TEXT]
+        Matrix-core utilisation per dispatch of the named kernels from a
+        --pmc run of MfmaUtil, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
+        (MfmaUtil = busy cycles summed over the SIMDs / (GUI-active cycles x
+        SIMD count), in percent), with the same source hash line.
+
+All read rocprofv3's own output files only; nothing here touches the GPU.
 """
 from __future__ import annotations
 
@@ -90,6 +97,47 @@ def _pmc_rows(d):
     return rows
 
 
+def _pmc_rows_by_counter(d):
+    """(kernel name, counter name, value, duration ns) per dispatch from a --pmc csv run."""
+    path = _find(d, "*counter_collection.csv")
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""), float(r["Counter_Value"]),
+                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return rows
+
+
+def mfma(a):
+    rows = _pmc_rows_by_counter(a.pmc)
+    lines = []
+    if a.command:
+        lines.append(f"command: {a.command}")
+    lines.append(f"workload: {a.workload}")
+    lines.append(f"source: {a.source}")
+    lines.append(f"source_sha256: {source_hash(a.source.split(','))}")
+    util = None
+    for k in a.kernels.split(","):
+        sel = [r for r in rows if k in r[0]]
+        if not sel:
+            lines.append(f"kernel {k}: not found in the counter run")
+            continue
+        by = {}
+        for name, cn, v, dur in sel:
+            by.setdefault(cn, []).append((v, dur))
+        avg = {cn: sum(v for v, _ in xs) / len(xs) for cn, xs in by.items()}
+        durs = [d for _, d in by.get("MfmaUtil", by[next(iter(by))])]
+        n = len(durs)
+        lines.append(f"kernel {k}: dispatches {n}, average duration {sum(durs) / n / 1e3:.2f} us")
+        for cn in sorted(avg):
+            lines.append(f"  {cn}: {avg[cn]:.2f}")
+        if util is None and "MfmaUtil" in avg:
+            util = avg["MfmaUtil"] / 100.0
+    if util is not None:
+        lines.append(f"mfma_util: {util:.4f}")
+    return "\n".join(lines)
+
+
 def _per_dispatch(rows, key):
     vals = [v for n, v in rows if key in n]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
@@ -145,8 +193,14 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--source", required=True)
     t.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True)
+    m.add_argument("--kernels", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--source", required=True)
+    m.add_argument("--command", default="")
     a = ap.parse_args(argv)
-    print(stats(a.dir) if a.cmd == "stats" else traffic(a))
+    print(stats(a.dir) if a.cmd == "stats" else traffic(a) if a.cmd == "traffic" else mfma(a))
 
 
 if __name__ == "__main__":

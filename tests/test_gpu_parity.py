@@ -149,6 +149,10 @@ SMALL = {
     # paged, mixed trees and chains, ragged lengths, poisoned tails
     "bf16-paged-mixed": lambda: _small(5, batch=6, vocab=7001, prefix=(1, 5000),
                                        kinds=[0, 1, 0, 1, 1, 0]),
+    # contiguous cache, trees and chains in one batch (each workgroup picks the
+    # 8-wave or the few-row form by its own sequence's rows), one and many splits
+    "bf16-contig-mixed": lambda: _small(5, batch=4, vocab=3000, block_size=0, prefix=(50, 9000),
+                                        kinds=[0, 1, 1, 0], poison_tail=True),
     # paged MHA (query rows <= 64: the 4-wave key-half kernel), ragged lengths, poisoned tails
     "bf16-mha-paged16": lambda: _small(2, batch=3, num_q_heads=8, num_kv_heads=8, prefix=(1, 2500),
                                        block_size=16, poison_tail=True, kinds=[0, 0, 0], vocab=3000),
