@@ -33,7 +33,7 @@ DEVERR_NONFINITE_ROW, DEVERR_CLOSURE, DEVERR_PREFIX, DEVERR_PATH, DEVERR_TREE = 
 EXPORTS = (
     "eagle_workspace_init", "eagle_read_errors",
     "eagle_build_tree_workspace_size", "eagle_build_tree",
-    "eagle_build_tree_mask", "eagle_build_tree_sampled", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
+    "eagle_build_tree_mask", "eagle_build_tree_mask_noalloc", "eagle_build_tree_sampled", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
     "eagle_tree_mask",
     "eagle_tree_attn_workspace_size", "eagle_tree_attn",
     "eagle_kv_commit",
@@ -90,6 +90,7 @@ def lib() -> C.CDLL:
                                        vp, sz, vp]
         L.eagle_build_tree_mask.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, sz, vp]
+        L.eagle_build_tree_mask_noalloc.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64] + [vp] * 11 + [vp]
         L.eagle_build_tree_sampled.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64] + [vp] * 8 + [sz, vp]
         L.eagle_build_tree_template.argtypes = [C.POINTER(TreeParams), i32, vp, C.c_int, i64, i32] + [vp] * 9 + [sz, vp]
         L.eagle_tree_expand.argtypes = [C.POINTER(TreeParams), i32, i32, vp, C.c_int, i64, vp, vp, vp, vp, sz, vp]
@@ -113,6 +114,7 @@ def lib() -> C.CDLL:
         L.eagle_last_error.argtypes = []
         L.eagle_last_error.restype = C.c_char_p
         for f in ("eagle_workspace_init", "eagle_read_errors", "eagle_build_tree", "eagle_build_tree_mask",
+                  "eagle_build_tree_mask_noalloc",
                   "eagle_build_tree_sampled", "eagle_build_tree_template", "eagle_tree_expand", "eagle_tree_finish",
                   "eagle_tree_mask", "eagle_tree_attn", "eagle_kv_commit", "eagle_accept", "eagle_accept_rrs",
                   "eagle_pdraft_prepare"):
@@ -200,6 +202,19 @@ def build_tree_mask(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind:
                                        _ptr(src_row), _ptr(num_nodes), _ptr(anc_mask), _ptr(pos), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "eagle_build_tree_mask")
+
+
+def build_tree_mask_noalloc(p: TreeParams, batch: int, draft_logits: torch.Tensor, kind: Optional[torch.Tensor],
+                            prefix_len, tokens, parent, depth, score, src_row, num_nodes, anc_mask, pos,
+                            device_errors: Optional[torch.Tensor] = None, stream=None):
+    """eagle_build_tree_mask on the library's static scratch (no workspace);
+    device_errors: optional int32 device tensor of one element."""
+    rows, stride = _rows(draft_logits)
+    _check(lib().eagle_build_tree_mask_noalloc(C.byref(p), batch, rows, dtype_code(draft_logits.dtype), stride,
+                                               _ptr(kind), _ptr(prefix_len), _ptr(tokens), _ptr(parent), _ptr(depth),
+                                               _ptr(score), _ptr(src_row), _ptr(num_nodes), _ptr(anc_mask), _ptr(pos),
+                                               _ptr(device_errors), _stream(stream)),
+           "eagle_build_tree_mask_noalloc")
 
 
 def build_tree_sampled(p: TreeParams, batch: int, draft_logits: torch.Tensor, child_words, tokens, parent, depth,

@@ -3,11 +3,17 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
 
 using namespace eagle;
+
+// scratch of eagle_build_tree_mask_noalloc (the build workspace of several
+// hundred sequences at the largest vocabulary)
+constexpr size_t kNoAllocScratch = 4u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
 
 namespace {
 
@@ -82,6 +88,56 @@ eagle_status check_tree_params(const eagle_tree_params *p, int32_t batch)
     return EAGLE_OK;
 }
 
+eagle_status check_build_mask_args(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                   eagle_dtype dtype, int64_t row_stride, const int32_t *prefix_len,
+                                   const int32_t *tokens, const int32_t *parent, const int32_t *depth,
+                                   const double *score, const int32_t *src_row, const int32_t *num_nodes,
+                                   const uint64_t *anc_mask, const int32_t *pos)
+{
+    eagle_status s = check_tree_params(p, batch);
+    if (s != EAGLE_OK) return s;
+    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes || !prefix_len ||
+        !anc_mask || !pos)
+        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
+    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
+    return EAGLE_OK;
+}
+
+// ---- scratch of the build-and-mask call that allocates nothing ----------
+// The static device array `scratch` (above) takes the place of the caller's
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends; its device address is taken once per device, with that
+// device current, and kept here.  Host code uses only that address: the
+// array's name is a host-side stand-in, not a device address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+eagle_status scratch_of_current_device(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(EAGLE_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return EAGLE_OK;
+}
+
+// the call's device error word, copied to the caller's (one lane: a vector store)
+__global__ void k_copy_error_word(const uint32_t *src, uint32_t *dst)
+{
+    const int i = threadIdx.x;
+    dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,13 +205,9 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                                    double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc_mask,
                                    int32_t *pos, void *workspace, size_t workspace_bytes, void *stream)
 {
-    eagle_status s = check_tree_params(p, batch);
+    eagle_status s = check_build_mask_args(p, batch, draft_logits, dtype, row_stride, prefix_len, tokens, parent,
+                                           depth, score, src_row, num_nodes, anc_mask, pos);
     if (s != EAGLE_OK) return s;
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
-    if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes || !prefix_len ||
-        !anc_mask || !pos)
-        return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
-    if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
     s = check_workspace(workspace, workspace_bytes, build_layout(p, batch).total);
     if (s != EAGLE_OK) return s;
     if (batch == 0) return ok();
@@ -163,6 +215,37 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                                              parent, depth, score, src_row, num_nodes, anc_mask, pos, workspace,
                                              (hipStream_t)stream),
                       "build_tree_mask launch");
+}
+
+eagle_status eagle_build_tree_mask_noalloc(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                           eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
+                                           const int32_t *prefix_len, int32_t *tokens, int32_t *parent,
+                                           int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                                           uint64_t *anc_mask, int32_t *pos, uint32_t *device_errors, void *stream)
+{
+    eagle_status s = check_build_mask_args(p, batch, draft_logits, dtype, row_stride, prefix_len, tokens, parent,
+                                           depth, score, src_row, num_nodes, anc_mask, pos);
+    if (s != EAGLE_OK) return s;
+    const size_t need = build_layout(p, batch).total;
+    if (need > kNoAllocScratch)
+        return fail(EAGLE_ERR_WORKSPACE, "the call needs %zu bytes of scratch; the static array holds %zu", need,
+                    kNoAllocScratch);
+    if (batch == 0) return ok();
+    void *ws = nullptr;
+    s = scratch_of_current_device(&ws);
+    if (s != EAGLE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    // the error word starts at zero on every call (a fill kernel, no memset node)
+    hipError_t e = launch_zero(ws, 16, st);
+    if (e == hipSuccess)
+        e = launch_build_tree_mask(p, batch, draft_logits, dtype, row_stride, kind, prefix_len, tokens, parent,
+                                   depth, score, src_row, num_nodes, anc_mask, pos, ws, st);
+    if (e == hipSuccess && device_errors) {
+        hipLaunchKernelGGL(k_copy_error_word, dim3(1), dim3(1), 0, st, static_cast<const uint32_t *>(ws),
+                           device_errors);
+        e = hipGetLastError();
+    }
+    return hip_status(e, "build_tree_mask_noalloc launch");
 }
 
 eagle_status eagle_build_tree_sampled(const eagle_tree_params *p, int32_t batch, const void *draft_logits,

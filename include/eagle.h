@@ -147,6 +147,9 @@ size_t eagle_build_tree_workspace_size(const eagle_tree_params *p, int32_t batch
  * an unknown policy or a tree without rerank larger than m_max;
  * EAGLE_ERR_UNSUPPORTED past the v1 limits; EAGLE_ERR_WORKSPACE if the
  * workspace is smaller than eagle_build_tree_workspace_size().
+ * Device errors: NONFINITE_ROW when a used draft row holds a NaN or +Inf or
+ * is all -Inf; that sequence's outputs are then unspecified (the other
+ * sequences' are not affected).
  */
 eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
                               eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
@@ -166,6 +169,28 @@ eagle_status eagle_build_tree_mask(const eagle_tree_params *p, int32_t batch, co
                                    const int32_t *prefix_len, int32_t *tokens, int32_t *parent, int32_t *depth,
                                    double *score, int32_t *src_row, int32_t *num_nodes, uint64_t *anc_mask,
                                    int32_t *pos, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * eagle_build_tree_mask without a workspace, for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, checks, outputs and
+ * kernels as eagle_build_tree_mask; its workspace is a static device array
+ * of the library (4 MiB on each GPU it runs on, held until the process
+ * ends).  The call allocates and frees nothing.
+ * device_errors: NULL, or a caller-owned device uint32 that receives this
+ * call's device error bits (EAGLE_DEVERR_*; the array's error word is
+ * cleared at the start of every call, by a kernel).  With batch == 0 nothing
+ * is launched and device_errors is left as it is.
+ * Calls on one GPU share its array and keep the last call's contents: calls
+ * that overlap on one GPU (other streams, other threads) race.
+ * Errors: those of eagle_build_tree_mask, and EAGLE_ERR_WORKSPACE when
+ * eagle_build_tree_workspace_size(p, batch) exceeds the array (4 MiB).
+ */
+eagle_status eagle_build_tree_mask_noalloc(const eagle_tree_params *p, int32_t batch, const void *draft_logits,
+                                           eagle_dtype dtype, int64_t row_stride, const int32_t *kind,
+                                           const int32_t *prefix_len, int32_t *tokens, int32_t *parent,
+                                           int32_t *depth, double *score, int32_t *src_row, int32_t *num_nodes,
+                                           uint64_t *anc_mask, int32_t *pos, uint32_t *device_errors, void *stream);
 
 /*
  * A dynamic tree whose children are drawn from the draft instead of taken

@@ -272,6 +272,28 @@ def test_zero_batch_launches_nothing():
                              C.c_void_p(1 << 21), 256, None) == E.EAGLE_OK
 
 
+def test_build_tree_mask_noalloc_checks_before_any_launch():
+    # the call with no workspace: same argument checks as the fused call, a
+    # size check against its static scratch, and batch 0 launches nothing
+    L = E.lib()
+    p = _tree()
+    out = C.c_void_p(1 << 24)
+    f = L.eagle_build_tree_mask_noalloc
+    assert f(C.byref(p), 1, None, 1, 32000, None, out, out, out, out, out, out, out, out, out, None, None) \
+        == E.EAGLE_ERR_INVALID
+    assert f(C.byref(p), 1, out, 1, 31999, None, out, out, out, out, out, out, out, out, out, None, None) \
+        == E.EAGLE_ERR_INVALID
+    assert f(C.byref(p), 1, out, 1, 32000, None, None, out, out, out, out, out, out, out, out, None, None) \
+        == E.EAGLE_ERR_INVALID
+    big = 100000
+    assert E.build_tree_workspace_size(p, big) > 4 << 20
+    assert f(C.byref(p), big, out, 1, 32000, None, out, out, out, out, out, out, out, out, out, None, None) \
+        == E.EAGLE_ERR_WORKSPACE
+    assert b"static array holds" in L.eagle_last_error()
+    assert f(C.byref(p), 0, out, 1, 32000, None, out, out, out, out, out, out, out, out, out, None, None) \
+        == E.EAGLE_OK
+
+
 def test_logit_rows_marshalling():
     """Rows inside a wider buffer pass their stride; anything else is refused."""
     import torch
