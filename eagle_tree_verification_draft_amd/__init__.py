@@ -20,7 +20,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libeagle.so")
+# EAGLE_LIB may name another build of the same sources (the host-sanitizer
+# build of tests/sanitize.py)
+LIB_PATH = os.environ.get("EAGLE_LIB") or os.path.join(_HERE, "libeagle.so")
 
 EAGLE_OK, EAGLE_ERR_INVALID, EAGLE_ERR_UNSUPPORTED, EAGLE_ERR_WORKSPACE, EAGLE_ERR_HIP = 0, -1, -2, -3, -4
 EAGLE_F32, EAGLE_BF16 = 0, 1

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 
 #include "common.h"
@@ -41,6 +42,22 @@ eagle_status hip_status(hipError_t e, const char *what)
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The integer a C caller stored in an enum-typed argument or field, read
+// without an enum-typed load: values outside the enum are rejected, not used.
+template <class T>
+int raw_int(const T &v)
+{
+    static_assert(sizeof(T) == sizeof(int), "enum arguments are int-sized");
+    int x;
+    std::memcpy(&x, &v, sizeof x);
+    return x;
+}
+bool valid_dtype(const eagle_dtype &d)
+{
+    const int x = raw_int(d);
+    return x == EAGLE_F32 || x == EAGLE_BF16;
+}
 
 eagle_status check_workspace(void *ws, size_t have, size_t need)
 {
@@ -96,7 +113,7 @@ eagle_status check_build_mask_args(const eagle_tree_params *p, int32_t batch, co
 {
     eagle_status s = check_tree_params(p, batch);
     if (s != EAGLE_OK) return s;
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes || !prefix_len ||
         !anc_mask || !pos)
         return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
@@ -187,7 +204,7 @@ eagle_status eagle_build_tree(const eagle_tree_params *p, int32_t batch, const v
 {
     eagle_status s = check_tree_params(p, batch);
     if (s != EAGLE_OK) return s;
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (!draft_logits || !tokens || !parent || !depth || !score || !src_row || !num_nodes)
         return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
     if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
@@ -264,7 +281,7 @@ eagle_status eagle_build_tree_sampled(const eagle_tree_params *p, int32_t batch,
     }
     if (tot > p->m_max)
         return fail(EAGLE_ERR_INVALID, "a sampled tree keeps all %lld candidates > m_max %d", tot, p->m_max);
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (!draft_logits || !child_words || !tokens || !parent || !depth || !score || !src_row || !num_nodes)
         return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
     if (row_stride < p->vocab) return fail(EAGLE_ERR_INVALID, "row_stride %lld < vocab %d", (long long)row_stride, p->vocab);
@@ -284,7 +301,7 @@ eagle_status eagle_build_tree_template(const eagle_tree_params *p, int32_t batch
 {
     if (!p) return fail(EAGLE_ERR_INVALID, "tree params are NULL");
     if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (p->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", p->vocab);
     if (p->vocab > kMaxVocab) return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d > %d", p->vocab, kMaxVocab);
     if (p->children < 1 || p->children > p->vocab)
@@ -312,7 +329,7 @@ eagle_status eagle_tree_expand(const eagle_tree_params *p, int32_t batch, int32_
 {
     eagle_status s = check_tree_params(p, batch);
     if (s != EAGLE_OK) return s;
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (level < 0 || level >= p->depth) return fail(EAGLE_ERR_INVALID, "level %d not in [0, depth %d)", level, p->depth);
     if (!level_logits || !frontier_tokens || !frontier_parent || !frontier_score)
         return fail(EAGLE_ERR_INVALID, "a required pointer is NULL");
@@ -366,7 +383,7 @@ static eagle_status check_attn_params(const eagle_attn_params *a, int32_t batch)
 {
     if (!a) return fail(EAGLE_ERR_INVALID, "attention params are NULL");
     if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
-    if (a->dtype != EAGLE_F32 && a->dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)a->dtype);
+    if (!valid_dtype(a->dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(a->dtype));
     if (a->num_kv_heads < 1 || a->num_q_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
         return fail(EAGLE_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
                     a->num_q_heads, a->num_kv_heads);
@@ -464,9 +481,9 @@ eagle_status eagle_accept(const eagle_accept_params *a, int32_t batch, const voi
 {
     if (!a) return fail(EAGLE_ERR_INVALID, "accept params are NULL");
     if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
-    if (a->mode != EAGLE_ACCEPT_GREEDY && a->mode != EAGLE_ACCEPT_SAMPLE)
-        return fail(EAGLE_ERR_INVALID, "accept mode %d", (int)a->mode);
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (raw_int(a->mode) != EAGLE_ACCEPT_GREEDY && raw_int(a->mode) != EAGLE_ACCEPT_SAMPLE)
+        return fail(EAGLE_ERR_INVALID, "accept mode %d", raw_int(a->mode));
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (a->mode == EAGLE_ACCEPT_SAMPLE && !(a->temperature > 0.0f && std::isfinite(a->temperature)))
         return fail(EAGLE_ERR_INVALID, "sampling needs a finite temperature > 0");
     if (a->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", a->vocab);
@@ -502,7 +519,7 @@ eagle_status eagle_accept_rrs(const eagle_accept_params *a, int32_t batch, const
 {
     if (!a) return fail(EAGLE_ERR_INVALID, "accept params are NULL");
     if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
-    if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!valid_dtype(dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(dtype));
     if (!(a->temperature > 0.0f && std::isfinite(a->temperature)))
         return fail(EAGLE_ERR_INVALID, "recursive rejection sampling needs a finite temperature > 0");
     if (a->vocab < 1) return fail(EAGLE_ERR_INVALID, "vocab %d < 1", a->vocab);
@@ -537,7 +554,7 @@ eagle_status eagle_pdraft_prepare(const eagle_pdraft_params *p, int32_t batch, c
 {
     if (!p) return fail(EAGLE_ERR_INVALID, "parallel-draft params are NULL");
     if (batch < 0) return fail(EAGLE_ERR_INVALID, "batch %d < 0", batch);
-    if (p->dtype != EAGLE_F32 && p->dtype != EAGLE_BF16) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", (int)p->dtype);
+    if (!valid_dtype(p->dtype)) return fail(EAGLE_ERR_UNSUPPORTED, "dtype %d", raw_int(p->dtype));
     if (p->m_max < 1 || p->m_max > kMaxMMax) return fail(EAGLE_ERR_INVALID, "m_max %d not in [1, %d]", p->m_max, kMaxMMax);
     if (p->max_accept < 1 || p->k_draft < 1 || p->hidden < 1)
         return fail(EAGLE_ERR_INVALID, "max_accept %d, k_draft %d and hidden %d must be >= 1", p->max_accept,

@@ -37,10 +37,15 @@ _lib = None
 
 
 def lib():
+    """Loads liboracle.so (built here when missing or stale), or the library
+    ORACLE_LIB names (a sanitizer build, see tests/sanitize.py)."""
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(_LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB
+        L = C.CDLL(path)
         vp, i32, i64, f32, f64 = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_double
         L.orc_exp_spec.restype = f32
         L.orc_exp_spec.argtypes = [f32]
