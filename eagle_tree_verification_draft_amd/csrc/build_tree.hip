@@ -523,6 +523,16 @@ struct TreeSmem {
     int lvl_off[kMaxDepth + 1];             // first creation index of each depth, then N
 };
 
+// next double below v, for a key v >= 0 (0 -> the negative denormal closest
+// to 0): for finite x, x >= v exactly when x > below(v)
+__device__ __forceinline__ double below(double v)
+{
+    return v > 0.0 ? __longlong_as_double(__double_as_longlong(v) - 1) : -__longlong_as_double(1ll);
+}
+
+// kC: the children per list when fixed at compile time (10, the common case),
+// or 0 for any C up to kMaxChildren
+template <int kC>
 __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
 {
     __shared__ TreeSmem sm;
@@ -580,7 +590,8 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
         return;
     }
 
-    const int D = a.depth_max, k = a.topk, C = a.children, m = a.m;
+    const int D = a.depth_max, k = a.topk, C = kC ? kC : a.children, m = a.m;
+    constexpr int kSlots = kC ? kC : kMaxChildren;   // list entries read per list
     const bool conf_key = a.policy == EAGLE_POLICY_CONF || a.policy == EAGLE_POLICY_CONF_NO_RERANK;
     const int R = 1 + (D - 1) * k;
     // the rows' children in rank order, c = W35(l - M) / W
@@ -628,15 +639,22 @@ __global__ __launch_bounds__(1024) void k_tree_select(TreeSelectArgs a)
                     // the whole list is read first (one LDS round trip); slots
                     // past C are read but not counted
                     const double *L = sm.key + off + q * C;
-                    double vl[kMaxChildren];
+                    double vl[kSlots];
 #pragma unroll
-                    for (int i = 0; i < kMaxChildren; ++i) vl[i] = L[i];
-                    // bit i set: entry i of q precedes x when its V equals x's
-                    // (earlier lists entirely; in x's own list, entries before x)
-                    const uint32_t tie = q < p ? 0xffffu : (q == p ? (1u << j) - 1u : 0u);
+                    for (int i = 0; i < kSlots; ++i) vl[i] = L[i];
+                    if (q != p) {
+                        // an earlier list's entries precede x when their key is
+                        // at least x's (ties: created first), a later list's
+                        // when it is greater: one compare against t each
+                        const double t = q < p ? below(vx) : vx;
 #pragma unroll
-                    for (int i = 0; i < kMaxChildren; ++i)
-                        c += (i < C && (vl[i] > vx || (vl[i] == vx && ((tie >> i) & 1u)))) ? 1 : 0;
+                        for (int i = 0; i < kSlots; ++i) c += ((kC || i < C) && vl[i] > t) ? 1 : 0;
+                    } else {
+                        // x's own list: entries created before x win ties
+#pragma unroll
+                        for (int i = 0; i < kSlots; ++i)
+                            c += ((kC || i < C) && (vl[i] > vx || (vl[i] == vx && i < j))) ? 1 : 0;
+                    }
                 }
                 if (c) atomicAdd(&sm.rank_d[off + x], c);
             }
@@ -1122,7 +1140,8 @@ static hipError_t launch_select(const eagle_tree_params *p, int32_t batch, const
     ta.pos = pos;
     ta.err = ra.err;
     if (batch <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_tree_select, dim3(batch), dim3(1024), 0, st, ta);
+    if (p->children == 10) hipLaunchKernelGGL(k_tree_select<10>, dim3(batch), dim3(1024), 0, st, ta);
+    else hipLaunchKernelGGL(k_tree_select<0>, dim3(batch), dim3(1024), 0, st, ta);
     return hipGetLastError();
 }
 
