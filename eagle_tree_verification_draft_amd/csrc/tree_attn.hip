@@ -90,15 +90,18 @@ template <int kRing> struct AttnSmem;
 template <> struct AttnSmem<4> {
     AttnBuf buf[4];
     u32x4a dv[kTK * 16];   // draft V rows as they arrive (key-major, swizzled like K)
-    int bt[kMaxPages];
+    // element offset of each page of the split within the cache, kv head
+    // included: page p's (kv head, key, dim) K element sits at pb[p] +
+    // key * head_dim + dim, its V^T element at pb[p] + dim * page + key
+    unsigned long long pb[kMaxPages];
 };
 template <> struct AttnSmem<5> {
     AttnBuf buf[5];
 };
 static_assert(sizeof(AttnSmem<5>) <= 160 * 1024, "LDS");
 
-__device__ __forceinline__ int *page_list(AttnSmem<4> &sm) { return sm.bt; }
-__device__ __forceinline__ int *page_list(AttnSmem<5> &) { return nullptr; }   // contiguous only
+__device__ __forceinline__ unsigned long long *page_list(AttnSmem<4> &sm) { return sm.pb; }
+__device__ __forceinline__ unsigned long long *page_list(AttnSmem<5> &) { return nullptr; }   // contiguous only
 // where the draft V rows land (key-major) before the transpose into V^T
 __device__ __forceinline__ u32x4a *draft_rows(AttnSmem<4> &sm, AttnBuf &) { return sm.dv; }
 __device__ __forceinline__ u32x4a *draft_rows(AttnSmem<5> &, AttnBuf &B) { return B.Vt; }
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
     constexpr int kLw = 2 * kPer;                       // loads per loading wave per item
     constexpr int kRW = kNW / kKS;                 // row waves
     __shared__ AttnSmem<kRing> sm;
-    int *const bt = page_list(sm);
+    unsigned long long *const pb = page_list(sm);
     const int tid = threadIdx.x, NT = kNW * 64, lane = tid & 63, wv = tid >> 6;
     constexpr int kThreads = kNW * 64 * (kProd ? 2 : 1);
     // kLoadProducers: waves kNW.. only issue the tile loads (producers), so
@@ -234,13 +237,11 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
 
     auto k_src = [&](int key, int J) -> const uint16_t * {
         if (!paged) return kslab + (size_t)key * kHD + J * 8;
-        const int blk = bt[key / bs - page0];
-        return kc + (((size_t)blk * a.Hkv + kvh) * bs + key % bs) * kHD + J * 8;
+        return kc + pb[key / bs - page0] + (key % bs) * kHD + J * 8;
     };
     auto v_src = [&](int e, int key) -> const uint16_t * {
         if (!paged) return vslab + (size_t)e * a.cap + key;
-        const int blk = bt[key / bs - page0];
-        return vc + (((size_t)blk * a.Hkv + kvh) * kHD + e) * bs + key % bs;
+        return vc + pb[key / bs - page0] + e * bs + key % bs;
     };
     const size_t drow = (size_t)b * m_max;               // draft rows of this sequence
     // pages of 8, 16, 32 or 64 keys tile a 64-key tile exactly (power-of-two
@@ -249,6 +250,27 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
     const int bshift = paged ? __builtin_ctz(bs) : 0;
     const size_t pstride = (size_t)a.Hkv * bs * kHD;     // elements per page (K and V^T alike)
     const size_t kvh_off = (size_t)kvh * bs * kHD;
+    // Per-lane parts of a full tile's addresses, the same for every tile (in
+    // elements): the K row chunk and the V^T chunk of each load slot, within
+    // the tile (contiguous cache) or within their page, with the page's slot
+    // in the tile (paged cache; one K load covers 4 keys of one page).
+    int kofs[kPer], vofs[kPer], kpg[kPer], vpg[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int it = lw * kPer + q, slot = it * 64 + lane;
+        const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
+        const int ko = swap23(r), kj = (P ^ (r & 15)) << 3, vj = (Q ^ ((e >> 1) & 7)) << 3;
+        if (!paged) {
+            kofs[q] = ko * kHD + kj;
+            vofs[q] = e * a.cap + vj;           // below 2^31: capacity <= 2^24
+            kpg[q] = vpg[q] = 0;
+        } else {
+            kofs[q] = (ko & (bs - 1)) * kHD + kj;
+            vofs[q] = e * bs + (vj & (bs - 1));
+            kpg[q] = ko >> bshift;
+            vpg[q] = vj >> bshift;
+        }
+    }
     auto issue = [&](int item) {
         AttnBuf &B = sm.buf[item % kRing];
         if (item >= nprefix) {
@@ -267,28 +289,23 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
                 const uint16_t *kt = kslab + (size_t)k0 * kHD, *vt = vslab + k0;
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    const int it = lw * kPer + q, slot = it * 64 + lane;
-                    const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
-                    load_lds16(kt + (swap23(r) * kHD + ((P ^ (r & 15)) << 3)), &B.K[it * 64]);
-                    load_lds16(vt + (e * a.cap + ((Q ^ ((e >> 1) & 7)) << 3)), &B.Vt[it * 64]);
+                    const int it = lw * kPer + q;
+                    load_lds16(kt + kofs[q], &B.K[it * 64]);
+                    load_lds16(vt + vofs[q], &B.Vt[it * 64]);
                 }
             } else {
-                const int tp = (k0 >> bshift) - page0;
-                int pk[kPer], pv[kPer];
+                const unsigned long long *pt = pb + ((k0 >> bshift) - page0);
+                unsigned long long pk[kPer], pv[kPer];
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    const int it = lw * kPer + q, slot = it * 64 + lane;
-                    pk[q] = bt[tp + (swap23(slot >> 4) >> bshift)];
-                    pv[q] = bt[tp + ((((slot & 7) ^ ((slot >> 4) & 7)) << 3) >> bshift)];
+                    pk[q] = pt[kpg[q]];
+                    pv[q] = pt[vpg[q]];
                 }
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    const int it = lw * kPer + q, slot = it * 64 + lane;
-                    const int r = slot >> 4, P = slot & 15, e = slot >> 3, Q = slot & 7;
-                    const int ko = swap23(r), vj = (Q ^ ((e >> 1) & 7)) << 3;
-                    load_lds16(kc + (size_t)pk[q] * pstride + kvh_off + (((ko & (bs - 1)) * kHD) + ((P ^ (r & 15)) << 3)),
-                               &B.K[it * 64]);
-                    load_lds16(vc + (size_t)pv[q] * pstride + kvh_off + (e * bs + (vj & (bs - 1))), &B.Vt[it * 64]);
+                    const int it = lw * kPer + q;
+                    load_lds16(kc + pk[q] + kofs[q], &B.K[it * 64]);
+                    load_lds16(vc + pv[q] + vofs[q], &B.Vt[it * 64]);
                 }
             }
         } else {
@@ -352,7 +369,8 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
         page0 = key_lo / bs;
         if (key_hi > key_lo) {
             const int np = (key_hi - 1) / bs - page0 + 1;
-            for (int i = tid; i < np; i += kThreads) bt[i] = a.block_table[(size_t)b * a.max_blocks + page0 + i];
+            for (int i = tid; i < np; i += kThreads)
+                pb[i] = (unsigned long long)a.block_table[(size_t)b * a.max_blocks + page0 + i] * pstride + kvh_off;
         }
         __syncthreads();   // page list visible
     }
