@@ -127,6 +127,7 @@ struct AttnPlan {
     int chunk;          // keys per split
     int nsplit;         // splits per (sequence, kv head)
     int max_prefix;     // cache capacity: every prefix_len is clamped to it
+    int sched;          // 1: blocks follow the longest-first table at off_cnt (k_attn_schedule)
     size_t off_part, off_ml, off_cnt, total;
 };
 AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch);

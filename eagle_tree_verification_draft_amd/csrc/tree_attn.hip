@@ -15,6 +15,8 @@
 // The draft tokens form one extra tile (at most 64 keys) masked by the
 // ancestor bits.  With several key splits, each writes an unnormalised
 // partial (O, max, sum) and a second kernel merges them.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -34,8 +36,9 @@ struct AttnArgs {
     void *out;
     float *part_o;
     float2 *part_ml;
+    int2 *sched_tab;   // sched != 0: (sequence, split) of each block group, or (-1, -1)
     uint32_t *err;
-    int Hq, Hkv, G, d, m_max, block_size, max_blocks, cap, chunk, nsplit, RG, rows_pg, units0;
+    int Hq, Hkv, G, d, m_max, block_size, max_blocks, cap, chunk, nsplit, RG, rows_pg, units0, sched;
     float scale_log2;
 };
 
@@ -65,7 +68,7 @@ __device__ __forceinline__ const T *v_elem(const AttnArgs &a, int b, int kvh, in
 }
 
 constexpr int kTileChunks = kTK * kHD * 2 / 16;   // 16-byte chunks per K (or V^T) tile: 1024
-constexpr int kMaxPages = 4096 / 8 + 2;             // pages of one split (chunk <= 4096, page >= 8)
+constexpr int kMaxPages = 4096 / 8 + 2;             // pages of one split (at most 513 pages of keys, + 1 unaligned)
 
 typedef unsigned int u32x4a __attribute__((ext_vector_type(4)));
 
@@ -200,13 +203,28 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
     const int lw = kProd ? wv - kNW : wv;               // loader wave index
     const int ln = lane & 31, hh = lane >> 5;
     const int rw = wv % kRW, kh = wv / kRW;        // row wave, key half (kKS = 2)
-    // block -> (split, row group, sequence/kv head); all splits and row groups
-    // of one (sequence, kv head) share blockIdx mod 8 when units0 % 8 == 0,
-    // which keeps them on one XCD and its L2
+    // block -> (split, row group, sequence/kv head).  In split-major order
+    // all splits and row groups of one (sequence, kv head) share blockIdx
+    // mod 8 when units0 % 8 == 0, which keeps them on one XCD and its L2.
+    // With a schedule table, consecutive groups of Hkv * RG blocks take one
+    // (sequence, split) each, in the table's order (the kv heads and row
+    // groups of a group keep their blockIdx mod 8 from split to split when
+    // Hkv * RG % 8 == 0); a group without an entry has nothing to do.
     const int x = blockIdx.x;
-    const int u0 = x % a.units0;
-    const int rest = x / a.units0;
-    const int rg = rest % a.RG, s = rest / a.RG;
+    int u0, rg, s;
+    if (a.sched) {
+        const int g = a.Hkv * a.RG, qg = x / g, wi = x - qg * g;
+        const int2 e = a.sched_tab[qg];
+        if (e.x < 0) return;                            // nothing requested yet
+        u0 = e.x * a.Hkv + wi / a.RG;
+        rg = wi % a.RG;
+        s = e.y;
+    } else {
+        u0 = x % a.units0;
+        const int rest = x / a.units0;
+        rg = rest % a.RG;
+        s = rest / a.RG;
+    }
     const int b = u0 / a.Hkv, kvh = u0 % a.Hkv;
     const int G = a.G, m_max = a.m_max;
 
@@ -677,6 +695,50 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
 }
 
 // ---------------------------------------------------------------------------
+// Dispatch order of the key splits (one workgroup, before the main kernel):
+// workgroups start in blockIdx order as compute units free up, so the order
+// decides how well the last round fills the chip.  Split-major order ends
+// with the late splits of the longest sequences; this order is the longest-
+// first rule in two parts, which is exact here because every split but a
+// sequence's last covers a full chunk:
+//   1. every split but the last of every sequence (full chunks), sequence by
+//      sequence;
+//   2. the last split of every sequence, by its prefix tiles, most first
+//      (ties: lower sequence first).
+// Entry q holds (sequence, split) for blocks q * Hkv * RG .. + Hkv * RG - 1;
+// entries past the last item hold (-1, -1).
+// ---------------------------------------------------------------------------
+constexpr int kSchedMaxBatch = 1024;
+
+__global__ __launch_bounds__(1024) void k_attn_schedule(AttnArgs a)
+{
+    __shared__ int s_ns[kSchedMaxBatch], s_lt[kSchedMaxBatch];
+    const int B = a.units0 / a.Hkv, ct = a.chunk / kTK, tid = threadIdx.x, NT = blockDim.x;
+    for (int b = tid; b < B; b += NT) {
+        int L = a.prefix_len[b];
+        L = L < 0 ? 0 : (L > a.cap ? a.cap : L);       // as the main kernel clamps it
+        const int ns = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+        s_ns[b] = ns;
+        s_lt[b] = (L + kTK - 1) / kTK - (ns - 1) * ct;  // prefix tiles of the last split
+    }
+    __syncthreads();
+    int n1 = 0;                                         // full-chunk splits in all
+    for (int c = 0; c < B; ++c) n1 += s_ns[c] - 1;
+    for (int b = tid; b < B; b += NT) {
+        const int lt = s_lt[b], ns = s_ns[b];
+        int before = 0, rank = 0;
+        for (int c = 0; c < B; ++c) {
+            const int l2 = s_lt[c];
+            before += c < b ? s_ns[c] - 1 : 0;
+            rank += (l2 > lt || (l2 == lt && c < b)) ? 1 : 0;
+        }
+        for (int j = 0; j < ns - 1; ++j) a.sched_tab[before + j] = make_int2(b, j);
+        a.sched_tab[n1 + rank] = make_int2(b, ns - 1);
+    }
+    for (int q = n1 + B + tid; q < B * a.nsplit; q += NT) a.sched_tab[q] = make_int2(-1, -1);
+}
+
+// ---------------------------------------------------------------------------
 // Merge of the key splits (launched right after the main kernel on the same
 // stream, so the kernel boundary makes every partial visible): for each row,
 // O = sum_s w_s O_s with w_s = exp2(m_s - M) / sum_s exp2(m_s - M) l_s.
@@ -958,7 +1020,7 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
         P.max_prefix = a->max_prefix;
     }
     if (a->dtype == EAGLE_F32) {
-        P.row_groups = 1; P.waves = 1; P.chunk = 0; P.nsplit = 1;
+        P.row_groups = 1; P.waves = 1; P.chunk = 0; P.nsplit = 1; P.sched = 0;
         P.off_part = P.off_ml = P.off_cnt = kWsHeader;
         P.total = kWsHeader;
         return P;
@@ -971,11 +1033,14 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
     const int units = batch * a->num_kv_heads * P.row_groups;
     // Key splits: one workgroup per CU (the LDS ring fills most of it), so a
     // launch runs in rounds of kCUs workgroups.  Pick the split count that
-    // minimises rounds x tiles per split (ties: fewer splits), with at most 64
-    // tiles (4096 keys) and, when the prefix allows, at least 4 tiles per split.
+    // minimises rounds x tiles per split (ties: fewer splits), with at most
+    // 128 tiles (8192 keys; a paged split's page list must fit its LDS
+    // array) and, when the prefix allows, at least 4 tiles per split.
     constexpr long long kCUs = 256;
     const int tiles = P.max_prefix > 0 ? (P.max_prefix + kTK - 1) / kTK : 1;
-    const int ns_lo = (tiles + 63) / 64;
+    int max_per = 128;
+    if (a->block_size > 0) max_per = std::min(max_per, (kMaxPages - 1) * a->block_size / kTK);
+    const int ns_lo = (tiles + max_per - 1) / max_per;
     const int ns_hi = tiles >= 4 * ns_lo ? tiles / 4 : ns_lo;
     int best = ns_lo;
     long long best_cost = -1;
@@ -988,11 +1053,15 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
     const int per = (tiles + best - 1) / best;
     P.chunk = per * kTK;
     P.nsplit = (tiles + per - 1) / per;
+    // Longest-first dispatch (k_attn_schedule) when the launch takes more
+    // than one round of long workgroups: with prefixes of different lengths
+    // the split-major order leaves CUs idle in the last round.
+    P.sched = (per >= 32 && (long long)units * P.nsplit > kCUs && batch <= kSchedMaxBatch) ? 1 : 0;
     const size_t rows_alloc = (size_t)units * P.nsplit * (size_t)(32 * ((rows_pg + 31) / 32));
     size_t o = kWsHeader;
     P.off_part = o; o = align_up(o + (P.nsplit > 1 ? rows_alloc * kHD * sizeof(float) : 0), 256);
     P.off_ml = o;   o = align_up(o + (P.nsplit > 1 ? rows_alloc * sizeof(float2) : 0), 256);
-    P.off_cnt = o;
+    P.off_cnt = o;  o = align_up(o + (P.sched ? (size_t)batch * P.nsplit * sizeof(int2) : 0), 256);
     P.total = o;
     return P;
 }
@@ -1011,6 +1080,8 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     a.out = out;
     a.part_o = reinterpret_cast<float *>(base + P.off_part);
     a.part_ml = reinterpret_cast<float2 *>(base + P.off_ml);
+    a.sched_tab = reinterpret_cast<int2 *>(base + P.off_cnt);
+    a.sched = P.sched;
     a.err = reinterpret_cast<uint32_t *>(base);
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = P.G; a.d = p->head_dim;
     a.m_max = p->m_max; a.block_size = p->block_size; a.max_blocks = p->max_blocks;
@@ -1036,6 +1107,11 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
     } else {
         const dim3 g((unsigned)(a.units0 * P.row_groups * P.nsplit));
         const bool contiguous = p->block_size == 0;
+        if (P.sched) {
+            hipLaunchKernelGGL(k_attn_schedule, dim3(1), dim3(1024), 0, st, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         if (P.waves == 4 && a.rows_pg <= 64) {
             if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16<4, 2, kLoadProducers, 5>), g, dim3(512), 0, st, a);
             else hipLaunchKernelGGL((k_tree_attn_bf16<4, 2, kLoadProducers, 4>), g, dim3(512), 0, st, a);

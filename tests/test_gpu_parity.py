@@ -146,6 +146,10 @@ SMALL = {
                                                kinds=[0, 1, 0, 1]),
     # GQA with two row groups (rows = 48 * 8 = 384)
     "bf16-gqa8-rowgroups": lambda: _small(4, batch=2, prefix=700, vocab=3000),
+    # paged serving shape with enough long workgroups for the longest-first
+    # dispatch table (more than one round of splits of at least 32 tiles)
+    "bf16-paged-longest-first": lambda: _small(5, batch=12, vocab=3000, prefix=(1000, 20000),
+                                               kinds=[0, 1] * 6, poison_tail=True),
     # paged, mixed trees and chains, ragged lengths, poisoned tails
     "bf16-paged-mixed": lambda: _small(5, batch=6, vocab=7001, prefix=(1, 5000),
                                        kinds=[0, 1, 0, 1, 1, 0]),
