@@ -207,17 +207,18 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
     // all splits and row groups of one (sequence, kv head) share blockIdx
     // mod 8 when units0 % 8 == 0, which keeps them on one XCD and its L2.
     // With a schedule table, consecutive groups of Hkv * RG blocks take one
-    // (sequence, split) each, in the table's order (the kv heads and row
-    // groups of a group keep their blockIdx mod 8 from split to split when
-    // Hkv * RG % 8 == 0); a group without an entry has nothing to do.
+    // (sequence, split) each, in the table's order, kv head fastest: when
+    // Hkv % 8 == 0 a (sequence, kv head) keeps blockIdx mod 8 = kv head mod 8
+    // from split to split, which is also the XCD of its merge blocks.  A
+    // group without an entry has nothing to do.
     const int x = blockIdx.x;
     int u0, rg, s;
     if (a.sched) {
         const int g = a.Hkv * a.RG, qg = x / g, wi = x - qg * g;
         const int2 e = a.sched_tab[qg];
         if (e.x < 0) return;                            // nothing requested yet
-        u0 = e.x * a.Hkv + wi / a.RG;
-        rg = wi % a.RG;
+        u0 = e.x * a.Hkv + wi % a.Hkv;
+        rg = wi / a.Hkv;
         s = e.y;
     } else {
         u0 = x % a.units0;
