@@ -184,14 +184,13 @@ __device__ __forceinline__ void wait_item(int later)
 constexpr int kLoadAll = 0, kLoadProducers = 1;
 
 template <int kNW, int kKS, int kLoad, int kRing>
-__global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void k_tree_attn_bf16(AttnArgs a)
+__device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing> &sm)
 {
     constexpr int kAhead = kRing - 1;                   // tiles in flight ahead of the one in use
     constexpr bool kProd = kLoad == kLoadProducers;
     constexpr int kPer = kTileChunks / 64 / kNW;        // 16-byte slots per loading wave per operand per tile
     constexpr int kLw = 2 * kPer;                       // loads per loading wave per item
     constexpr int kRW = kNW / kKS;                 // row waves
-    __shared__ AttnSmem<kRing> sm;
     unsigned long long *const pb = page_list(sm);
     const int tid = threadIdx.x, NT = kNW * 64, lane = tid & 63, wv = tid >> 6;
     constexpr int kThreads = kNW * 64 * (kProd ? 2 : 1);
@@ -695,6 +694,60 @@ __global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void 
     }
 }
 
+template <int kNW, int kKS, int kLoad, int kRing>
+__global__ __launch_bounds__(kNW * 64 * (kLoad == kLoadProducers ? 2 : 1)) void k_tree_attn_bf16(AttnArgs a)
+{
+    __shared__ AttnSmem<kRing> sm;
+    tree_attn_body<kNW, kKS, kLoad, kRing>(a, sm);
+}
+
+// One launch for batches that mix sequences with many and with few query
+// rows (trees and chains): a workgroup whose row group holds at most 64 rows
+// with a real node takes the 4-wave key-half form with 4 load waves (two
+// SIMDs compute every tile instead of one), the others the 8-wave form.  The
+// key-half form writes the first 64 rows of its row group; with a single
+// split the group's other rows (no real node) are zeroed here.
+template <int kRing>
+__global__ __launch_bounds__(512) void k_tree_attn_bf16_mixed(AttnArgs a)
+{
+    __shared__ AttnSmem<kRing> sm;
+    const int x = blockIdx.x;
+    int u0, rg, s;
+    if (a.sched) {
+        const int g = a.Hkv * a.RG, qg = x / g, wi = x - qg * g;
+        const int2 e = a.sched_tab[qg];
+        if (e.x < 0) return;
+        u0 = e.x * a.Hkv + wi % a.Hkv;
+        rg = wi / a.Hkv;
+        s = e.y;
+    } else {
+        u0 = x % a.units0;
+        const int rest = x / a.units0;
+        rg = rest % a.RG;
+        s = rest / a.RG;
+    }
+    const int b = u0 / a.Hkv, kvh = u0 % a.Hkv;
+    int n = a.num_nodes[b];
+    n = n < 0 ? 0 : (n > a.m_max ? a.m_max : n);
+    if (n * a.G - rg * a.rows_pg > 64) {
+        tree_attn_body<8, 1, kLoadAll, kRing>(a, sm);
+        return;
+    }
+    tree_attn_body<4, 2, kLoadProducers, kRing>(a, sm);
+    int L = a.prefix_len[b];
+    L = L < 0 ? 0 : (L > a.cap ? a.cap : L);
+    if (s != 0 || (L > 0 && (L + a.chunk - 1) / a.chunk > 1)) return;
+    // rows 64 .. rows_pg - 1 of the row group, 16 bytes per thread
+    uint4 *out = static_cast<uint4 *>(a.out);
+    const int per_row = kHD * 2 / 16;
+    for (int t = threadIdx.x; t < (a.rows_pg - 64) * per_row; t += blockDim.x) {
+        const int row = rg * a.rows_pg + 64 + t / per_row, node = row / a.G;
+        if (node >= a.m_max) continue;
+        const int h = kvh * a.G + row % a.G;
+        out[(((size_t)b * a.m_max + node) * a.Hq + h) * per_row + t % per_row] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Dispatch order of the key splits (one workgroup, before the main kernel):
 // workgroups start in blockIdx order as compute units free up, so the order
@@ -1120,8 +1173,8 @@ hipError_t launch_tree_attn(const eagle_attn_params *p, const AttnPlan &P, int32
             if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16<4, 1, kLoadAll, 5>), g, dim3(256), 0, st, a);
             else hipLaunchKernelGGL((k_tree_attn_bf16<4, 1, kLoadAll, 4>), g, dim3(256), 0, st, a);
         } else {
-            if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16<8, 1, kLoadAll, 5>), g, dim3(512), 0, st, a);
-            else hipLaunchKernelGGL((k_tree_attn_bf16<8, 1, kLoadAll, 4>), g, dim3(512), 0, st, a);
+            if (contiguous) hipLaunchKernelGGL((k_tree_attn_bf16_mixed<5>), g, dim3(512), 0, st, a);
+            else hipLaunchKernelGGL((k_tree_attn_bf16_mixed<4>), g, dim3(512), 0, st, a);
         }
         if (P.nsplit > 1) {
             const hipError_t e = hipGetLastError();
