@@ -757,8 +757,12 @@ __global__ __launch_bounds__(512) void k_tree_attn_bf16_mixed(AttnArgs a)
 // sequence's last covers a full chunk:
 //   1. every split but the last of every sequence (full chunks), sequence by
 //      sequence;
-//   2. the last split of every sequence, by its prefix tiles, most first
-//      (ties: lower sequence first).
+//   2. the last split of every sequence, longest first (ties: lower sequence
+//      first), weighing a tile by the form that computes it: with the mixed
+//      launch a tile of a sequence with at most 64 query rows (key-half
+//      form) costs about half one of the 8-wave form (1.5 against 2.8 us
+//      per CU on this chip), so a split weighs (prefix tiles + draft tile)
+//      x 10 or x 19.
 // Entry q holds (sequence, split) for blocks q * Hkv * RG .. + Hkv * RG - 1;
 // entries past the last item hold (-1, -1).
 // ---------------------------------------------------------------------------
@@ -771,9 +775,11 @@ __global__ __launch_bounds__(1024) void k_attn_schedule(AttnArgs a)
     for (int b = tid; b < B; b += NT) {
         int L = a.prefix_len[b];
         L = L < 0 ? 0 : (L > a.cap ? a.cap : L);       // as the main kernel clamps it
+        int n = a.num_nodes[b];
+        n = n < 0 ? 0 : (n > a.m_max ? a.m_max : n);
         const int ns = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
         s_ns[b] = ns;
-        s_lt[b] = (L + kTK - 1) / kTK - (ns - 1) * ct;  // prefix tiles of the last split
+        s_lt[b] = ((L + kTK - 1) / kTK - (ns - 1) * ct + (n > 0 ? 1 : 0)) * (n * a.G > 64 ? 19 : 10);
     }
     __syncthreads();
     int n1 = 0;                                         // full-chunk splits in all
