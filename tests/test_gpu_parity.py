@@ -150,6 +150,12 @@ SMALL = {
     # dispatch table (more than one round of splits of at least 32 tiles)
     "bf16-paged-longest-first": lambda: _small(5, batch=12, vocab=3000, prefix=(1000, 20000),
                                                kinds=[0, 1] * 6, poison_tail=True),
+    # two row groups (GQA 8, 384 rows) with the longest-first table and chains:
+    # a chain's first row group (56 rows) takes the key-half form and its
+    # second (no rows with a node) is zeroed; a tree's groups take the 8-wave form
+    "bf16-gqa8-rowgroups-sched-chains": lambda: _small(4, batch=6, vocab=3000, prefix=(3000, 20000),
+                                                       kinds=[0, 1] * 3, chain_k=7, block_size=16,
+                                                       poison_tail=True),
     # paged, mixed trees and chains, ragged lengths, poisoned tails
     "bf16-paged-mixed": lambda: _small(5, batch=6, vocab=7001, prefix=(1, 5000),
                                        kinds=[0, 1, 0, 1, 1, 0]),
