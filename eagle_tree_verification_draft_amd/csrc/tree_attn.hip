@@ -115,6 +115,22 @@ __device__ __forceinline__ int vpos(int e, int J) { return e * 8 + (J ^ ((e >> 1
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4a v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + the sum of the eight bf16 values of v (dot products with ones: the
+// sum of exactly the weights the PV product multiplies).  The pairs are taken
+// with vector shuffles: a bit cast of one 32-bit element of the vector to
+// bf16x2 was compiled as element 0 every time.
+__device__ __forceinline__ float add_bf16x8(bf16x8 v, float acc)
+{
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
+}
+
 // v combined with the value of lane ^ 32 through one lane-half swap (a VALU
 // instruction, no LDS round trip); the result is the same in both lanes
 __device__ __forceinline__ float max_xor32(float v)
@@ -407,10 +423,11 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-    // running max in raw score units and running sum; scores enter exp2 as
-    // fma(s, c, -m c) with c = scale * log2(e) > 0
+    // exponent reference in raw score units (finite: 0 until a tile moves it)
+    // and running sum; scores enter exp2 as fma(s, c, -m c) with
+    // c = scale * log2(e) > 0
     const float c2 = a.scale_log2;
-    float m_run = -__builtin_inff(), l_run = 0.0f;
+    float m_run = 0.0f, l_run = 0.0f;
 
     // the remaining first items (from the first one not requested as a
     // prefix tile: a sequence shorter than the capacity has its draft tile
@@ -564,39 +581,52 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
                         sacc[u][r] = kq < lim ? sacc[u][r] : -__builtin_inff();
                     }
             }
-            float tmax = -__builtin_inff();
+            // Weights against the current reference, and their row sum (of
+            // the bf16 weights themselves, as the PV product uses them)
+            bf16x8 pf[kNH][2];
+            auto weigh = [&]() -> float {
+                const float mc = m_run * c2;
 #pragma unroll
-            for (int u = 0; u < kNH; ++u)
+                for (int u = 0; u < kNH; ++u)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[u][r]);
-            tmax = max_xor32(tmax);
-            // Lazy rescaling: the exponent reference m_run moves (and O, l are
-            // rescaled) only when some row's max grew by more than 2^8 in exp2
-            // units; otherwise p = exp2((s - m_run) c) <= 2^8, which fp32 sums
-            // and bf16 products carry exactly as well, and O / l is unchanged.
-            const float m_new = fmaxf(m_run, tmax);
-            if (__any((m_new - m_run) * c2 > 8.0f)) {
-                const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-                const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+                    for (int r = 0; r < 16; ++r)
+                        pf[u][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][r], c2, -mc));
+                float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+                for (int u = 0; u < kNH; ++u) {
+                    s0 = add_bf16x8(pf[u][0], s0);
+                    s1 = add_bf16x8(pf[u][1], s1);
+                }
+                return sum_xor32(s0 + s1);
+            };
+            float lsum = weigh();
+            // Lazy rescaling: the reference m_run moves only when some weight
+            // exceeds 2^8 (then so does the row sum), or while nothing has
+            // been accumulated (reference 0 may lie far above every score,
+            // where all weights underflow).  Otherwise every weight is at
+            // most 2^8, which fp32 sums and bf16 products carry as well as
+            // weights below 1, and O / l is unchanged.  When it moves, it goes
+            // to the row max (only up once something is accumulated), O and l
+            // are rescaled and the weights formed again; the row max is not
+            // computed otherwise.
+            if (__any(!(lsum <= 256.0f) || l_run + lsum == 0.0f)) {
+                float tmax = -__builtin_inff();
+#pragma unroll
+                for (int u = 0; u < kNH; ++u)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[u][r]);
+                tmax = max_xor32(tmax);
+                const bool empty = l_run == 0.0f;
+                const float m_new = empty ? (tmax == -__builtin_inff() ? m_run : tmax) : fmaxf(m_run, tmax);
+                const float corr = empty ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
                 l_run *= corr;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
                 m_run = m_new;
+                lsum = weigh();
             }
-            const float mc = (m_run == -__builtin_inff() ? 0.0f : m_run) * c2;
-            float lsum = 0.0f;
-            bf16x8 pf[kNH][2];
-#pragma unroll
-            for (int u = 0; u < kNH; ++u)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][r], c2, -mc));
-                    lsum += p;
-                    pf[u][r >> 3][r & 7] = (__bf16)p;
-                }
-            lsum = sum_xor32(lsum);
             l_run += lsum;
             // ---- O^T += V^T P^T: four independent accumulators per k-step ----
             if constexpr (kEarly == kNV) {
@@ -641,10 +671,12 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
         __syncthreads();
         if (kh == 1) return;
         if (wave_active) {
+            // a half with nothing accumulated (every key masked) has no max
             const float2 o = xml[lane];
-            const float mn = fmaxf(m_run, o.x);
+            const float ma = l_run > 0.0f ? m_run : -__builtin_inff(), mb = o.y > 0.0f ? o.x : -__builtin_inff();
+            const float mn = fmaxf(ma, mb);
             const float mu = mn == -__builtin_inff() ? 0.0f : mn;
-            const float e0 = __builtin_amdgcn_exp2f((m_run - mu) * c2), e1 = __builtin_amdgcn_exp2f((o.x - mu) * c2);
+            const float e0 = __builtin_amdgcn_exp2f((ma - mu) * c2), e1 = __builtin_amdgcn_exp2f((mb - mu) * c2);
             l_run = l_run * e0 + o.y * e1;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
@@ -690,7 +722,8 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
                     make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
             }
         // partial max in log2 units (raw max times c), as the merge expects
-        if (hh == 0) a.part_ml[pbase + row_local] = make_float2(m_run * c2, l_run);
+        // (a row with nothing accumulated has no max: -inf, as the merge expects)
+        if (hh == 0) a.part_ml[pbase + row_local] = make_float2(l_run > 0.0f ? m_run * c2 : -__builtin_inff(), l_run);
     }
 }
 
