@@ -381,12 +381,15 @@ def bench_workload(n, args, extras, cpu_seconds):
                    "accept": "greedy" if w.accept_mode == synth.ACCEPT_GREEDY else f"sample T={w.temperature}",
                    "input_sets": nsets, "cold": True,
                    "launch": "graph" if graphs is not None else "eager"},
-        "roofline": {"kernel": "k_tree_attn_bf16" if w.dtype == torch.bfloat16 else "k_tree_attn_f32",
+        "roofline": {"kernel": ("k_tree_attn_f32" if w.dtype != torch.bfloat16 else
+                                "k_tree_attn_bf16_mixed" if w.m_max * (w.num_q_heads // w.num_kv_heads) > 128
+                                else "k_tree_attn_bf16"),
                      "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "traffic_source": traffic_src,
-                     "call": "eagle_tree_attn (k_tree_attn_* plus k_tree_attn_merge when the keys are split)",
+                     "call": "eagle_tree_attn (k_attn_schedule when the splits are ordered longest first, "
+                             "k_tree_attn_*, k_tree_attn_merge when the keys are split)",
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "avg_us": round(attn_avg_ms * 1e3, 2), "timed_calls": attn_calls,
                      "eager_event_us": round(attn_eager_ms * 1e3, 2),
