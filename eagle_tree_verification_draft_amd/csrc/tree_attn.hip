@@ -1128,13 +1128,15 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
     // launch runs in rounds of kCUs workgroups.  Pick the split count that
     // minimises rounds x tiles per split (ties: fewer splits), with at most
     // 128 tiles (8192 keys; a paged split's page list must fit its LDS
-    // array) and, when the prefix allows, at least 4 tiles per split.
+    // array) and, when the prefix allows, at least 6 tiles per split (a split
+    // costs a merge share and a workgroup's fixed cost: workload 2's call ran
+    // 18.2 us with 5 to 7 tiles per split, 20.1 us with 4).
     constexpr long long kCUs = 256;
     const int tiles = P.max_prefix > 0 ? (P.max_prefix + kTK - 1) / kTK : 1;
     int max_per = 128;
     if (a->block_size > 0) max_per = std::min(max_per, (kMaxPages - 1) * a->block_size / kTK);
     const int ns_lo = (tiles + max_per - 1) / max_per;
-    const int ns_hi = tiles >= 4 * ns_lo ? tiles / 4 : ns_lo;
+    const int ns_hi = tiles >= 6 * ns_lo ? tiles / 6 : ns_lo;
     int best = ns_lo;
     long long best_cost = -1;
     for (int ns = ns_lo; ns <= ns_hi; ++ns) {
