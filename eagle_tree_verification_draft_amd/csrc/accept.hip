@@ -537,28 +537,35 @@ __global__ __launch_bounds__(1024) void k_accept_reg(AcceptArgs a)
 // one workgroup per row; a second kernel walks each tree over those argmaxes.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(1024) void k_row_argmax(AcceptArgs a, int32_t *g)
+// One part of one row: the first maximum (value desc, id asc) of entries
+// [part * span, (part + 1) * span); span is a multiple of 8 entries, so every
+// part starts 16-byte aligned where the row does.  Rows past a sequence's
+// node count are skipped.
+__global__ __launch_bounds__(1024) void k_row_argmax(AcceptArgs a, int2 *g, int parts, int span)
 {
     __shared__ BlockScratch red;
     const int m1 = a.m_max + 1;
-    const int b = blockIdx.x / m1, u = blockIdx.x % m1;
+    const int r = blockIdx.x / parts, part = blockIdx.x - r * parts;
+    const int b = r / m1, u = r - b * m1;
     int n = a.num_nodes[b];
     n = n < 0 ? 0 : (n > a.m_max ? a.m_max : n);
     if (u > n) return;
-    const T *row = static_cast<const T *>(a.target) + ((size_t)b * m1 + u) * (size_t)a.row_stride;
+    const int lo = part * span, hi = min(a.vocab, lo + span);
+    const T *row = static_cast<const T *>(a.target) + ((size_t)b * m1 + u) * (size_t)a.row_stride + lo;
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
     bool nan = false;
-    for_each_elem<T>(row, a.vocab, a.vec_ok, [&](float f, int id) {
-        nan |= (f != f);
-        if (before(f, id, bv, bi)) { bv = f; bi = id; }
-    });
+    if (lo < hi)
+        for_each_elem<T>(row, hi - lo, a.vec_ok, [&](float f, int id) {
+            nan |= (f != f);
+            if (before(f, lo + id, bv, bi)) { bv = f; bi = lo + id; }
+        });
     if (__any(nan) && (threadIdx.x & 63) == 0) raise_error(a.err, EAGLE_DEVERR_NONFINITE_ROW);
     block_best(bv, bi, red);
-    if (threadIdx.x == 0) g[(size_t)b * m1 + u] = bi;
+    if (threadIdx.x == 0) g[(size_t)r * parts + part] = make_int2(__float_as_int(bv), bi);
 }
 
-__global__ __launch_bounds__(64) void k_greedy_walk(AcceptArgs a, const int32_t *g)
+__global__ __launch_bounds__(64) void k_greedy_walk(AcceptArgs a, const int2 *g, int parts)
 {
     // one wave per sequence; lane i holds node i (m_max <= 64), and the child
     // whose token matches the current argmax is found by a ballot
@@ -571,7 +578,17 @@ __global__ __launch_bounds__(64) void k_greedy_walk(AcceptArgs a, const int32_t 
     }
     const int tok = lane < n ? a.tokens[(size_t)b * m_max + lane] : -1;
     const int par = lane < n ? a.parent[(size_t)b * m_max + lane] : -2;
-    for (int u = lane; u <= n; u += 64) gs[u] = g[(size_t)b * (m_max + 1) + u];
+    // each row's argmax: the first of its parts' maxima in (value desc, id asc)
+    for (int u = lane; u <= n; u += 64) {
+        const int2 *pr = g + ((size_t)b * (m_max + 1) + u) * parts;
+        float bv = -__builtin_inff();
+        int bi = 0x7fffffff;
+        for (int q = 0; q < parts; ++q) {
+            const int2 e = pr[q];
+            if (before(__int_as_float(e.x), e.y, bv, bi)) { bv = __int_as_float(e.x); bi = e.y; }
+        }
+        gs[u] = bi;
+    }
     __syncthreads();
     int32_t *acc = a.accepted + (size_t)b * a.max_accept;
     int cur = -1, len = 0, bonus = -1;
@@ -598,11 +615,16 @@ __global__ __launch_bounds__(64) void k_greedy_walk(AcceptArgs a, const int32_t 
 // rows below which greedy acceptance reads every row in parallel
 constexpr int kParallelGreedyRows = 512;
 
+// parts per row of the parallel greedy argmax: at least 4096 entries each,
+// at most 8 (each part is one workgroup; a row of 32000 bf16 entries takes 7)
+static int argmax_parts(int vocab) { return vocab / 4096 < 1 ? 1 : (vocab / 4096 > 8 ? 8 : vocab / 4096); }
+static int argmax_span(int vocab, int parts) { return ((vocab + parts - 1) / parts + 7) / 8 * 8; }
+
 size_t accept_layout_bytes(const eagle_accept_params *p, int32_t batch)
 {
     size_t o = kWsHeader;
     if (p && p->mode == EAGLE_ACCEPT_GREEDY && (size_t)batch * (p->m_max + 1) <= (size_t)kParallelGreedyRows)
-        o = align_up(o + (size_t)batch * (p->m_max + 1) * sizeof(int32_t), 256);
+        o = align_up(o + (size_t)batch * (p->m_max + 1) * argmax_parts(p->vocab) * sizeof(int2), 256);
     return o;
 }
 
@@ -634,17 +656,18 @@ hipError_t launch_accept(const eagle_accept_params *p, int32_t batch, const void
     a.err = err;
     const int vec = dt == EAGLE_F32 ? 4 : 8;
     if (p->mode == EAGLE_ACCEPT_GREEDY && (size_t)batch * (p->m_max + 1) <= (size_t)kParallelGreedyRows) {
-        int nt = (p->vocab / vec + 63) / 64 * 64;
+        const int parts = argmax_parts(p->vocab), span = argmax_span(p->vocab, parts);
+        int nt = (span / vec + 63) / 64 * 64;
         nt = nt < 64 ? 64 : (nt > kAcceptThreads ? kAcceptThreads : nt);
-        int32_t *g = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(err) + kWsHeader);
-        const dim3 grid((unsigned)(batch * (p->m_max + 1)));
+        int2 *g = reinterpret_cast<int2 *>(reinterpret_cast<char *>(err) + kWsHeader);
+        const dim3 grid((unsigned)(batch * (p->m_max + 1) * parts));
         if (dt == EAGLE_F32)
-            hipLaunchKernelGGL(k_row_argmax<float>, grid, dim3(nt), 0, st, a, g);
+            hipLaunchKernelGGL(k_row_argmax<float>, grid, dim3(nt), 0, st, a, g, parts, span);
         else
-            hipLaunchKernelGGL(k_row_argmax<uint16_t>, grid, dim3(nt), 0, st, a, g);
+            hipLaunchKernelGGL(k_row_argmax<uint16_t>, grid, dim3(nt), 0, st, a, g, parts, span);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_greedy_walk, dim3(batch), dim3(64), 0, st, a, (const int32_t *)g);
+        hipLaunchKernelGGL(k_greedy_walk, dim3(batch), dim3(64), 0, st, a, (const int2 *)g, parts);
         return hipGetLastError();
     }
     // register-resident walk: kNV vectors per thread, the fewest threads that hold the row
