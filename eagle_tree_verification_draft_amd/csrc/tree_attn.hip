@@ -516,7 +516,118 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
         }
         if (!kProd && item + kAhead < nitems) issue(item + kAhead);
 
-        if (wave_active) {
+        if (kNW == 8 && kRing == 5 && wave_active) {
+            // Two compute waves per SIMD, contiguous cache: the tile goes by
+            // key halves h = 0, 1 (keys 32h..32h+31), software-pipelined so
+            // that the products of one half are interleaved with the softmax
+            // of the other:
+            //   QK(0); QK(1) with weights(0); PV(0) with weights(1); PV(1).
+            // A half's weights are formed against the reference in force
+            // when they are formed (the lazy rule below, per half); a
+            // reference moved by half 1 applies to O as it stands after
+            // PV(0), whose weights were formed against the old one.  (The
+            // paged form keeps the plain order: its page bookkeeping leaves
+            // too few registers for the pipelined one, which spilled.)
+            f32x16 sh[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sh[h][r] = 0.0f;
+            u32x4a kb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(ln, 2 * j + hh)];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sh[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[0], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(32 + ln, 2 * j + hh)];
+            // sh[h][8t + q] is the raw score of tile key 32h + 16t + 8hh + q for
+            // row my_row; masking as in the other forms
+            auto mask_half = [&](int h) {
+                if (draft) {
+                    const uint32_t mk = (uint32_t)(my_anc >> (32 * h)) >> (8 * hh);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int bit = 16 * (r >> 3) + (r & 7);
+                        sh[h][r] = ((mk >> bit) & 1u) ? sh[h][r] : -__builtin_inff();
+                    }
+                } else if (k0 + kTK > key_hi) {
+                    const int lim = key_hi - k0 - 8 * hh;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kq = 32 * h + 16 * (r >> 3) + (r & 7);
+                        sh[h][r] = kq < lim ? sh[h][r] : -__builtin_inff();
+                    }
+                }
+            };
+            bf16x8 ph[2][2];
+            // half h's weights against the current reference; returns their row sum
+            auto weigh_half = [&](int h) -> float {
+                const float mc = m_run * c2;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    ph[h][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sh[h][r], c2, -mc));
+                return sum_xor32(add_bf16x8(ph[h][0], 0.0f) + add_bf16x8(ph[h][1], 0.0f));
+            };
+            // the lazy rule of the other forms, for one half
+            auto settle_half = [&](int h, float lsum) {
+                if (__any(!(lsum <= 256.0f) || l_run + lsum == 0.0f)) {
+                    float tmax = -__builtin_inff();
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sh[h][r]);
+                    tmax = max_xor32(tmax);
+                    const bool empty = l_run == 0.0f;
+                    const float m_new = empty ? (tmax == -__builtin_inff() ? m_run : tmax) : fmaxf(m_run, tmax);
+                    const float corr = empty ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+                    l_run *= corr;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
+                    m_run = m_new;
+                    lsum = weigh_half(h);
+                }
+                l_run += lsum;
+            };
+            mask_half(0);
+            // ---- QK(1) with weights(0) ----
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sh[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[1], 0, 0, 0);
+            float ls = weigh_half(0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            settle_half(0, ls);
+            // V^T operands of half 0 (keys 0..31: chunks 2t + hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 2 * (j >> 2) + hh)];
+            mask_half(1);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- PV(0) with weights(1) ----
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[0][j >> 2], oacc[j & 3], 0, 0, 0);
+            ls = weigh_half(1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            settle_half(1, ls);
+            // ---- PV(1) ----
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 4 + 2 * (j >> 2) + hh)];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[1][j >> 2], oacc[j & 3], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if (wave_active) {
             // ---- S^T = K Q^T: two independent 32-key accumulators ----
             // the K operands are read from LDS ahead of the products (all of
             // them with 4 waves; in two halves with 8 waves, two per SIMD,
@@ -815,11 +926,15 @@ __global__ __launch_bounds__(1024) void k_attn_schedule(AttnArgs a)
         s_lt[b] = ((L + kTK - 1) / kTK - (ns - 1) * ct + (n > 0 ? 1 : 0)) * (n * a.G > 64 ? 19 : 10);
     }
     __syncthreads();
+    // (the loops over the batch are unrolled so that their LDS reads go out
+    // in groups instead of one round trip per sequence)
     int n1 = 0;                                         // full-chunk splits in all
+#pragma unroll 16
     for (int c = 0; c < B; ++c) n1 += s_ns[c] - 1;
     for (int b = tid; b < B; b += NT) {
         const int lt = s_lt[b], ns = s_ns[b];
         int before = 0, rank = 0;
+#pragma unroll 16
         for (int c = 0; c < B; ++c) {
             const int l2 = s_lt[c];
             before += c < b ? s_ns[c] - 1 : 0;
