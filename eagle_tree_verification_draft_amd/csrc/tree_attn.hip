@@ -115,6 +115,14 @@ __device__ __forceinline__ int vpos(int e, int J) { return e * 8 + (J ^ ((e >> 1
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4a v) { return __builtin_bit_cast(bf16x8, v); }
 
+// a value the optimiser must treat as new at this point (keeps expressions
+// built from it from being hoisted out of loops and held in registers)
+__device__ __forceinline__ int opaque_i(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // acc + the sum of the eight bf16 values of v (dot products with ones: the
@@ -288,7 +296,9 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
     // elements): the K row chunk and the V^T chunk of each load slot, within
     // the tile (contiguous cache) or within their page, with the page's slot
     // in the tile (paged cache; one K load covers 4 keys of one page).
-    int kofs[kPer], vofs[kPer], kpg[kPer], vpg[kPer];
+    // (paged: the page slot sits in bits 16.. above the offset, which is
+    // below 2^13 for pages of at most 64 keys: one register per operand)
+    int kofs[kPer], vofs[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int it = lw * kPer + q, slot = it * 64 + lane;
@@ -297,12 +307,9 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
         if (!paged) {
             kofs[q] = ko * kHD + kj;
             vofs[q] = e * a.cap + vj;           // below 2^31: capacity <= 2^24
-            kpg[q] = vpg[q] = 0;
         } else {
-            kofs[q] = (ko & (bs - 1)) * kHD + kj;
-            vofs[q] = e * bs + (vj & (bs - 1));
-            kpg[q] = ko >> bshift;
-            vpg[q] = vj >> bshift;
+            kofs[q] = ((ko & (bs - 1)) * kHD + kj) | ((ko >> bshift) << 16);
+            vofs[q] = (e * bs + (vj & (bs - 1))) | ((vj >> bshift) << 16);
         }
     }
     auto issue = [&](int item) {
@@ -332,14 +339,15 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
                 unsigned long long pk[kPer], pv[kPer];
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
-                    pk[q] = pt[kpg[q]];
-                    pv[q] = pt[vpg[q]];
+                    pk[q] = pt[kofs[q] >> 16];
+                    pv[q] = pt[vofs[q] >> 16];
                 }
 #pragma unroll
                 for (int q = 0; q < kPer; ++q) {
                     const int it = lw * kPer + q;
-                    load_lds16(kc + pk[q] + kofs[q], &B.K[it * 64]);
-                    load_lds16(vc + pv[q] + vofs[q], &B.Vt[it * 64]);
+                    // (offsets re-read each tile: hoisted 64-bit bases cost registers)
+                    load_lds16(kc + pk[q] + (opaque_i(kofs[q]) & 0xffff), &B.K[it * 64]);
+                    load_lds16(vc + pv[q] + (opaque_i(vofs[q]) & 0xffff), &B.Vt[it * 64]);
                 }
             }
         } else {
@@ -516,18 +524,15 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
         }
         if (!kProd && item + kAhead < nitems) issue(item + kAhead);
 
-        if (kNW == 8 && kRing == 5 && wave_active) {
-            // Two compute waves per SIMD, contiguous cache: the tile goes by
-            // key halves h = 0, 1 (keys 32h..32h+31), software-pipelined so
-            // that the products of one half are interleaved with the softmax
-            // of the other:
+        if (kNW == 8 && wave_active) {
+            // Two compute waves per SIMD: the tile goes by key halves h = 0, 1
+            // (keys 32h..32h+31), software-pipelined so that the products of
+            // one half are interleaved with the softmax of the other:
             //   QK(0); QK(1) with weights(0); PV(0) with weights(1); PV(1).
             // A half's weights are formed against the reference in force
             // when they are formed (the lazy rule below, per half); a
             // reference moved by half 1 applies to O as it stands after
-            // PV(0), whose weights were formed against the old one.  (The
-            // paged form keeps the plain order: its page bookkeeping leaves
-            // too few registers for the pipelined one, which spilled.)
+            // PV(0), whose weights were formed against the old one.
             f32x16 sh[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
