@@ -18,8 +18,9 @@ namespace eagle {
 //   - k_row_stats (few rows, where latency matters): the row is read once with
 //     16-byte coalesced loads and kept in registers across up to 1024 threads;
 //   - k_row_stats_stream (many rows or long rows): a streaming max pass, then a
-//     streaming weight pass over the same lines (second read from L2), with
-//     few registers, so two workgroups share a compute unit and overlap.
+//     streaming weight pass over the same lines (second read from the caches,
+//     non-temporal), with few registers, so two workgroups share a compute
+//     unit and overlap.
 //
 // Candidates: every element >= T, with T such that at least C elements are
 // >= T: with at least C waves, the C-th largest wave maximum (C waves hold
@@ -241,12 +242,15 @@ __global__ __launch_bounds__(1024) void k_row_stats_stream(RowStatsArgs a)
 
     const bool use_list = thr != -__builtin_inff();
     double wsum = 0.0;
+    // the weight pass is the lines' last use: non-temporal reads (the max
+    // pass reads them with the default policy, so they are still cached)
     for (int v0 = tid; v0 < nvec; v0 += 4 * NT) {
         uint4 x[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int v = v0 + u * NT;
-            x[u] = v < nvec ? load_vec<T>(row, v * VEC, V, a.vec_ok) : make_uint4(0u, 0u, 0u, 0u);   // (skipped below)
+            x[u] = v >= nvec ? make_uint4(0u, 0u, 0u, 0u)   // (skipped below)
+                 : (a.vec_ok && v * VEC + VEC <= V) ? ld16_stream(row + v * VEC) : load_vec<T>(row, v * VEC, V, a.vec_ok);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
