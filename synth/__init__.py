@@ -291,6 +291,46 @@ def plant_draft_keys(attn: AttnInputs, w: Workload, seed: int, gamma: float = 1.
     return dataclasses.replace(attn, q=q, k_draft=kd)
 
 
+def rising_prefix_keys(attn: AttnInputs, w: Workload, seed: int, top: float = 6.0) -> AttnInputs:
+    """A copy of `attn` whose prefix scores rise along the prefix, so that an
+    online softmax meets a new maximum again and again, also between the two
+    halves of one 64-key tile.
+
+    Per (sequence b, kv head) one direction u is drawn, N(0, 1)^d rescaled to
+    |u|^2 = d; every query head of that kv head becomes u + q / 2 and the
+    prefix key at position p (of L_b) becomes top * (p / L_b) * u + k / 2.  At
+    scale 1/sqrt(d) a query then scores key p near top * sqrt(d) * p / L_b (up
+    to about 68 at d = 128): the scores climb by tens of natural-log units
+    over the prefix.  Values are combined in fp32 and rounded (RNE) to the
+    workload dtype; positions past L_b keep whatever they held.
+    """
+    B, Hkv, d = w.batch, w.num_kv_heads, w.head_dim
+    G = w.num_q_heads // Hkv
+    dev = attn.q.device
+    g = _gen(seed, "plant", "cpu")
+    u = torch.randn((B, Hkv, d), generator=g, dtype=torch.float32)
+    u = (u * (math.sqrt(d) / u.norm(dim=-1, keepdim=True))).to(dev)
+    uq = u.repeat_interleave(G, dim=1)                               # [B][Hq][d]
+    q = (0.5 * attn.q.to(torch.float32) + uq[:, None]).to(w.dtype)
+    kc = attn.k_cache.clone()
+    plen = attn.prefix_len.cpu().tolist()
+    for b in range(B):
+        L = int(plen[b])
+        if L <= 0:
+            continue
+        coef = (top * torch.arange(L, dtype=torch.float32, device=dev) / L)     # [L]
+        add = coef[None, :, None] * u[b][:, None, :]                          # [Hkv][L][d]
+        if attn.block_size == 0:
+            kc[b, :, :L] = (0.5 * kc[b, :, :L].to(torch.float32) + add).to(w.dtype)
+        else:
+            bs = attn.block_size
+            for i in range((L + bs - 1) // bs):
+                blk = int(attn.block_table[b, i])
+                n = min(bs, L - i * bs)
+                kc[blk, :, :n] = (0.5 * kc[blk, :, :n].to(torch.float32) + add[:, i * bs:i * bs + n]).to(w.dtype)
+    return dataclasses.replace(attn, q=q, k_cache=kc)
+
+
 def rand_words(w: Workload, seed: int, device="cpu") -> torch.Tensor:
     """[B][m_max+1] uniform 32-bit words, held as int32 bit patterns."""
     g = _gen(seed, "words", "cpu")

@@ -146,6 +146,12 @@ SMALL = {
                                                kinds=[0, 1, 0, 1]),
     # GQA with two row groups (rows = 48 * 8 = 384)
     "bf16-gqa8-rowgroups": lambda: _small(4, batch=2, prefix=700, vocab=3000),
+    # prefix scores that climb along the prefix: the softmax reference moves
+    # again and again, also between the key halves of one tile (the 8-wave
+    # form's per-half rule, contiguous and paged; the key-half form)
+    "bf16-gqa8-rising": lambda: _small(4, batch=2, prefix=(700, 2100), vocab=3000),
+    "bf16-paged-rising": lambda: _small(5, batch=4, vocab=3000, prefix=(300, 2500)),
+    "bf16-keyhalf-rising": lambda: _small(2, batch=2, num_q_heads=8, num_kv_heads=8, prefix=(500, 1500), vocab=3000),
     # paged serving shape with enough long workgroups for the longest-first
     # dispatch table (more than one round of splits of at least 32 tiles)
     "bf16-paged-longest-first": lambda: _small(5, batch=12, vocab=3000, prefix=(1000, 20000),
@@ -213,6 +219,8 @@ def small_case(request):
     c = make_case(w, seed=7, plant=(w.accept_mode == synth.ACCEPT_GREEDY))
     if request.param.endswith("-planted"):
         c.attn = synth.plant_draft_keys(c.attn, w, c.seed)
+    if request.param.endswith("-rising"):
+        c.attn = synth.rising_prefix_keys(c.attn, w, c.seed)
     run_gpu(c)
     c.planted_keys = request.param.endswith("-planted")
     return c
