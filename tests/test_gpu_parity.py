@@ -206,6 +206,7 @@ SMALL = {
     "bf16-v16001-stream-mixed": lambda: _small(5, batch=6, vocab=16001, prefix=(50, 300), kinds=[0, 1, 1, 0, 0, 1]),
     # rows too long for registers: streaming kernel (bf16 and fp32, ragged vocab)
     "bf16-stream": lambda: _small(2, batch=2, vocab=70001, prefix=100),
+    "bf16-stream-ragged-long": lambda: _small(2, batch=2, vocab=120003, prefix=100),
     "f32-stream": lambda: _small(1, vocab=40003, prefix=64),
     # the largest vocabulary, heavy ties
     "bf16-vmax-ties": lambda: _small(2, vocab=1 << 17, draft_sigma=0.05, prefix=64),
