@@ -42,6 +42,9 @@ struct AttnArgs {
     float scale_log2;
 };
 
+// a key half as a type, so that code for one half is compiled with h fixed
+template <int H> struct HalfC { static constexpr int value = H; };
+
 __device__ __forceinline__ int swap23(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
 // address of key `key`'s K row (head_dim elements) for (b, kvh)
@@ -225,7 +228,26 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
     const bool loader = !kProd || producer;
     const int lw = kProd ? wv - kNW : wv;               // loader wave index
     const int ln = lane & 31, hh = lane >> 5;
-    const int rw = wv % kRW, kh = wv / kRW;        // row wave, key half (kKS = 2)
+    int rw = wv % kRW;                                  // row wave (32 query rows)
+    const int kh = wv / kRW;                            // key half (kKS = 2)
+    // 8-wave form with 5 to 7 row blocks: the waves past the first
+    // nb - (8 - nb) take the last 8 - nb blocks by key halves, so that every
+    // SIMD computes the same share of a tile (6 blocks: four SIMDs with one
+    // whole block and one half each, instead of two with two whole blocks).
+    // hsplit: 0 = both key halves, 1 = keys 0..31 only, 2 = keys 32..63 only.
+    int hsplit = 0, nsplit_rb = 0, nfull_rb = 0;
+    if (kNW == 8 && kKS == 1) {
+        const int nb = a.rows_pg / 32;
+        if (nb >= 5 && nb <= 7) {
+            nsplit_rb = 8 - nb;
+            nfull_rb = nb - nsplit_rb;
+            if (wv >= nfull_rb) {
+                const int j = wv - nfull_rb;
+                rw = nfull_rb + (j >> 1);
+                hsplit = 1 + (j & 1);
+            }
+        }
+    }
     // block -> (split, row group, sequence/kv head).  In split-major order
     // all splits and row groups of one (sequence, kv head) share blockIdx
     // mod 8 when units0 % 8 == 0, which keeps them on one XCD and its L2.
@@ -466,311 +488,379 @@ __device__ __forceinline__ void tree_attn_body(const AttnArgs &a, AttnSmem<kRing
         }
         return;
     }
-    for (int item = 0; item < nitems; ++item) {
-        // this wave's loads of `item` have landed once at most the loads of
-        // the (up to kAhead - 1) later items issued so far are outstanding
-        wait_item<kLw, kAhead - 1>(min(kAhead - 1, nitems - 1 - item));
-        __syncthreads();                      // ... and every wave's; item - 1 is fully consumed
-        AttnBuf &B = sm.buf[item % kRing];
-        const bool draft = item >= nprefix;
-        // V^T of this item: with the 5-buffer ring the draft's V rows are staged
-        // in its own buffer's V^T area and transposed into the previous item's
-        // buffer (fully consumed, and the draft is the last item, so nothing is
-        // requested into it again)
-        u32x4a *const Vt = (kRing == 5 && draft) ? sm.buf[(item + kRing - 1) % kRing].Vt : B.Vt;
-        const int k0 = key_lo + item * kTK;
-        if (draft) {
-            // draft V rows (key-major) -> V^T, zeros for keys >= n; thread =
-            // (8 dims, 8 keys): an 8x8 block of bf16 transposed in registers
-            const u32x4a *dv = draft_rows(sm, B);
-            if (tid < 128) {
-                const int e8 = tid & 15, kg = tid >> 4;
-                u32x4a rows[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int t = 8 * kg + u;
-                    rows[u] = t < n ? dv[t * 16 + (e8 ^ (t & 15))] : u32x4a{0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int sh = 16 * (q & 1), w = q >> 1;
-                    u32x4a o;
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const uint32_t lo = (rows[2 * p][w] >> sh) & 0xffffu;
-                        const uint32_t hi = (rows[2 * p + 1][w] >> sh) & 0xffffu;
-                        o[p] = lo | (hi << 16);
+    // The tile loop, compiled once per kind of wave: hs = 0 for waves that
+    // compute both key halves, 1 or 2 for the waves of a split row block
+    // (separate loops keep the one-half code from crowding the registers of
+    // the pipelined loop).  Every copy meets the same barriers.
+    auto tile_loop = [&](auto hsc) {
+        constexpr int hs = decltype(hsc)::value;
+        for (int item = 0; item < nitems; ++item) {
+            // this wave's loads of `item` have landed once at most the loads of
+            // the (up to kAhead - 1) later items issued so far are outstanding
+            wait_item<kLw, kAhead - 1>(min(kAhead - 1, nitems - 1 - item));
+            __syncthreads();                      // ... and every wave's; item - 1 is fully consumed
+            AttnBuf &B = sm.buf[item % kRing];
+            const bool draft = item >= nprefix;
+            // V^T of this item: with the 5-buffer ring the draft's V rows are staged
+            // in its own buffer's V^T area and transposed into the previous item's
+            // buffer (fully consumed, and the draft is the last item, so nothing is
+            // requested into it again)
+            u32x4a *const Vt = (kRing == 5 && draft) ? sm.buf[(item + kRing - 1) % kRing].Vt : B.Vt;
+            const int k0 = key_lo + item * kTK;
+            if (draft) {
+                // draft V rows (key-major) -> V^T, zeros for keys >= n; thread =
+                // (8 dims, 8 keys): an 8x8 block of bf16 transposed in registers
+                const u32x4a *dv = draft_rows(sm, B);
+                if (tid < 128) {
+                    const int e8 = tid & 15, kg = tid >> 4;
+                    u32x4a rows[8];
+    #pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int t = 8 * kg + u;
+                        rows[u] = t < n ? dv[t * 16 + (e8 ^ (t & 15))] : u32x4a{0, 0, 0, 0};
                     }
-                    Vt[vpos(8 * e8 + q, kg)] = o;
+    #pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int sh = 16 * (q & 1), w = q >> 1;
+                        u32x4a o;
+    #pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            const uint32_t lo = (rows[2 * p][w] >> sh) & 0xffffu;
+                            const uint32_t hi = (rows[2 * p + 1][w] >> sh) & 0xffffu;
+                            o[p] = lo | (hi << 16);
+                        }
+                        Vt[vpos(8 * e8 + q, kg)] = o;
+                    }
                 }
-            }
-            __syncthreads();
-        } else if (k0 + kTK > key_hi) {
-            // tail tile: zero V^T entries of keys >= key_hi in every chunk from
-            // the one holding key_hi on (those chunks were loaded from it)
-            const int lim = key_hi - k0, J0 = lim >> 3, nJ = 8 - J0;
-            for (int c = tid; c < kHD * nJ; c += NT) {
-                const int e = c / nJ, J = J0 + c % nJ;
-                u32x4a v = B.Vt[vpos(e, J)];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int key = 8 * J + 2 * p;
-                    const uint32_t keep = (key < lim ? 0xffffu : 0u) | (key + 1 < lim ? 0xffff0000u : 0u);
-                    v[p] &= keep;
+                __syncthreads();
+            } else if (k0 + kTK > key_hi) {
+                // tail tile: zero V^T entries of keys >= key_hi in every chunk from
+                // the one holding key_hi on (those chunks were loaded from it)
+                const int lim = key_hi - k0, J0 = lim >> 3, nJ = 8 - J0;
+                for (int c = tid; c < kHD * nJ; c += NT) {
+                    const int e = c / nJ, J = J0 + c % nJ;
+                    u32x4a v = B.Vt[vpos(e, J)];
+    #pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const int key = 8 * J + 2 * p;
+                        const uint32_t keep = (key < lim ? 0xffffu : 0u) | (key + 1 < lim ? 0xffff0000u : 0u);
+                        v[p] &= keep;
+                    }
+                    B.Vt[vpos(e, J)] = v;
                 }
-                B.Vt[vpos(e, J)] = v;
+                __syncthreads();
             }
-            __syncthreads();
-        }
-        if (!kProd && item + kAhead < nitems) issue(item + kAhead);
+            if (!kProd && item + kAhead < nitems) issue(item + kAhead);
 
-        if (kNW == 8 && wave_active) {
-            // Two compute waves per SIMD: the tile goes by key halves h = 0, 1
-            // (keys 32h..32h+31), software-pipelined so that the products of
-            // one half are interleaved with the softmax of the other:
-            //   QK(0); QK(1) with weights(0); PV(0) with weights(1); PV(1).
-            // A half's weights are formed against the reference in force
-            // when they are formed (the lazy rule below, per half); a
-            // reference moved by half 1 applies to O as it stands after
-            // PV(0), whose weights were formed against the old one.
-            f32x16 sh[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sh[h][r] = 0.0f;
-            u32x4a kb[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(ln, 2 * j + hh)];
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sh[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[0], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(32 + ln, 2 * j + hh)];
-            // sh[h][8t + q] is the raw score of tile key 32h + 16t + 8hh + q for
-            // row my_row; masking as in the other forms
-            auto mask_half = [&](int h) {
+            if (kNW == 8 && wave_active) {
+                // Two compute waves per SIMD: the tile goes by key halves h = 0, 1
+                // (keys 32h..32h+31), software-pipelined so that the products of
+                // one half are interleaved with the softmax of the other:
+                //   QK(0); QK(1) with weights(0); PV(0) with weights(1); PV(1).
+                // A half's weights are formed against the reference in force
+                // when they are formed (the lazy rule below, per half); a
+                // reference moved by half 1 applies to O as it stands after
+                // PV(0), whose weights were formed against the old one.  A wave
+                // of a split row block (hsplit) computes its one half only.
+                f32x16 sh[2];
+    #pragma unroll
+                for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) sh[h][r] = 0.0f;
+                u32x4a kb[8];
+                // sh[h][8t + q] is the raw score of tile key 32h + 16t + 8hh + q for
+                // row my_row; masking as in the other forms
+                auto mask_half = [&](int h) {
+                    if (draft) {
+                        const uint32_t mk = (uint32_t)(my_anc >> (32 * h)) >> (8 * hh);
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int bit = 16 * (r >> 3) + (r & 7);
+                            sh[h][r] = ((mk >> bit) & 1u) ? sh[h][r] : -__builtin_inff();
+                        }
+                    } else if (k0 + kTK > key_hi) {
+                        const int lim = key_hi - k0 - 8 * hh;
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kq = 32 * h + 16 * (r >> 3) + (r & 7);
+                            sh[h][r] = kq < lim ? sh[h][r] : -__builtin_inff();
+                        }
+                    }
+                };
+                bf16x8 ph[2][2];
+                // half h's weights against the current reference; returns their row sum
+                auto weigh_half = [&](int h) -> float {
+                    const float mc = m_run * c2;
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        ph[h][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sh[h][r], c2, -mc));
+                    return sum_xor32(add_bf16x8(ph[h][0], 0.0f) + add_bf16x8(ph[h][1], 0.0f));
+                };
+                // the lazy rule of the other forms, for one half
+                auto settle_half = [&](int h, float lsum) {
+                    if (__any(!(lsum <= 256.0f) || l_run + lsum == 0.0f)) {
+                        float tmax = -__builtin_inff();
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sh[h][r]);
+                        tmax = max_xor32(tmax);
+                        const bool empty = l_run == 0.0f;
+                        const float m_new = empty ? (tmax == -__builtin_inff() ? m_run : tmax) : fmaxf(m_run, tmax);
+                        const float corr = empty ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+                        l_run *= corr;
+    #pragma unroll
+                        for (int dt = 0; dt < 4; ++dt)
+    #pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
+                        m_run = m_new;
+                        lsum = weigh_half(h);
+                    }
+                    l_run += lsum;
+                };
+                // one key half of the tile, QK, weights, PV (split row blocks)
+                auto one_half = [&](auto hc) {
+                    constexpr int h = decltype(hc)::value;
+    #pragma unroll
+                    for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(32 * h + ln, 2 * j + hh)];
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int j = 0; j < 8; ++j) sh[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[h], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 4 * h + 2 * (j >> 2) + hh)];
+                    mask_half(h);
+                    settle_half(h, weigh_half(h));
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[h][j >> 2], oacc[j & 3], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                if constexpr (hs == 1) {
+                    one_half(HalfC<0>{});
+                } else if constexpr (hs == 2) {
+                    one_half(HalfC<1>{});
+                } else {
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(ln, 2 * j + hh)];
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) sh[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[0], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) kb[j] = B.K[kpos(32 + ln, 2 * j + hh)];
+                mask_half(0);
+                // ---- QK(1) with weights(0) ----
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) sh[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[1], 0, 0, 0);
+                float ls = weigh_half(0);
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                settle_half(0, ls);
+                // V^T operands of half 0 (keys 0..31: chunks 2t + hh)
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 2 * (j >> 2) + hh)];
+                mask_half(1);
+                __builtin_amdgcn_sched_barrier(0);
+                // ---- PV(0) with weights(1) ----
+    #pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[0][j >> 2], oacc[j & 3], 0, 0, 0);
+                ls = weigh_half(1);
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                settle_half(1, ls);
+                // ---- PV(1) ----
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 4 + 2 * (j >> 2) + hh)];
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[1][j >> 2], oacc[j & 3], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                }
+            } else if (wave_active) {
+                // ---- S^T = K Q^T: two independent 32-key accumulators ----
+                // the K operands are read from LDS ahead of the products (all of
+                // them with 4 waves; in two halves with 8 waves, two per SIMD,
+                // whose registers hold only half), so the products issue back to
+                // back behind one LDS round trip per group
+                constexpr int kGroup = kNW == 8 ? 4 : 8;
+                // key halves this wave covers: sh = 0, 1 (kKS = 1) or sh = kh
+                constexpr int kNH = 2 / kKS;
+                const int sh0 = kKS == 2 ? kh : 0;
+                f32x16 sacc[kNH];
+    #pragma unroll
+                for (int u = 0; u < kNH; ++u)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[u][r] = 0.0f;
+    #pragma unroll
+                for (int g0 = 0; g0 < 8; g0 += kGroup) {
+                    u32x4a ka[kNH][kGroup];
+    #pragma unroll
+                    for (int j = 0; j < kGroup; ++j)
+    #pragma unroll
+                        for (int u = 0; u < kNH; ++u) ka[u][j] = B.K[kpos(32 * (sh0 + u) + ln, 2 * (g0 + j) + hh)];
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int j = 0; j < kGroup; ++j)
+    #pragma unroll
+                        for (int u = 0; u < kNH; ++u)
+                            sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[u][j]), qf[g0 + j], sacc[u], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // the V^T operands of this tile, in flight during the softmax (with
+                // 8 waves, two per SIMD, the registers hold them only after it)
+                constexpr int kNV = 8 * kNH;                  // V^T operands per tile
+                constexpr int kEarly = kNW == 8 ? 0 : kNV;
+                u32x4a va[kNV];
+    #pragma unroll
+                for (int j = 0; j < kEarly; ++j) {
+                    const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
+                    va[j] = Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // sacc[u][8t + q] is the raw score of tile key 32(sh0 + u) + 16t + 8hh + q
+                // for row my_row.  Rows without a node have zero Q (finite scores, never
+                // written out), so only keys need masking: past prefix_len in the
+                // tail tile, and non-ancestors in the draft tile.
                 if (draft) {
-                    const uint32_t mk = (uint32_t)(my_anc >> (32 * h)) >> (8 * hh);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int bit = 16 * (r >> 3) + (r & 7);
-                        sh[h][r] = ((mk >> bit) & 1u) ? sh[h][r] : -__builtin_inff();
+    #pragma unroll
+                    for (int u = 0; u < kNH; ++u) {
+                        const uint32_t mk = (uint32_t)(my_anc >> (32 * (sh0 + u))) >> (8 * hh);
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int bit = 16 * (r >> 3) + (r & 7);
+                            sacc[u][r] = ((mk >> bit) & 1u) ? sacc[u][r] : -__builtin_inff();
+                        }
                     }
                 } else if (k0 + kTK > key_hi) {
-                    const int lim = key_hi - k0 - 8 * hh;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kq = 32 * h + 16 * (r >> 3) + (r & 7);
-                        sh[h][r] = kq < lim ? sh[h][r] : -__builtin_inff();
-                    }
+                    const int lim = key_hi - k0 - 8 * hh;    // tile keys below lim + 8hh are valid
+    #pragma unroll
+                    for (int u = 0; u < kNH; ++u)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kq = 32 * (sh0 + u) + 16 * (r >> 3) + (r & 7);
+                            sacc[u][r] = kq < lim ? sacc[u][r] : -__builtin_inff();
+                        }
                 }
-            };
-            bf16x8 ph[2][2];
-            // half h's weights against the current reference; returns their row sum
-            auto weigh_half = [&](int h) -> float {
-                const float mc = m_run * c2;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    ph[h][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sh[h][r], c2, -mc));
-                return sum_xor32(add_bf16x8(ph[h][0], 0.0f) + add_bf16x8(ph[h][1], 0.0f));
-            };
-            // the lazy rule of the other forms, for one half
-            auto settle_half = [&](int h, float lsum) {
+                // Weights against the current reference, and their row sum (of
+                // the bf16 weights themselves, as the PV product uses them)
+                bf16x8 pf[kNH][2];
+                auto weigh = [&]() -> float {
+                    const float mc = m_run * c2;
+    #pragma unroll
+                    for (int u = 0; u < kNH; ++u)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            pf[u][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][r], c2, -mc));
+                    float s0 = 0.0f, s1 = 0.0f;
+    #pragma unroll
+                    for (int u = 0; u < kNH; ++u) {
+                        s0 = add_bf16x8(pf[u][0], s0);
+                        s1 = add_bf16x8(pf[u][1], s1);
+                    }
+                    return sum_xor32(s0 + s1);
+                };
+                float lsum = weigh();
+                // Lazy rescaling: the reference m_run moves only when some weight
+                // exceeds 2^8 (then so does the row sum), or while nothing has
+                // been accumulated (reference 0 may lie far above every score,
+                // where all weights underflow).  Otherwise every weight is at
+                // most 2^8, which fp32 sums and bf16 products carry as well as
+                // weights below 1, and O / l is unchanged.  When it moves, it goes
+                // to the row max (only up once something is accumulated), O and l
+                // are rescaled and the weights formed again; the row max is not
+                // computed otherwise.
                 if (__any(!(lsum <= 256.0f) || l_run + lsum == 0.0f)) {
                     float tmax = -__builtin_inff();
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sh[h][r]);
+    #pragma unroll
+                    for (int u = 0; u < kNH; ++u)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[u][r]);
                     tmax = max_xor32(tmax);
                     const bool empty = l_run == 0.0f;
                     const float m_new = empty ? (tmax == -__builtin_inff() ? m_run : tmax) : fmaxf(m_run, tmax);
                     const float corr = empty ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
                     l_run *= corr;
-#pragma unroll
+    #pragma unroll
                     for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
+    #pragma unroll
                         for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
                     m_run = m_new;
-                    lsum = weigh_half(h);
+                    lsum = weigh();
                 }
                 l_run += lsum;
-            };
-            mask_half(0);
-            // ---- QK(1) with weights(0) ----
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sh[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), qf[j], sh[1], 0, 0, 0);
-            float ls = weigh_half(0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            settle_half(0, ls);
-            // V^T operands of half 0 (keys 0..31: chunks 2t + hh)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 2 * (j >> 2) + hh)];
-            mask_half(1);
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- PV(0) with weights(1) ----
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[0][j >> 2], oacc[j & 3], 0, 0, 0);
-            ls = weigh_half(1);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            settle_half(1, ls);
-            // ---- PV(1) ----
-#pragma unroll
-            for (int j = 0; j < 8; ++j) kb[j] = Vt[vpos(32 * (j & 3) + ln, 4 + 2 * (j >> 2) + hh)];
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[j]), ph[1][j >> 2], oacc[j & 3], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        } else if (wave_active) {
-            // ---- S^T = K Q^T: two independent 32-key accumulators ----
-            // the K operands are read from LDS ahead of the products (all of
-            // them with 4 waves; in two halves with 8 waves, two per SIMD,
-            // whose registers hold only half), so the products issue back to
-            // back behind one LDS round trip per group
-            constexpr int kGroup = kNW == 8 ? 4 : 8;
-            // key halves this wave covers: sh = 0, 1 (kKS = 1) or sh = kh
-            constexpr int kNH = 2 / kKS;
-            const int sh0 = kKS == 2 ? kh : 0;
-            f32x16 sacc[kNH];
-#pragma unroll
-            for (int u = 0; u < kNH; ++u)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[u][r] = 0.0f;
-#pragma unroll
-            for (int g0 = 0; g0 < 8; g0 += kGroup) {
-                u32x4a ka[kNH][kGroup];
-#pragma unroll
-                for (int j = 0; j < kGroup; ++j)
-#pragma unroll
-                    for (int u = 0; u < kNH; ++u) ka[u][j] = B.K[kpos(32 * (sh0 + u) + ln, 2 * (g0 + j) + hh)];
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < kGroup; ++j)
-#pragma unroll
-                    for (int u = 0; u < kNH; ++u)
-                        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[u][j]), qf[g0 + j], sacc[u], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // the V^T operands of this tile, in flight during the softmax (with
-            // 8 waves, two per SIMD, the registers hold them only after it)
-            constexpr int kNV = 8 * kNH;                  // V^T operands per tile
-            constexpr int kEarly = kNW == 8 ? 0 : kNV;
-            u32x4a va[kNV];
-#pragma unroll
-            for (int j = 0; j < kEarly; ++j) {
-                const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
-                va[j] = Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // sacc[u][8t + q] is the raw score of tile key 32(sh0 + u) + 16t + 8hh + q
-            // for row my_row.  Rows without a node have zero Q (finite scores, never
-            // written out), so only keys need masking: past prefix_len in the
-            // tail tile, and non-ancestors in the draft tile.
-            if (draft) {
-#pragma unroll
-                for (int u = 0; u < kNH; ++u) {
-                    const uint32_t mk = (uint32_t)(my_anc >> (32 * (sh0 + u))) >> (8 * hh);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int bit = 16 * (r >> 3) + (r & 7);
-                        sacc[u][r] = ((mk >> bit) & 1u) ? sacc[u][r] : -__builtin_inff();
-                    }
-                }
-            } else if (k0 + kTK > key_hi) {
-                const int lim = key_hi - k0 - 8 * hh;    // tile keys below lim + 8hh are valid
-#pragma unroll
-                for (int u = 0; u < kNH; ++u)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kq = 32 * (sh0 + u) + 16 * (r >> 3) + (r & 7);
-                        sacc[u][r] = kq < lim ? sacc[u][r] : -__builtin_inff();
-                    }
-            }
-            // Weights against the current reference, and their row sum (of
-            // the bf16 weights themselves, as the PV product uses them)
-            bf16x8 pf[kNH][2];
-            auto weigh = [&]() -> float {
-                const float mc = m_run * c2;
-#pragma unroll
-                for (int u = 0; u < kNH; ++u)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        pf[u][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][r], c2, -mc));
-                float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-                for (int u = 0; u < kNH; ++u) {
-                    s0 = add_bf16x8(pf[u][0], s0);
-                    s1 = add_bf16x8(pf[u][1], s1);
-                }
-                return sum_xor32(s0 + s1);
-            };
-            float lsum = weigh();
-            // Lazy rescaling: the reference m_run moves only when some weight
-            // exceeds 2^8 (then so does the row sum), or while nothing has
-            // been accumulated (reference 0 may lie far above every score,
-            // where all weights underflow).  Otherwise every weight is at
-            // most 2^8, which fp32 sums and bf16 products carry as well as
-            // weights below 1, and O / l is unchanged.  When it moves, it goes
-            // to the row max (only up once something is accumulated), O and l
-            // are rescaled and the weights formed again; the row max is not
-            // computed otherwise.
-            if (__any(!(lsum <= 256.0f) || l_run + lsum == 0.0f)) {
-                float tmax = -__builtin_inff();
-#pragma unroll
-                for (int u = 0; u < kNH; ++u)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[u][r]);
-                tmax = max_xor32(tmax);
-                const bool empty = l_run == 0.0f;
-                const float m_new = empty ? (tmax == -__builtin_inff() ? m_run : tmax) : fmaxf(m_run, tmax);
-                const float corr = empty ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-                l_run *= corr;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
-                m_run = m_new;
-                lsum = weigh();
-            }
-            l_run += lsum;
-            // ---- O^T += V^T P^T: four independent accumulators per k-step ----
-            if constexpr (kEarly == kNV) {
-#pragma unroll
-                for (int j = 0; j < kNV; ++j) {
-                    const int u = j >> 3, t = (j >> 2) & 1, dt = j & 3;
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[u][t], oacc[dt], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int g0 = 0; g0 < kNV; g0 += 8) {
-#pragma unroll
-                    for (int j = g0; j < g0 + 8; ++j) {
-                        const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
-                        va[j] = Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int j = g0; j < g0 + 8; ++j) {
+                // ---- O^T += V^T P^T: four independent accumulators per k-step ----
+                if constexpr (kEarly == kNV) {
+    #pragma unroll
+                    for (int j = 0; j < kNV; ++j) {
                         const int u = j >> 3, t = (j >> 2) & 1, dt = j & 3;
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[u][t], oacc[dt], 0, 0, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+    #pragma unroll
+                    for (int g0 = 0; g0 < kNV; g0 += 8) {
+    #pragma unroll
+                        for (int j = g0; j < g0 + 8; ++j) {
+                            const int sh = sh0 + (j >> 3), t = (j >> 2) & 1, dt = j & 3;
+                            va[j] = Vt[vpos(32 * dt + ln, 4 * sh + 2 * t + hh)];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                        for (int j = g0; j < g0 + 8; ++j) {
+                            const int u = j >> 3, t = (j >> 2) & 1, dt = j & 3;
+                            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[j]), pf[u][t], oacc[dt], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
         }
-    }
+    };
+    if (kNW == 8 && hsplit == 1) tile_loop(HalfC<1>{});
+    else if (kNW == 8 && hsplit == 2) tile_loop(HalfC<2>{});
+    else tile_loop(HalfC<0>{});
 
+    if (kNW == 8 && kKS == 1 && nsplit_rb > 0) {
+        // split row blocks: the key-1 half's state goes through LDS to the
+        // key-0 half's wave, which combines and writes the rows (the tile
+        // ring is free once every wave has left the loop)
+        __syncthreads();
+        const int slot = rw - nfull_rb;                 // split block of this wave
+        float *xo = reinterpret_cast<float *>(sm.buf) + (size_t)slot * 64 * 64;   // [64 regs][64 lanes]
+        float2 *xml = reinterpret_cast<float2 *>(reinterpret_cast<float *>(sm.buf) + (size_t)3 * 64 * 64) + slot * 64;
+        if (hsplit == 2 && wave_active) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xo[(16 * dt + r) * 64 + lane] = oacc[dt][r];
+            xml[lane] = make_float2(m_run, l_run);
+        }
+        __syncthreads();
+        if (hsplit == 2) return;
+        if (hsplit == 1 && wave_active) {
+            // a half with nothing accumulated (every key masked) has no max
+            const float2 o = xml[lane];
+            const float ma = l_run > 0.0f ? m_run : -__builtin_inff(), mb = o.y > 0.0f ? o.x : -__builtin_inff();
+            const float mn = fmaxf(ma, mb);
+            const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+            const float e0 = __builtin_amdgcn_exp2f((ma - mu) * c2), e1 = __builtin_amdgcn_exp2f((mb - mu) * c2);
+            l_run = l_run * e0 + o.y * e1;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * e0 + xo[(16 * dt + r) * 64 + lane] * e1;
+            m_run = mn;
+        }
+    }
     if constexpr (kKS == 2) {
         // combine the key halves: the second half's state goes through LDS
         // (the tile ring is free once every wave has left the loop)

@@ -144,6 +144,11 @@ SMALL = {
     "bf16-gqa8-split-planted": lambda: _small(4, batch=2, prefix=(6000, 12000), vocab=3000),
     "bf16-paged-split-planted": lambda: _small(5, batch=4, vocab=3000, prefix=(9000, 20000),
                                                kinds=[0, 1, 0, 1]),
+    # 8-wave form with 5 and 7 row blocks (rows 20 * 8 = 160, 56 * 4 = 224):
+    # the last blocks are computed by key halves on two waves each
+    "bf16-gqa8-m20-split-blocks": lambda: _small(4, batch=2, m=20, prefix=(700, 3000), vocab=3000),
+    "bf16-paged-m56-split-blocks": lambda: _small(5, batch=3, m=56, vocab=3000, prefix=(300, 2500),
+                                                  kinds=[0, 0, 0]),
     # GQA with two row groups (rows = 48 * 8 = 384)
     "bf16-gqa8-rowgroups": lambda: _small(4, batch=2, prefix=700, vocab=3000),
     # prefix scores that climb along the prefix: the softmax reference moves
