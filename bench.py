@@ -4,9 +4,12 @@
 A step is the whole hot path on one stream: eagle_build_tree (draft-row
 softmax statistics, top-C children, expansion, rerank, compaction),
 eagle_tree_mask, eagle_tree_attn and eagle_accept, over one batch of
-synthetic inputs already resident in HBM.  The default workload is the
-Llama-2-7B-shaped one (batch 1, bf16, 32 heads x 128, prefix 2048, vocab
-32000, depth 6, k = 10, m = 60, greedy).  Prints one JSON line.
+synthetic inputs already resident in HBM.  The headline workload is the
+batched serving mix (batch 64, bf16, Llama-3-8B attention shape 32 q / 8 kv
+heads x 128, prefixes uniform in 1k-32k in 16-token pages, vocab 128256,
+half dynamic trees with m = 60, half K = 7 parallel-draft chains, greedy);
+the other four workloads are timed in the same run and reported under
+"workloads".  Prints one JSON line.
 
 Inputs: seeded synthetic draft/target logits and Q/K/V (random numbers stand
 in for trained models and text benchmarks).  The timed steps rotate over
