@@ -284,8 +284,14 @@ def test_heavy_ties_use_exact_fallback():
     assert_tree_equal(c)
 
 
-def test_determinism():
-    w = _small(5, batch=4, vocab=9000, prefix=(100, 3000), kinds=[0, 1, 0, 0])
+@pytest.mark.parametrize("shape", ["paged-mixed", "gqa8-split-blocks"])
+def test_determinism(shape):
+    # the paged mix of trees and chains (8-wave and key-half forms), and row
+    # groups of 6 blocks (the last two computed by key halves on two waves each)
+    if shape == "paged-mixed":
+        w = _small(5, batch=4, vocab=9000, prefix=(100, 3000), kinds=[0, 1, 0, 0])
+    else:
+        w = _small(4, batch=2, vocab=3000, prefix=(1500, 5000))
     c = make_case(w, seed=11)
     outs = []
     for _ in range(10):
