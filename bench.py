@@ -273,6 +273,26 @@ def bench_workload(n, args, extras, cpu_seconds):
     log(f"[bench] timed {K} steps ({'graph replays' if graphs is not None else 'eager'}): "
         f"{ms_per_step * 1e3:.1f} us/step")
 
+    # ---- per-step times (cold, sets rotate): events between the replays --
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    step_ev[0].record()
+    for k in range(K):
+        if graphs is not None:
+            graphs[k % nsets].replay()
+        else:
+            run_step(sets[k % nsets])
+        step_ev[k + 1].record()
+    torch.cuda.synchronize()
+    step_us = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) * 1e3 for k in range(K)])
+    pctl = {f"p{q}": round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)}
+
+    # accepted draft tokens per sequence, from the last step of input set 0
+    run_step(sets[0])
+    torch.cuda.synchronize()
+    acc_len = step.accept_len.to(torch.float64)
+    mean_accepted = float(acc_len.mean().item())
+
     # ---- eager steps (context), events around each attention call -----
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
@@ -365,6 +385,11 @@ def bench_workload(n, args, extras, cpu_seconds):
     else:
         bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
     value = tokens_per_step / (ms_per_step * 1e-3)
+    # draft-row bytes the build reads (every row a sequence's tree or chain owns, once)
+    esz = 2 if w.dtype == torch.bfloat16 else 4
+    build_bytes = sum((w.rows_dynamic if kd == synth.TREE_DYNAMIC else w.chain_k) for kd in w.kinds) * w.vocab * esz
+    stage_gbs = {"build_tree+mask": round(build_bytes / (stage_us["build_tree+mask"] * 1e-6) / 1e9, 1),
+                 "tree_attn": round(nbytes / (stage_us["tree_attn"] * 1e-6) / 1e9, 1)}
     traffic, traffic_src = traffic_note(w)
     mfma_util, mfma_src = mfma_note(w)
 
@@ -402,6 +427,11 @@ def bench_workload(n, args, extras, cpu_seconds):
                      "mfma_util_counter": mfma_util, "mfma_util_source": mfma_src},
         "cpu_baseline": cpu,
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stages_gbs": stage_gbs,
+        "stages_bytes": {"build_tree+mask": build_bytes, "tree_attn": nbytes},
+        "step_us_percentiles": pctl,
+        "mean_accepted_tokens": round(mean_accepted, 3),
+        "tau": round(mean_accepted + 1.0, 3),
         "warm": {"ms_per_step": round(warm_ms, 5), "value": round(tokens_per_step / (warm_ms * 1e-3), 1)},
         "launch": "hipGraph replay per step" if graphs is not None else "eager",
         "eager": {"ms_per_step": round(eager_ms, 5), "value": round(tokens_per_step / (eager_ms * 1e-3), 1)},
