@@ -204,6 +204,12 @@ SMALL = {
     "f32-tiny-vocab": lambda: _small(1, vocab=37, children=16, depth=3, topk=4, m=40, prefix=40),
     # chain only, K = depth 64 is not allowed (m_max <= 64), use K = 64 nodes
     "bf16-chain64": lambda: _small(5, batch=2, kinds=[1, 1], chain_k=64, vocab=3000, prefix=(50, 200)),
+    # the largest dynamic trees: m = 64 (a full 64-node draft tile, mask bit
+    # 63), GQA 8 (two row groups of 8 blocks); and a wide tree, 16 children per
+    # node and 16 expanded per depth (784 candidates, the general-C select)
+    "bf16-gqa8-m64": lambda: _small(4, batch=2, m=64, prefix=(300, 2000), vocab=3000),
+    "bf16-wide-c16-k16-m64": lambda: _small(5, batch=2, kinds=[0, 0], depth=4, topk=16, children=16, m=64,
+                                            vocab=3000, prefix=(100, 1500)),
     # register-held rows (few rows) with heavy ties (sd 0.02), and at 8 vectors per thread
     "bf16-v32000-ties": lambda: _small(2, vocab=32000, draft_sigma=0.02, prefix=100),
     "f32-v32000": lambda: _small(1, vocab=32000, prefix=64),
