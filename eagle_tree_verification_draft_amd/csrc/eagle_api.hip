@@ -83,8 +83,18 @@ eagle_status check_tree_params(const eagle_tree_params *p, int32_t batch)
     if (p->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", p->m_max, kMaxMMax);
     const long long N = (long long)p->children + (long long)(p->depth - 1) * p->topk * p->children;
     if (N > kMaxCand) return fail(EAGLE_ERR_UNSUPPORTED, "%lld candidates > %d", N, kMaxCand);
-    if (p->m < 1 || p->m > p->m_max || p->m > N)
-        return fail(EAGLE_ERR_INVALID, "m %d not in [1, min(m_max %d, candidates %lld)]", p->m, p->m_max, N);
+    // the candidates a tree really generates: a depth with fewer than k nodes
+    // expands all of them (depth d + 1 holds min(k, nodes of depth d) x C)
+    long long n_gen = 0;
+    for (long long d = 0, nn = p->children; d < p->depth; ++d) {
+        n_gen += nn;
+        nn = (nn < p->topk ? nn : p->topk) * (long long)p->children;
+    }
+    // the EAGLE-2 rerank keeps m of them; the other policies keep what their
+    // rule selects (at most m)
+    const long long m_cap = p->policy == EAGLE_POLICY_EAGLE2 ? n_gen : N;
+    if (p->m < 1 || p->m > p->m_max || p->m > m_cap)
+        return fail(EAGLE_ERR_INVALID, "m %d not in [1, min(m_max %d, candidates %lld)]", p->m, p->m_max, m_cap);
     const long long rows_dyn = 1 + (long long)(p->depth - 1) * p->topk;
     if (rows_dyn > kMaxRows) return fail(EAGLE_ERR_UNSUPPORTED, "dynamic trees use %lld rows > %d", rows_dyn, kMaxRows);
     if (rows_dyn > p->r_max) return fail(EAGLE_ERR_INVALID, "dynamic trees use %lld rows > r_max %d", rows_dyn, p->r_max);

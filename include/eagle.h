@@ -122,7 +122,10 @@ typedef struct {
     int32_t depth;      /* D >= 1: draft tokens sit at depths 1..D */
     int32_t topk;       /* k >= 1: nodes expanded per depth */
     int32_t children;   /* C in [1, 16]: children per expanded node */
-    int32_t m;          /* nodes kept for dynamic trees, 1 <= m <= min(m_max, C + (D-1)kC) */
+    int32_t m;          /* nodes kept for dynamic trees, 1 <= m <= min(m_max, C + (D-1)kC);
+                           with the EAGLE2 policy m must not exceed the candidates
+                           generated, sum over depths of n_d (n_1 = C,
+                           n_(d+1) = min(k, n_d) C), which is smaller when k > n_d */
     int32_t chain_k;    /* K for chain sequences, 0 if there are none; K <= m_max */
     int32_t vocab;      /* V in [C, 131072] */
     int32_t m_max;      /* output slots per sequence, <= 64 */

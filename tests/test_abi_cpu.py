@@ -4,9 +4,11 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 import eagle_tree_verification_draft_amd as E
+import oracle
 
 HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "eagle.h")
 
@@ -54,10 +56,26 @@ def _call_build(p, batch=1, logits=1 << 20, dtype=E.EAGLE_BF16, stride=None, ws=
     (dict(depth=0), E.EAGLE_ERR_INVALID),
     (dict(chain_k=61), E.EAGLE_ERR_INVALID),
     (dict(depth=8, topk=16, children=16, m=60), E.EAGLE_ERR_UNSUPPORTED),   # 1808 candidates
+    # k = 5 > C = 2: depth 1 has 2 nodes to expand, so 2 + 4 = 6 candidates are
+    # generated (C + (D-1)kC = 12 bounds them); the rerank cannot keep 8
+    (dict(depth=2, topk=5, children=2, m=8, m_max=8, r_max=6), E.EAGLE_ERR_INVALID),
 ])
 def test_build_tree_rejects_bad_params(over, want):
     assert _call_build(_tree(**over)) == want
     assert E.lib().eagle_last_error()
+
+
+def test_m_up_to_the_generated_candidates_is_accepted():
+    # the same k > C tree keeping all 6 generated candidates is valid, and the
+    # oracle builds it (its own check is against the generated count too)
+    p = _tree(depth=2, topk=5, children=2, m=6, m_max=8, r_max=6)
+    assert E.lib().eagle_build_tree_workspace_size(C.byref(p), 1) > 0
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((1, 6, 100)).astype(np.float32)
+    t = oracle.build_tree(logits, 2, 5, 2, 6, m_max=8)
+    assert int(t["num_nodes"][0]) == 6
+    with pytest.raises(oracle.OracleError):
+        oracle.build_tree(logits, 2, 5, 2, 7, m_max=8)
 
 
 def test_build_tree_rejects_null_stride_and_workspace():
