@@ -25,6 +25,7 @@ import oracle
 import synth
 from conftest import to_np
 from gpu_harness import (BF16_TOL, F32_TOL, assert_accept_equal, assert_tree_equal, check_attn_rows, make_case,
+                         sample_rows,
                          oracle_mask, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
@@ -338,3 +339,47 @@ def test_random_template(i):
     assert errs == 0
     for k in ("tokens", "parent", "depth", "score", "src_row", "num_nodes"):
         assert np.array_equal(got[k], ot[k]), k
+
+
+# ---------------------------------------------------------------------------
+# larger random attention shapes (key splits, merge, longest-first order),
+# with planted draft keys so that the check sees the tree at long prefixes
+# ---------------------------------------------------------------------------
+N_LARGE = 8
+
+
+def random_large_workload(i: int) -> synth.Workload:
+    rng = np.random.default_rng(9800 + i)
+    w = dataclasses.replace(synth.workload(5))
+    kv = int(rng.choice([2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    w.num_kv_heads, w.num_q_heads = kv, kv * g
+    w.block_size = int(rng.choice([0, 16, 32, 64]))
+    w.batch = int(rng.integers(4, 25))
+    w.m = int(rng.integers(20, 65))
+    w.chain_k = int(rng.integers(1, 9))
+    w.kinds = [int(rng.random() < 0.5) for _ in range(w.batch)]
+    w.kinds[0] = synth.TREE_DYNAMIC
+    w.vocab = int(rng.integers(2000, 6000))
+    lo = int(rng.integers(500, 8000))
+    w.prefix = (lo, int(rng.integers(lo + 1, 24000)))
+    w.poison_tail = bool(rng.random() < 0.5)
+    w.name = f"random-large-{i}"
+    return w
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_attention_planted(i):
+    w = random_large_workload(i)
+    say(f"[random large {i}] {w}")
+    c = make_case(w, seed=500 + i)
+    c.attn = synth.plant_draft_keys(c.attn, w, c.seed)
+    run_gpu(c)
+    assert_tree_equal(c)
+    rng = np.random.default_rng(600 + i)
+    sel = sample_rows(c, 96, rng)
+    mx, rl2 = check_attn_rows(c, sel, BF16_TOL, power=0.1)
+    say(f"[random large {i}] max-abs {mx:.3g}, relative L2 {rl2:.3g}")
+    assert rl2 <= 1e-2
+    assert_accept_equal(c)
+    assert c.step.errors() == 0
