@@ -11,6 +11,8 @@ namespace eagle {
 constexpr int kWave = 64;
 constexpr int kMaxChildren = 16;
 constexpr int kMaxMMax = 64;
+constexpr int kMaxHeads = 1024;           // query heads per call
+constexpr long long kMaxQueryRows = 1ll << 26;   // batch x num_q_heads x m_max
 constexpr int kMaxVocab = 1 << 17;
 
 // ---------------------------------------------------------------------------

@@ -397,12 +397,15 @@ static eagle_status check_attn_params(const eagle_attn_params *a, int32_t batch)
     if (a->num_kv_heads < 1 || a->num_q_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
         return fail(EAGLE_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
                     a->num_q_heads, a->num_kv_heads);
+    if (a->num_q_heads > kMaxHeads) return fail(EAGLE_ERR_UNSUPPORTED, "num_q_heads %d > %d", a->num_q_heads, kMaxHeads);
     if (a->dtype == EAGLE_BF16 && a->head_dim != 128)
         return fail(EAGLE_ERR_UNSUPPORTED, "bf16 head_dim %d (only 128)", a->head_dim);
     if (a->dtype == EAGLE_F32 && a->head_dim != 64 && a->head_dim != 128)
         return fail(EAGLE_ERR_UNSUPPORTED, "fp32 head_dim %d (only 64, 128)", a->head_dim);
     if (a->m_max < 1) return fail(EAGLE_ERR_INVALID, "m_max %d < 1", a->m_max);
     if (a->m_max > kMaxMMax) return fail(EAGLE_ERR_UNSUPPORTED, "m_max %d > %d", a->m_max, kMaxMMax);
+    if ((long long)batch * a->num_q_heads * a->m_max > kMaxQueryRows)
+        return fail(EAGLE_ERR_UNSUPPORTED, "batch x num_q_heads x m_max above %lld query rows", kMaxQueryRows);
     if (a->block_size < 0 || a->max_prefix < 0) return fail(EAGLE_ERR_INVALID, "negative block_size or max_prefix");
     if (a->dtype == EAGLE_BF16 && a->block_size == 0 && a->max_prefix % 8 != 0)
         return fail(EAGLE_ERR_UNSUPPORTED, "bf16 contiguous cache needs max_prefix %% 8 == 0");
@@ -444,6 +447,7 @@ eagle_status eagle_tree_attn(const eagle_attn_params *a, int32_t batch, const vo
           aligned16(out)))
         return fail(EAGLE_ERR_UNSUPPORTED, "bf16 tensors must be 16-byte aligned");
     const AttnPlan P = attn_plan(a, batch);
+    if (P.total == 0) return fail(EAGLE_ERR_UNSUPPORTED, "more than 2^31 - 1 workgroups in one launch");
     s = check_workspace(workspace, workspace_bytes, P.total);
     if (s != EAGLE_OK) return s;
     if (batch == 0) return ok();

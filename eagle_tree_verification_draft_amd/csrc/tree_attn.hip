@@ -1358,6 +1358,7 @@ AttnPlan attn_plan(const eagle_attn_params *a, int32_t batch)
     const int per = (tiles + best - 1) / best;
     P.chunk = per * kTK;
     P.nsplit = (tiles + per - 1) / per;
+    if ((long long)units * P.nsplit > INT32_MAX) { P.total = 0; return P; }   // rejected by the caller
     // Longest-first dispatch (k_attn_schedule) when the launch takes more
     // than one round of long workgroups: with prefixes of different lengths
     // the split-major order leaves CUs idle in the last round.

@@ -334,7 +334,9 @@ eagle_status eagle_tree_mask(int32_t batch, int32_t m_max, const int32_t *parent
  * k_cache / v_cache may be NULL for a contiguous cache with max_prefix 0.
  * Errors: EAGLE_ERR_INVALID for null pointers, num_q_heads % num_kv_heads != 0,
  * a missing block table in paged mode; EAGLE_ERR_UNSUPPORTED past the v1
- * limits; EAGLE_ERR_WORKSPACE for a short workspace.
+ * limits (num_q_heads <= 1024, batch x num_q_heads x m_max <= 2^26, at most
+ * 2^31 - 1 workgroups in the attention launch); EAGLE_ERR_WORKSPACE for a
+ * short workspace.
  */
 typedef struct {
     int32_t num_q_heads;

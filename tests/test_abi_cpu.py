@@ -116,6 +116,8 @@ def _call_attn(a, bt=True, align=0, ws=1 << 21, wsb=1 << 30):
     (dict(block_size=0, max_blocks=0, max_prefix=13), E.EAGLE_ERR_UNSUPPORTED),
     (dict(max_blocks=0), E.EAGLE_ERR_INVALID),
     (dict(scale=float("nan")), E.EAGLE_ERR_INVALID),
+    (dict(num_q_heads=2048), E.EAGLE_ERR_UNSUPPORTED),
+    (dict(num_q_heads=(1 << 31) - 1, num_kv_heads=1), E.EAGLE_ERR_UNSUPPORTED),
 ])
 def test_tree_attn_rejects_bad_params(over, want):
     assert _call_attn(_attn(**over)) == want
@@ -126,6 +128,18 @@ def test_tree_attn_rejects_missing_table_misalignment_and_workspace():
     assert _call_attn(_attn(), align=2) == E.EAGLE_ERR_UNSUPPORTED
     assert _call_attn(_attn(), wsb=8) == E.EAGLE_ERR_WORKSPACE
     assert E.lib().eagle_tree_attn_workspace_size(C.byref(_attn()), 2) >= 256
+
+
+def test_tree_attn_size_limits():
+    """Query rows and the launch's workgroup count stay within their stated
+    limits; past them the size query returns 0 and the call is unsupported."""
+    L = E.lib()
+    a = _attn(num_q_heads=64, num_kv_heads=64, m_max=64, block_size=16, max_blocks=4)
+    assert L.eagle_tree_attn_workspace_size(C.byref(a), 1 << 14) > 0          # 2^26 query rows
+    assert L.eagle_tree_attn_workspace_size(C.byref(a), (1 << 14) + 1) == 0
+    big = _attn(num_q_heads=64, num_kv_heads=64, m_max=64, block_size=1 << 16, max_blocks=1 << 14)
+    assert L.eagle_tree_attn_workspace_size(C.byref(big), 1 << 14) == 0        # > 2^31 - 1 workgroups
+    assert L.eagle_tree_attn_workspace_size(C.byref(big), 1) > 0
 
 
 def _call_commit(a, max_accept=6, bt=True, align=0, null_slot=False, ws=1 << 21, wsb=256):
