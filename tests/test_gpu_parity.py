@@ -290,6 +290,31 @@ def test_heavy_ties_use_exact_fallback():
     assert_tree_equal(c)
 
 
+@pytest.mark.parametrize("vocab", [20000, 70000])
+def test_weight_bins_and_direct_weights_agree_with_the_oracle(vocab):
+    # bf16 rows long enough for the binned weight sum (register form at 20000,
+    # streaming form at 70000), planted with values outside the bins' range
+    # (zeros, tiny, at and past both range ends, -inf) and rows whose maximum
+    # is so large that every binned weight is 0
+    w = _small(2, batch=1, vocab=vocab, prefix=64)
+    c = make_case(w, seed=7)
+    g = torch.Generator().manual_seed(17)
+    d = c.draft.float().cpu()
+    R, V = d.shape[1], d.shape[2]
+    planted = torch.tensor([0.0, -0.0, 1e-6, -1e-6, 2.0 ** -9, -(2.0 ** -9), 2.0 ** -10, 3e-3, 127.0, 128.0,
+                            -128.0, 200.0, -300.0, float("-inf")])
+    for r in range(R):
+        idx = torch.randperm(V, generator=g)[:4 * planted.numel()]
+        d[0, r, idx] = planted.repeat(4)
+        if r % 5 == 1:
+            d[0, r, int(torch.randint(V, (1,), generator=g))] = 400.0
+    c.draft.copy_(d.to(c.draft.dtype))
+    c.otree = oracle.build_tree(to_np(c.draft), w.depth, w.topk, w.children, w.m, m_max=w.m_max)
+    c.step.build(c.draft, c.kinds)
+    torch.cuda.synchronize()
+    assert_tree_equal(c)
+
+
 @pytest.mark.parametrize("shape", ["paged-mixed", "gqa8-split-blocks"])
 def test_determinism(shape):
     # the paged mix of trees and chains (8-wave and key-half forms), and row
